@@ -1,0 +1,166 @@
+"""Pins of the oracle's load-balancing plan (CPU only).
+
+Hand-worked examples (tests/golden/plan_hand_examples.json), the structural
+invariants that the scheduler's steps imply, the appendix-D workspace bound,
+and Graham's LPT makespan bound against a brute-forced optimum on tiny inputs.
+"""
+
+import itertools
+import json
+import os
+import random
+
+import pytest
+
+from oracle import plan
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _examples():
+    with open(os.path.join(GOLDEN, "plan_hand_examples.json")) as f:
+        return json.load(f)["examples"]
+
+
+@pytest.mark.parametrize("ex", _examples())
+def test_hand_examples(ex):
+    n = len(ex["kv_lens"])
+    st = plan.lpt_plan([1] * n, ex["kv_lens"], 1, ex["num_ctas"], ex["alpha"], ex["beta"])
+    assert st.kv_chunk == ex["kv_chunk"]
+    assert [[it.w, it.req, it.kv_begin, it.kv_end] for it in st.items] == ex["items"]
+    assert st.order == ex["sorted_order"]
+    assert st.cta_items == ex["cta_items"]
+    assert st.cta_cost == ex["cta_cost"]
+    slots = plan.assign_slots(st, lambda r: True)
+    assert slots == ex["slots"]
+    wt = sorted({st.items[w].req for w, s in enumerate(slots) if s < 0})
+    assert wt == ex["write_through_requests"]
+
+
+def _random_case(rng, tile_q=1):
+    n = rng.randint(1, 40)
+    kv = [rng.choice([0, 1, 2, 5, 16, 100, rng.randint(0, 5000)]) for _ in range(n)]
+    qo = [1] * n if tile_q == 1 else [rng.randint(0, 9) for _ in range(n)]
+    return qo, kv, rng.randint(1, 64), rng.choice([1, 1, 4, 16])
+
+
+@pytest.mark.parametrize("seed", range(30))
+@pytest.mark.parametrize("tile_q", [1, 4])
+def test_invariants(seed, tile_q):
+    rng = random.Random(seed)
+    qo, kv, ctas, align = _random_case(rng, tile_q)
+    alpha, beta = rng.randint(0, 3), rng.randint(0, 3)
+    st = plan.lpt_plan(qo, kv, tile_q, ctas, alpha, beta, align)
+    L = st.kv_chunk
+    S = sum(plan.ceil_div(a, tile_q) * b for a, b in zip(qo, kv))
+    assert L % align == 0 and L >= max(1, plan.ceil_div(S, ctas))
+    assert L < max(1, plan.ceil_div(S, ctas)) + align
+    # chunks of every tile partition [0, l_kv) exactly, ceil(l/L) of them, at most L long
+    by_tile = {}
+    for it in st.items:
+        by_tile.setdefault((it.req, it.tile), []).append(it)
+        assert 0 < it.length <= L
+    for i, (lqo, lkv) in enumerate(zip(qo, kv)):
+        for j in range(plan.ceil_div(lqo, tile_q)):
+            ch = by_tile.get((i, j), [])
+            assert len(ch) == plan.ceil_div(lkv, L)
+            assert [c.kv_begin for c in ch] == [k * L for k in range(len(ch))]
+            if ch:
+                assert ch[-1].kv_end == lkv
+                assert all(a.kv_end == b.kv_begin for a, b in zip(ch, ch[1:]))
+            assert all(c.lq == min(tile_q, lqo - j * tile_q) for c in ch)
+    # enumeration order and sorted order
+    assert [it.w for it in st.items] == list(range(len(st.items)))
+    lens = [st.items[w].length for w in st.order]
+    assert lens == sorted(lens, reverse=True)
+    for a, b in zip(st.order, st.order[1:]):
+        if st.items[a].length == st.items[b].length:
+            assert a < b
+    # every item assigned once; costs add up
+    flat = sorted(w for c in st.cta_items for w in c)
+    assert flat == list(range(len(st.items)))
+    for c, ws in enumerate(st.cta_items):
+        assert st.cta_cost[c] == sum(alpha * st.items[w].lq + beta * st.items[w].length for w in ws)
+    # item count bound and the appendix-D workspace bound
+    n_tiles = sum(plan.ceil_div(a, tile_q) for a in qo)
+    assert len(st.items) <= ctas + n_tiles
+    slots = plan.assign_slots(st, lambda r: True)
+    n_slots = sum(1 for s in slots if s >= 0)
+    assert n_slots <= 2 * ctas
+    assert sorted(s for s in slots if s >= 0) == list(range(n_slots))
+
+
+def test_queue_ties_go_to_smaller_cta():
+    st = plan.lpt_plan([1] * 4, [5, 5, 5, 5], 1, 4, enable_split=False)
+    assert st.cta_items == [[0], [1], [2], [3]]
+    st = plan.lpt_plan([1] * 5, [5, 5, 5, 5, 5], 1, 2, enable_split=False)
+    assert st.cta_items == [[0, 2, 4], [1, 3]]
+
+
+def test_empty_and_degenerate():
+    st = plan.lpt_plan([1, 1], [0, 0], 1, 8)
+    assert st.items == [] and st.kv_chunk == 1 and st.cta_cost == [0] * 8
+    st = plan.lpt_plan([], [], 1, 3)
+    assert st.items == []
+    st = plan.lpt_plan([1], [1], 1, 1000)
+    assert len(st.items) == 1 and st.kv_chunk == 1
+    st = plan.lpt_plan([1, 1], [100, 3], 1, 4, enable_split=False)
+    assert [it.length for it in st.items] == [100, 3]
+    with pytest.raises(ValueError):
+        plan.lpt_plan([1], [-1], 1, 4)
+
+
+def _opt_makespan(costs, m):
+    best = None
+    for assign in itertools.product(range(m), repeat=len(costs)):
+        loads = [0] * m
+        for c, a in zip(costs, assign):
+            loads[a] += c
+        mk = max(loads)
+        best = mk if best is None else min(best, mk)
+    return best
+
+
+@pytest.mark.parametrize("seed", range(25))
+def test_lpt_graham_bound(seed):
+    """With one query per request every item costs alpha + beta * length, so
+    sorting by length is sorting by cost and the plan is Graham's LPT rule:
+    makespan <= (4/3 - 1/(3m)) * OPT."""
+    rng = random.Random(seed)
+    m = rng.randint(2, 3)
+    n = rng.randint(2, 6)
+    kv = [rng.randint(1, 30) for _ in range(n)]
+    st = plan.lpt_plan([1] * n, kv, 1, m, 1, 1, enable_split=rng.random() < 0.5)
+    if len(st.items) > 8:
+        pytest.skip("too many items for brute force")
+    costs = [1 + it.length for it in st.items]
+    opt = _opt_makespan(costs, m)
+    assert plan.makespan(st) * 3 * m <= (4 * m - 1) * opt
+
+
+def test_cascade_plan_merge_lists():
+    """Level states first (levels in order, chunks ascending), then the
+    request's own chunks; write-through only for requests no level covers."""
+    levels = [{"qo_indptr": [0, 4], "kv_lens": [40]},
+              {"qo_indptr": [0, 2, 3], "kv_lens": [10, 0]}]
+    cp = plan.cascade_plan(5, levels, [8, 0, 30, 3, 4], num_ctas=4, level_ctas=2,
+                           level_tile_q=[2, 1], alpha=1, beta=1)
+    # level 0: 2 tiles of 2 queries x 40 tokens -> S = 80, L = 40 -> one chunk per tile
+    assert [(it.req, it.tile, it.kv_begin, it.kv_end) for it in cp.levels[0].items] == [(0, 0, 0, 40), (0, 1, 0, 40)]
+    assert cp.levels[0].slots == [0, 1]
+    # level 1 (T_q = 1): group 0 has 2 one-query tiles of 10 tokens, group 1 has no KV
+    # -> S = 2 * 10 = 20, L = 10 -> one chunk per tile
+    assert [(it.req, it.tile, it.kv_begin, it.kv_end) for it in cp.levels[1].items] == \
+        [(0, 0, 0, 10), (0, 1, 0, 10)]
+    assert cp.levels[1].slots == [0, 1]
+    # suffix: S = 45, L = 12
+    assert cp.suffix.kv_chunk == 12
+    assert [(it.req, it.kv_begin, it.kv_end) for it in cp.suffix.items] == \
+        [(0, 0, 8), (2, 0, 12), (2, 12, 24), (2, 24, 30), (3, 0, 3), (4, 0, 4)]
+    assert cp.suffix.slots == [0, 1, 2, 3, 4, -1]
+    assert cp.write_through == [False, False, False, False, True]
+    assert cp.merge[0] == [(0, 0, 0), (1, 0, 0), ("suffix", 0, 0)]
+    assert cp.merge[1] == [(0, 0, 1), (1, 1, 0)]
+    assert cp.merge[2] == [(0, 1, 0), ("suffix", 1, 0), ("suffix", 2, 0), ("suffix", 3, 0)]
+    assert cp.merge[3] == [(0, 1, 1), ("suffix", 4, 0)]
+    assert cp.merge[4] == []
