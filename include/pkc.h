@@ -1,0 +1,336 @@
+/*
+ * pkc.h -- C ABI of libpkc: paged-KV cascade decode attention for AMD MI355X (gfx950).
+ *
+ * What the library computes
+ * -------------------------
+ * Decode attention of one query token per request over a paged KV cache, returned as an
+ * attention state: the output O and the log-sum-exp LSE of the scaled scores (natural log).
+ * States of disjoint token sets of the same query combine with the merge operator
+ *     (O, LSE)(I u J) = ( (e^{LSE_I} O_I + e^{LSE_J} O_J) / (e^{LSE_I} + e^{LSE_J}),
+ *                         log(e^{LSE_I} + e^{LSE_J}) )
+ * which is commutative and associative ("Attention States and Recursive Attention",
+ * FlashInfer tutorial, merge operator equations; FlashInfer paper summary, section A2
+ * "Attention composition").  Three uses of it are built in:
+ *   - split-KV: a request's KV is cut into chunks that run on different workgroups and are
+ *     merged in a second pass (the tutorial's "KV sequence parallelism" application);
+ *   - cascade: queries that share a prefix attend to it with a multi-query (MFMA) kernel that
+ *     reads the shared KV once, attend to their own suffix with the decode kernel, and the
+ *     states are merged ("Cascade Inference" blog, algorithm section); more than two levels
+ *     and several shared prefixes per level are supported (same blog, future-work section);
+ *   - a CPU load-balancing plan assigns KV chunks to workgroups (FlashInfer paper summary,
+ *     section A3, "load-balancing scheduling"; appendix D, workspace and write-through).
+ *
+ * Data layout (all device arrays are caller-owned, contiguous, row-major)
+ * ---------------------------------------------------------------------
+ *   q            [B, Hq, D]                 dtype      one query token per request
+ *   k_pool,v_pool[num_pages, P, Hkv, D]     dtype      head_dim contiguous; token t of a page
+ *                                                      run lives in page run[t / P], slot t % P
+ *   block_table  [B, max_blocks]            int32      physical page of each logical block of a
+ *                                                      request; -1 = not allocated ("Paged
+ *                                                      attention" page, decode path)
+ *   cache_seqlens[B]                        int32      cached tokens per request
+ *   o            [B, Hq, D]                 out dtype  final output (rounded once, RNE)
+ *   lse          [B, Hq]                    float32    natural-log LSE; -inf for an empty set
+ * Query head h reads KV head h / (Hq / Hkv) (grouped-query attention, contiguous groups).
+ * A request attends over exactly the tokens [kv_start[b], cache_seqlens[b]) of its table
+ * row: blocks past the last cached token are never dereferenced, so a block allocated for the
+ * next token (or -1) there is harmless.  An invalid entry (-1 or >= num_pages) INSIDE that
+ * range is a caller error: the kernels never read memory through it (such a page contributes
+ * no tokens) and pkc_validate_block_table reports it.
+ *
+ * Supported: dtype f32 / f16 / bf16 (q, k, v share it); head_dim 64 or 128; page size a power
+ * of two in [1, 1024]; Hq / Hkv in {1, 2, 4, 8}.  The multi-query prefix kernel needs
+ * f16 or bf16 and page size >= 4; other combinations return PKC_ERR_UNSUPPORTED.
+ *
+ * Conventions
+ * -----------
+ * Every function is extern "C", never throws, and returns a pkc_status.  On failure
+ * pkc_last_error() gives a thread-local message.  All shape/argument checks happen on the host
+ * before any launch.  Device work is enqueued on the caller's HIP stream (`stream`, a
+ * hipStream_t; NULL = the null stream) and calls return without synchronising.  The library
+ * never allocates or frees device or pinned memory; the plan and the partial states live in a
+ * caller-provided device workspace whose size pkc_plan_buffer_sizes returns.  The only global
+ * state is cached device properties and the optional timing ring.
+ */
+#ifndef PKC_H
+#define PKC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pkc_status {
+  PKC_OK = 0,
+  PKC_ERR_INVALID_ARG = 1,         /* bad pointer, shape, length or parameter */
+  PKC_ERR_UNSUPPORTED = 2,         /* dtype / head_dim / page size / group size not built */
+  PKC_ERR_WORKSPACE_TOO_SMALL = 3, /* host or device buffer smaller than required */
+  PKC_ERR_PLAN_MISMATCH = 4,       /* plan built for other shapes or another workspace */
+  PKC_ERR_HIP = 5,                 /* a HIP runtime call failed (message has the HIP error) */
+  PKC_ERR_INTERNAL = 6
+} pkc_status;
+
+typedef enum pkc_dtype { PKC_F32 = 0, PKC_F16 = 1, PKC_BF16 = 2 } pkc_dtype;
+
+#define PKC_MAX_LEVELS 8
+#define PKC_PLAN_MAGIC 0x504b4331u /* "PKC1" */
+
+/* Diagnostics. */
+const char* pkc_status_string(pkc_status s);
+const char* pkc_last_error(void);
+const char* pkc_version(void);
+
+/* sizeof of the ABI structs below, so that language bindings can check their mirrors. */
+void pkc_abi_struct_sizes(size_t* plan_params, size_t* level_host, size_t* level_dev,
+                          size_t* plan_info);
+
+/* Compute units and wavefront size of a device (HIP device ordinal). */
+pkc_status pkc_device_info(int32_t device, int32_t* num_cus, int32_t* wave_size,
+                           int64_t* lds_bytes_per_block);
+
+/*
+ * Plan parameters.  The plan follows the load-balancing scheduler of the FlashInfer paper
+ * summary (section A3): the cost of a tile is alpha * l_q + beta * l_kv; the maximum chunk is
+ * L_kv = ceil(sum_i ceil(l_qo(i) / T_q) * l_kv(i) / #CTA) (rounded up to chunk_align); every
+ * tile's KV is cut greedily into chunks of at most L_kv; chunks are sorted longest first
+ * (stable) and each goes to the CTA with the smallest cost so far (ties: smaller CTA index).
+ * A CTA is one workgroup per KV head (head-group fusion, paper appendix A): a stage launches
+ * #CTA x Hkv workgroups.
+ */
+typedef struct pkc_plan_params {
+  int32_t batch;        /* B: requests (one query token each) */
+  int32_t num_qo_heads; /* Hq */
+  int32_t num_kv_heads; /* Hkv (divides Hq) */
+  int32_t head_dim;     /* D */
+  int32_t page_size;    /* P */
+  int32_t num_ctas;     /* #CTA of the decode stage; 0 -> 2 x compute units of the current device */
+  int32_t level_ctas;   /* #CTA of every cascade level; 0 -> max(1, ceil(2 x CUs / Hkv)) */
+  int32_t level_tile_q; /* T_q of the cascade levels (queries per tile); 0 -> 128 / (Hq/Hkv) */
+  int32_t chunk_align;  /* round L_kv up to a multiple of this; 0 or 1 -> no rounding */
+  int32_t enable_split; /* 0 -> L_kv = longest KV length (one chunk per tile, no split-KV) */
+  int64_t alpha;        /* cost per query row (>= 0) */
+  int64_t beta;         /* cost per KV token (>= 0) */
+} pkc_plan_params;
+
+/* Host description of one cascade level: groups of consecutive requests sharing a KV run.
+ * Group g holds requests qo_indptr[g] <= b < qo_indptr[g+1] (0 <= qo_indptr[0],
+ * non-decreasing, qo_indptr[G] <= B) and attends over kv_lens[g] tokens. */
+typedef struct pkc_level_host {
+  int32_t num_groups;
+  const int32_t* qo_indptr; /* [G+1] host */
+  const int32_t* kv_lens;   /* [G] host, tokens */
+} pkc_level_host;
+
+/* Device description of one cascade level (block-sparse row view of the KV cache, paper
+ * summary section A3): token t of group g is in page kv_page_indices[kv_page_indptr[g] + t/P],
+ * slot t % P.  The group's run must hold ceil(kv_lens[g] / P) pages. */
+typedef struct pkc_level_dev {
+  const int32_t* kv_page_indptr;  /* [G+1] device */
+  const int32_t* kv_page_indices; /* [nnz] device */
+  int32_t num_page_indices;       /* nnz (host value, for validation) */
+} pkc_level_dev;
+
+/*
+ * A plan: plain data describing where the plan's integer arrays and the partial states sit in
+ * the device workspace.  Produced by pkc_plan / pkc_plan_host, consumed by the run calls.
+ * The integer arrays are laid out identically in the host buffer and the device workspace
+ * (see pkc_plan for the format).  Do not edit; a plan is valid only with the workspace it was
+ * built for.
+ */
+typedef struct pkc_plan_info {
+  uint32_t magic;
+  int32_t batch, num_qo_heads, num_kv_heads, head_dim, page_size;
+  int32_t num_levels;
+  int32_t num_ctas;        /* decode stage #CTA (resolved) */
+  int32_t level_ctas;      /* level #CTA (resolved) */
+  int32_t dec_items;       /* work items of the decode stage */
+  int32_t dec_slots;       /* partial slots of the decode stage */
+  int32_t dec_kv_chunk;    /* L_kv of the decode stage */
+  int32_t lvl_groups[PKC_MAX_LEVELS];
+  int32_t lvl_tile_q[PKC_MAX_LEVELS];
+  int32_t lvl_items[PKC_MAX_LEVELS];
+  int32_t lvl_kv_chunk[PKC_MAX_LEVELS];
+  int32_t lvl_row_base[PKC_MAX_LEVELS]; /* first state row of each level */
+  int32_t dec_row_base;    /* first state row of the decode stage */
+  int32_t state_rows;      /* rows of the fp32 partial-state buffer */
+  int32_t merge_entries;   /* length of the merge row list */
+  int32_t num_merge;       /* requests whose output the merge kernel writes */
+  int64_t off_dec_indptr;  /* byte offsets inside the host buffer / device workspace */
+  int64_t off_dec_items;
+  int64_t off_lvl_indptr[PKC_MAX_LEVELS];
+  int64_t off_lvl_items[PKC_MAX_LEVELS];
+  int64_t off_merge_ptr;
+  int64_t off_merge_rows;
+  int64_t off_req_flags;
+  int64_t int_bytes;       /* bytes of integer plan data (copied host -> device) */
+  int64_t off_state_o;     /* fp32 [state_rows, Hq, D] */
+  int64_t off_state_lse;   /* fp32 [state_rows, Hq] */
+  int64_t dev_bytes;       /* device workspace bytes this plan uses */
+  uint64_t dev_ws;         /* address of the workspace the plan was copied to (0: host-only) */
+} pkc_plan_info;
+
+/*
+ * Upper bounds of the pinned host buffer and device workspace for any plan with these
+ * parameters and level shapes (only num_groups and qo_indptr of each level are read;
+ * kv_lens may be NULL), so that pointers can stay fixed across steps (paper appendix D: the
+ * workspace is sized from upper bounds for graph capture).  The decode stage's partial
+ * states are bounded by 2 x #CTA rows, the appendix-D bound 2 x #CTA x T_q x Hq x (D + 1)
+ * floats with T_q = 1.
+ */
+pkc_status pkc_plan_buffer_sizes(const pkc_plan_params* params, const pkc_level_host* levels,
+                                 int32_t num_levels, size_t* host_bytes, size_t* device_bytes);
+
+/*
+ * Build a plan on the CPU and enqueue its copy into the device workspace.
+ *   kv_lens_h: [B] host, tokens each request attends over in its own KV (the suffix in a
+ *              cascade; cache_seqlens - kv_start for a plain decode).
+ *   levels_h:  num_levels cascade levels (0 for a plain split-KV decode).
+ *   host_buf:  caller-owned pinned host buffer (hipHostMalloc / torch pin_memory) of at least
+ *              the size pkc_plan_buffer_sizes returned; it must stay untouched until the copy
+ *              enqueued on `stream` has completed.
+ *   dev_ws:    caller-owned device workspace (256-byte aligned).
+ * Plan format (int32 arrays at the plan's offsets):
+ *   stage indptr [#CTA + 1]: items of CTA c are [indptr[c], indptr[c+1]), in assignment order;
+ *   stage items  8 int32 per item: {group_or_request, first_query, num_queries, kv_begin,
+ *                kv_end, state_row (-1 = written to the final output), tile, w};
+ *   merge_ptr    [B, num_levels + 2]: the merge rows of request b for level l are
+ *                merge_rows[merge_ptr[b][l] .. merge_ptr[b][l+1]) (level num_levels = the
+ *                request's own KV), in merge order: levels ascending, chunks ascending;
+ *   merge_rows   state rows; req_flags [B]: 1 when the decode stage writes the output.
+ */
+pkc_status pkc_plan(const pkc_plan_params* params, const int32_t* kv_lens_h,
+                    const pkc_level_host* levels_h, int32_t num_levels, void* host_buf,
+                    size_t host_bytes, void* dev_ws, size_t dev_bytes, void* stream,
+                    pkc_plan_info* out);
+
+/* The same plan without any HIP call (for CPU-side checks): fills host_buf and *out only;
+ * out->dev_ws is 0.  num_ctas / level_ctas must be given explicitly (no device query). */
+pkc_status pkc_plan_host(const pkc_plan_params* params, const int32_t* kv_lens_h,
+                         const pkc_level_host* levels_h, int32_t num_levels, void* host_buf,
+                         size_t host_bytes, pkc_plan_info* out);
+
+/*
+ * Paged batch decode ("Paged attention" page, decode path; "Cascade Inference" blog,
+ * single-query kernels): request b attends over tokens [kv_start[b], cache_seqlens[b]).
+ *   plan == NULL: one workgroup per (request, KV head); every request writes o/lse directly.
+ *   plan != NULL: split-KV over the plan's decode stage (kv_lens_h of the plan must equal
+ *                 cache_seqlens - kv_start; the token ranges come from the plan); unsplit
+ *                 requests write o/lse directly (write-through, paper appendix D), split ones
+ *                 write fp32 partial states to the workspace and a merge kernel finishes them.
+ *                 The plan must have no levels.
+ *   kv_start: NULL = 0 for every request.
+ * dev_ws / dev_bytes may be NULL / 0 when plan is NULL.
+ */
+pkc_status pkc_batch_decode_paged(const pkc_plan_info* plan, const void* q, const void* k_pool,
+                                  const void* v_pool, int64_t num_pages,
+                                  const int32_t* block_table, int32_t max_blocks,
+                                  const int32_t* cache_seqlens, const int32_t* kv_start,
+                                  int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t page_size, pkc_dtype dtype,
+                                  float sm_scale, void* o, float* lse, void* dev_ws,
+                                  size_t dev_bytes, void* stream);
+
+/*
+ * Multi-query attention of one cascade level ("Cascade Inference" blog, algorithm step 1):
+ * every request covered by the level attends over its group's KV run; the group's queries run
+ * as the rows of MFMA tiles so the run is read from HBM once per tile, not once per request.
+ * The level's chunks are computed per the plan and merged into o_state [B, Hq, D] (o_dtype)
+ * and lse_state [B, Hq]; requests the level does not cover get the identity (0, -inf).
+ */
+pkc_status pkc_prefix_attention(const pkc_plan_info* plan, int32_t level, const void* q,
+                                const void* k_pool, const void* v_pool, int64_t num_pages,
+                                const pkc_level_dev* level_dev, int32_t batch,
+                                int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t page_size, pkc_dtype dtype, float sm_scale,
+                                void* o_state, pkc_dtype o_dtype, float* lse_state,
+                                void* dev_ws, size_t dev_bytes, void* stream);
+
+/*
+ * n-ary merge of attention states ("Attention States and Recursive Attention", n-ary merge
+ * equation; maximum subtracted for stability):
+ *   o_states [num_states, H, D] (in_dtype), lse_states [num_states, H] fp32.
+ *   Output i merges states indices[indptr[i] .. indptr[i+1]) in that order (indices NULL: the
+ *   states indptr[i] .. indptr[i+1]); indptr NULL: states i*S .. i*S + S - 1 with
+ *   S = states_per_output.  Zero states, or all LSE = -inf, give (0, -inf).
+ *   o_out [num_outputs, H, D] (out_dtype), lse_out [num_outputs, H].
+ * indptr / indices are device arrays and are not range-checked on the device beyond
+ * 0 <= index < num_states (out-of-range indices are skipped).
+ */
+pkc_status pkc_merge_states(const void* o_states, pkc_dtype in_dtype, const float* lse_states,
+                            int32_t num_states, const int32_t* indptr, const int32_t* indices,
+                            int32_t num_outputs, int32_t states_per_output, int32_t num_heads,
+                            int32_t head_dim, void* o_out, pkc_dtype out_dtype, float* lse_out,
+                            void* stream);
+
+/* Binary merge in place: (o_a, lse_a) <- (o_a, lse_a) merged with (o_b, lse_b), for
+ * num_rows x num_heads states of head_dim; o_a and o_b share `dtype`. */
+pkc_status pkc_merge_state_inplace(void* o_a, float* lse_a, const void* o_b, const float* lse_b,
+                                   int32_t num_rows, int32_t num_heads, int32_t head_dim,
+                                   pkc_dtype dtype, void* stream);
+
+/*
+ * Cascade decode ("Cascade Inference" blog, algorithm section, generalised to num_levels
+ * levels): for every level, the multi-query kernel over each group's KV run; then the decode
+ * kernel over every request's own KV (block_table rows, tokens [0, suffix_seqlens[b]) per the
+ * plan); then one merge per request of all its states in the order levels ascending, chunks
+ * ascending, own KV last.  The plan must have been built with the same levels and with
+ * kv_lens_h == suffix_seqlens.  Requests that no level covers and whose own KV is a single
+ * chunk are written directly by the decode kernel.
+ */
+pkc_status pkc_cascade_decode(const pkc_plan_info* plan, const void* q, const void* k_pool,
+                              const void* v_pool, int64_t num_pages,
+                              const pkc_level_dev* levels, int32_t num_levels,
+                              const int32_t* block_table, int32_t max_blocks,
+                              const int32_t* suffix_seqlens, int32_t batch, int32_t num_qo_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                              pkc_dtype dtype, float sm_scale, void* o, float* lse, void* dev_ws,
+                              size_t dev_bytes, void* stream);
+
+/*
+ * Host-side check of block-table contents (host arrays): every block holding one of the
+ * tokens [kv_start[b], cache_seqlens[b]) must name a page in [0, num_pages).  Returns
+ * PKC_ERR_INVALID_ARG naming the first bad (request, block) otherwise.  Not on the hot path.
+ */
+pkc_status pkc_validate_block_table(const int32_t* block_table, int32_t max_blocks,
+                                    const int32_t* cache_seqlens, const int32_t* kv_start,
+                                    int32_t batch, int32_t page_size, int64_t num_pages);
+
+/*
+ * Debug export of the integer gather: rows_out[b * max_tokens + t] = the physical row
+ * page * P + slot that the kernels read for token t (t < max_tokens) of request b, or -1
+ * when t is outside [kv_start[b], cache_seqlens[b]) or its block entry is invalid.  Uses the
+ * same device address routine as the decode kernel.
+ */
+pkc_status pkc_debug_gather_rows(const int32_t* block_table, int32_t max_blocks,
+                                 const int32_t* cache_seqlens, const int32_t* kv_start,
+                                 int32_t batch, int32_t page_size, int64_t num_pages,
+                                 int32_t* rows_out, int32_t max_tokens, void* stream);
+
+/*
+ * Debug export of the work-to-workgroup map as the device walks it: for stage `stage`
+ * (0 .. num_levels-1 = a level, num_levels = the decode stage), workgroup c writes, for its
+ * k-th item, the item's 8 plan fields to trace_out[(c * max_items_per_cta + k) * 8 ...];
+ * unused entries are -1.  trace_len counts int32 elements.
+ */
+pkc_status pkc_debug_cta_trace(const pkc_plan_info* plan, int32_t stage, const void* dev_ws,
+                               int32_t* trace_out, int64_t trace_len,
+                               int32_t max_items_per_cta, void* stream);
+
+/*
+ * Per-kernel timing with HIP events (for measurements): when enabled, every kernel launch
+ * of the calls above is bracketed by events recorded on the same stream.  pkc_timing_read
+ * waits for the recorded events and returns, per kernel kind, the number of launches and the
+ * summed duration in milliseconds since the last reset.
+ * Kernel kinds: 0 decode, 1 prefix (MFMA), 2 merge (plan-driven), 3 merge (generic / in place).
+ */
+pkc_status pkc_timing_enable(int32_t enable);
+pkc_status pkc_timing_reset(void);
+pkc_status pkc_timing_read(int32_t kind, int64_t* launches, double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKC_H */

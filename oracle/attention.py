@@ -61,26 +61,26 @@ def attention_state(q, keys, values, sm_scale):
     return o, lse
 
 
-def _gather(pool, pages, slots):
-    """Rows pool[page, slot] as float64 [n, H, D] (exact upcast)."""
-    return np.asarray(pool[pages, slots], dtype=np.float64)
+def _gather(pool, pages, slots, kv_head):
+    """Rows pool[page, slot, kv_head] as float64 [n, D] (exact upcast)."""
+    return np.asarray(pool[pages, slots, kv_head], dtype=np.float64)
 
 
 def _state_over_rows(q, k_pool, v_pool, pages, slots, sm_scale, heads):
     """O [Hq, D] and LSE [Hq] of one query token over gathered rows.
-    GQA head map: query head h reads kv head h // g (reading R3)."""
+    GQA head map: query head h reads kv head h // g (reading R3).
+    One kv head is gathered at a time to bound memory."""
     hq, d = q.shape
     hkv = k_pool.shape[2]
     g = hq // hkv
     o = np.full((hq, d), np.nan)
     lse = np.full(hq, np.nan)
-    K = _gather(k_pool, pages, slots)
-    V = _gather(v_pool, pages, slots)
-    for h in heads:
-        kh = h // g
-        oh, lh = attention_state(q[h], K[:, kh, :], V[:, kh, :], sm_scale)
-        o[h] = oh
-        lse[h] = lh
+    for kh in sorted({h // g for h in heads}):
+        K = _gather(k_pool, pages, slots, kh)
+        V = _gather(v_pool, pages, slots, kh)
+        for h in heads:
+            if h // g == kh:
+                o[h], lse[h] = attention_state(q[h], K, V, sm_scale)
     return o, lse
 
 

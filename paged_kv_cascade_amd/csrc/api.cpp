@@ -1,0 +1,562 @@
+// C ABI entry points of libpkc (host side): argument validation, plan copy, kernel launches on
+// the caller's stream, optional per-kernel event timing.  See include/pkc.h for the contract.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "plan_core.h"
+
+using pkc::fail;
+
+namespace {
+
+int log2i(int x) {
+  int s = 0;
+  while ((1 << s) < x) ++s;
+  return s;
+}
+
+pkc_status hip_fail(hipError_t e, const char* what) {
+  return fail(PKC_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+int g_cached_cus[64] = {0};
+std::mutex g_mu;
+
+pkc_status device_cus(int32_t* cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev >= 0 && dev < 64 && g_cached_cus[dev] > 0) {
+    *cus = g_cached_cus[dev];
+    return PKC_OK;
+  }
+  int n = 0;
+  e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+  if (dev >= 0 && dev < 64) g_cached_cus[dev] = n;
+  *cus = n;
+  return PKC_OK;
+}
+
+// ---- per-kernel timing ring ---------------------------------------------------------------
+struct TimedLaunch {
+  int kind;
+  hipEvent_t start, stop;
+};
+bool g_timing = false;
+std::vector<TimedLaunch> g_pending;
+std::vector<hipEvent_t> g_free_events;
+int64_t g_launches[4] = {0, 0, 0, 0};
+double g_ms[4] = {0, 0, 0, 0};
+
+hipEvent_t take_event() {
+  if (!g_free_events.empty()) {
+    hipEvent_t e = g_free_events.back();
+    g_free_events.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Runs `launch` and, when timing is on, brackets it with events on the same stream.
+template <typename F>
+pkc_status timed(int kind, hipStream_t s, const char* what, F&& launch) {
+  hipEvent_t a = nullptr, b = nullptr;
+  if (g_timing) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    a = take_event();
+    b = take_event();
+    if (a) (void)hipEventRecord(a, s);
+  }
+  hipError_t e = launch();
+  if (e != hipSuccess) return hip_fail(e, what);
+  if (g_timing && a && b) {
+    (void)hipEventRecord(b, s);
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_pending.push_back({kind, a, b});
+  }
+  return PKC_OK;
+}
+
+bool dtype_ok(pkc_dtype d) { return d == PKC_F32 || d == PKC_F16 || d == PKC_BF16; }
+
+pkc_status check_shapes(int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim,
+                        int32_t page_size, pkc_dtype dtype, float sm_scale) {
+  if (batch < 0) return fail(PKC_ERR_INVALID_ARG, "batch must be >= 0");
+  if (hq <= 0 || hkv <= 0 || hq % hkv)
+    return fail(PKC_ERR_INVALID_ARG, "num_qo_heads must be a positive multiple of num_kv_heads");
+  const int g = hq / hkv;
+  if (!(g == 1 || g == 2 || g == 4 || g == 8))
+    return fail(PKC_ERR_UNSUPPORTED, "group size Hq/Hkv must be 1, 2, 4 or 8");
+  if (!(head_dim == 64 || head_dim == 128)) return fail(PKC_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (!pkc::is_pow2(page_size) || page_size > 1024)
+    return fail(PKC_ERR_UNSUPPORTED, "page_size must be a power of two in [1, 1024]");
+  if (!dtype_ok(dtype)) return fail(PKC_ERR_UNSUPPORTED, "unknown dtype");
+  if (!(sm_scale > 0.f) || !std::isfinite(sm_scale))
+    return fail(PKC_ERR_INVALID_ARG, "sm_scale must be positive and finite");
+  return PKC_OK;
+}
+
+pkc_status check_plan(const pkc_plan_info* plan, int32_t batch, int32_t hq, int32_t hkv,
+                      int32_t head_dim, int32_t page_size, const void* dev_ws, size_t dev_bytes) {
+  if (plan->magic != PKC_PLAN_MAGIC) return fail(PKC_ERR_PLAN_MISMATCH, "not a plan (bad magic)");
+  if (plan->batch != batch || plan->num_qo_heads != hq || plan->num_kv_heads != hkv ||
+      plan->head_dim != head_dim || plan->page_size != page_size)
+    return fail(PKC_ERR_PLAN_MISMATCH, "plan was built for other shapes");
+  if (plan->dev_ws == 0 || plan->dev_ws != (uint64_t)(uintptr_t)dev_ws)
+    return fail(PKC_ERR_PLAN_MISMATCH, "plan was copied to another device workspace");
+  if (dev_bytes < (size_t)plan->dev_bytes)
+    return fail(PKC_ERR_WORKSPACE_TOO_SMALL, "device workspace smaller than the plan needs");
+  return PKC_OK;
+}
+
+template <typename T>
+T* at(void* base, int64_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(base) + off);
+}
+
+pkc::DecodeParams decode_params(const void* q, const void* k, const void* v, int64_t num_pages,
+                                const int32_t* bt, int32_t max_blocks, const int32_t* seqlens,
+                                const int32_t* kv_start, int32_t hq, int32_t hkv,
+                                int32_t page_size, float sm_scale, void* o, float* lse) {
+  pkc::DecodeParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.num_pages = num_pages;
+  p.block_table = bt;
+  p.max_blocks = max_blocks;
+  p.seqlens = seqlens;
+  p.kv_start = kv_start;
+  p.hq = hq;
+  p.hkv = hkv;
+  p.page_size = page_size;
+  p.page_shift = log2i(page_size);
+  p.scale_log2 = sm_scale * 1.4426950408889634f;
+  p.o = o;
+  p.lse = lse;
+  return p;
+}
+
+pkc::MergePlanParams merge_params(const pkc_plan_info* plan, void* ws, int l0, int l1, bool skip_wt,
+                                  void* o, float* lse) {
+  pkc::MergePlanParams m{};
+  m.st_o = at<float>(ws, plan->off_state_o);
+  m.st_lse = at<float>(ws, plan->off_state_lse);
+  m.merge_ptr = at<int32_t>(ws, plan->off_merge_ptr);
+  m.merge_rows = at<int32_t>(ws, plan->off_merge_rows);
+  m.req_flags = skip_wt ? at<int32_t>(ws, plan->off_req_flags) : nullptr;
+  m.nl2 = plan->num_levels + 2;
+  m.l0 = l0;
+  m.l1 = l1;
+  m.batch = plan->batch;
+  m.hq = plan->num_qo_heads;
+  m.o = o;
+  m.lse = lse;
+  return m;
+}
+
+pkc_status run_level(const pkc_plan_info* plan, int level, const void* q, const void* k, const void* v,
+                     int64_t num_pages, const pkc_level_dev* lv, pkc_dtype dtype, float sm_scale,
+                     void* ws, hipStream_t s) {
+  if (plan->lvl_groups[level] > 0 && (!lv->kv_page_indptr || !lv->kv_page_indices))
+    return fail(PKC_ERR_INVALID_ARG, "level " + std::to_string(level) + ": NULL page arrays");
+  pkc::PrefixParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.num_pages = num_pages;
+  p.page_indptr = lv->kv_page_indptr;
+  p.page_indices = lv->kv_page_indices;
+  p.num_page_indices = lv->num_page_indices;
+  p.hq = plan->num_qo_heads;
+  p.hkv = plan->num_kv_heads;
+  p.page_size = plan->page_size;
+  p.page_shift = log2i(plan->page_size);
+  p.scale_log2 = sm_scale * 1.4426950408889634f;
+  p.st_o = at<float>(ws, plan->off_state_o);
+  p.st_lse = at<float>(ws, plan->off_state_lse);
+  p.indptr = at<int32_t>(ws, plan->off_lvl_indptr[level]);
+  p.items = at<int32_t>(ws, plan->off_lvl_items[level]);
+  const int g = plan->num_qo_heads / plan->num_kv_heads;
+  return timed(1, s, "prefix kernel launch", [&] {
+    return pkc::launch_prefix(dtype, plan->head_dim, g, plan->lvl_tile_q[level], p,
+                              plan->level_ctas, s);
+  });
+}
+
+// Checks the parameters and fills #CTA defaults from the current device: 2 x compute units
+// for the decode stage, ceil(2 x compute units / Hkv) for every level.
+pkc_status resolve_params(const pkc_plan_params* params, pkc::Resolved* r) {
+  pkc_status st = pkc::check_params(params, false, r);
+  if (st != PKC_OK) return st;
+  if (r->p.num_ctas == 0 || r->p.level_ctas == 0) {
+    int32_t cus = 0;
+    if ((st = device_cus(&cus)) != PKC_OK) return st;
+    if (r->p.num_ctas == 0) r->p.num_ctas = 2 * cus;
+    if (r->p.level_ctas == 0)
+      r->p.level_ctas = (int32_t)std::max<int64_t>(1, pkc::ceil_div(2 * (int64_t)cus, r->p.num_kv_heads));
+  }
+  return PKC_OK;
+}
+
+pkc_status check_prefix_supported(pkc_dtype dtype, int32_t page_size) {
+  if (dtype != PKC_F16 && dtype != PKC_BF16)
+    return fail(PKC_ERR_UNSUPPORTED, "the multi-query prefix kernel needs f16 or bf16");
+  if (page_size < 4) return fail(PKC_ERR_UNSUPPORTED, "the multi-query prefix kernel needs page_size >= 4");
+  return PKC_OK;
+}
+
+}  // namespace
+
+#define PKC_TRY_BEGIN \
+  try {               \
+    pkc::clear_error();
+#define PKC_TRY_END(name)                                                   \
+  }                                                                         \
+  catch (...) {                                                             \
+    return fail(PKC_ERR_INTERNAL, std::string("exception in ") + (name));   \
+  }
+
+extern "C" {
+
+const char* pkc_status_string(pkc_status s) {
+  switch (s) {
+    case PKC_OK: return "PKC_OK";
+    case PKC_ERR_INVALID_ARG: return "PKC_ERR_INVALID_ARG";
+    case PKC_ERR_UNSUPPORTED: return "PKC_ERR_UNSUPPORTED";
+    case PKC_ERR_WORKSPACE_TOO_SMALL: return "PKC_ERR_WORKSPACE_TOO_SMALL";
+    case PKC_ERR_PLAN_MISMATCH: return "PKC_ERR_PLAN_MISMATCH";
+    case PKC_ERR_HIP: return "PKC_ERR_HIP";
+    case PKC_ERR_INTERNAL: return "PKC_ERR_INTERNAL";
+  }
+  return "PKC_UNKNOWN_STATUS";
+}
+
+const char* pkc_version(void) { return "pkc 0.1 gfx950"; }
+
+void pkc_abi_struct_sizes(size_t* plan_params, size_t* level_host, size_t* level_dev,
+                          size_t* plan_info) {
+  if (plan_params) *plan_params = sizeof(pkc_plan_params);
+  if (level_host) *level_host = sizeof(pkc_level_host);
+  if (level_dev) *level_dev = sizeof(pkc_level_dev);
+  if (plan_info) *plan_info = sizeof(pkc_plan_info);
+}
+
+pkc_status pkc_device_info(int32_t device, int32_t* num_cus, int32_t* wave_size,
+                           int64_t* lds_bytes_per_block) {
+  PKC_TRY_BEGIN
+  int v = 0;
+  hipError_t e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, device);
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(CUs)");
+  if (num_cus) *num_cus = v;
+  if ((e = hipDeviceGetAttribute(&v, hipDeviceAttributeWarpSize, device)) != hipSuccess)
+    return hip_fail(e, "hipDeviceGetAttribute(wave size)");
+  if (wave_size) *wave_size = v;
+  if ((e = hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, device)) != hipSuccess)
+    return hip_fail(e, "hipDeviceGetAttribute(LDS)");
+  if (lds_bytes_per_block) *lds_bytes_per_block = v;
+  return PKC_OK;
+  PKC_TRY_END("pkc_device_info")
+}
+
+pkc_status pkc_plan_buffer_sizes(const pkc_plan_params* params, const pkc_level_host* levels,
+                                 int32_t num_levels, size_t* host_bytes, size_t* device_bytes) {
+  PKC_TRY_BEGIN
+  pkc::Resolved r;
+  pkc_status st = resolve_params(params, &r);
+  if (st != PKC_OK) return st;
+  if ((st = pkc::check_levels(levels, num_levels, r.p.batch, false)) != PKC_OK) return st;
+  pkc::Layout L;
+  if ((st = pkc::compute_layout(r, levels, num_levels, &L)) != PKC_OK) return st;
+  if (host_bytes) *host_bytes = (size_t)L.int_bytes;
+  if (device_bytes) *device_bytes = (size_t)L.dev_bytes;
+  return PKC_OK;
+  PKC_TRY_END("pkc_plan_buffer_sizes")
+}
+
+pkc_status pkc_plan(const pkc_plan_params* params, const int32_t* kv_lens_h,
+                    const pkc_level_host* levels_h, int32_t num_levels, void* host_buf,
+                    size_t host_bytes, void* dev_ws, size_t dev_bytes, void* stream,
+                    pkc_plan_info* out) {
+  PKC_TRY_BEGIN
+  pkc::Resolved r;
+  pkc_status st = resolve_params(params, &r);
+  if (st != PKC_OK) return st;
+  if (!dev_ws || ((uintptr_t)dev_ws & 255)) return fail(PKC_ERR_INVALID_ARG, "dev_ws must be 256-byte aligned");
+  if ((st = pkc::build_plan_host(r, kv_lens_h, levels_h, num_levels, host_buf, host_bytes, out)) != PKC_OK)
+    return st;
+  if (dev_bytes < (size_t)out->dev_bytes)
+    return fail(PKC_ERR_WORKSPACE_TOO_SMALL, "device workspace smaller than " + std::to_string(out->dev_bytes) + " bytes");
+  hipError_t e = hipMemcpyAsync(dev_ws, host_buf, (size_t)out->int_bytes, hipMemcpyHostToDevice,
+                                reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(plan)");
+  out->dev_ws = (uint64_t)(uintptr_t)dev_ws;
+  return PKC_OK;
+  PKC_TRY_END("pkc_plan")
+}
+
+pkc_status pkc_batch_decode_paged(const pkc_plan_info* plan, const void* q, const void* k_pool,
+                                  const void* v_pool, int64_t num_pages,
+                                  const int32_t* block_table, int32_t max_blocks,
+                                  const int32_t* cache_seqlens, const int32_t* kv_start,
+                                  int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t page_size, pkc_dtype dtype,
+                                  float sm_scale, void* o, float* lse, void* dev_ws,
+                                  size_t dev_bytes, void* stream) {
+  PKC_TRY_BEGIN
+  pkc_status st = check_shapes(batch, num_qo_heads, num_kv_heads, head_dim, page_size, dtype, sm_scale);
+  if (st != PKC_OK) return st;
+  if (batch == 0) return PKC_OK;
+  if (!q || !k_pool || !v_pool || !block_table || !o || !lse)
+    return fail(PKC_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (!plan && !cache_seqlens) return fail(PKC_ERR_INVALID_ARG, "cache_seqlens is NULL");
+  if (num_pages < 0 || max_blocks < 0) return fail(PKC_ERR_INVALID_ARG, "negative num_pages / max_blocks");
+  if ((int64_t)max_blocks * page_size > INT32_MAX)
+    return fail(PKC_ERR_INVALID_ARG, "max_blocks * page_size exceeds int32");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  pkc::DecodeParams p = decode_params(q, k_pool, v_pool, num_pages, block_table, max_blocks,
+                                      cache_seqlens, kv_start, num_qo_heads, num_kv_heads,
+                                      page_size, sm_scale, o, lse);
+  const int g = num_qo_heads / num_kv_heads;
+  int grid_x = batch;
+  if (plan) {
+    if ((st = check_plan(plan, batch, num_qo_heads, num_kv_heads, head_dim, page_size, dev_ws, dev_bytes)) != PKC_OK)
+      return st;
+    if (plan->num_levels != 0) return fail(PKC_ERR_PLAN_MISMATCH, "batch decode needs a plan without levels");
+    p.st_o = at<float>(dev_ws, plan->off_state_o);
+    p.st_lse = at<float>(dev_ws, plan->off_state_lse);
+    p.indptr = at<int32_t>(dev_ws, plan->off_dec_indptr);
+    p.items = at<int32_t>(dev_ws, plan->off_dec_items);
+    grid_x = plan->num_ctas;
+  }
+  if ((st = timed(0, s, "decode kernel launch", [&] { return pkc::launch_decode(dtype, head_dim, g, p, grid_x, s); })) != PKC_OK)
+    return st;
+  if (plan && plan->num_merge > 0) {
+    pkc::MergePlanParams m = merge_params(plan, dev_ws, 0, 1, true, o, lse);
+    if ((st = timed(2, s, "merge kernel launch", [&] { return pkc::launch_merge_plan(dtype, head_dim, m, s); })) != PKC_OK)
+      return st;
+  }
+  return PKC_OK;
+  PKC_TRY_END("pkc_batch_decode_paged")
+}
+
+pkc_status pkc_prefix_attention(const pkc_plan_info* plan, int32_t level, const void* q,
+                                const void* k_pool, const void* v_pool, int64_t num_pages,
+                                const pkc_level_dev* level_dev, int32_t batch,
+                                int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t page_size, pkc_dtype dtype, float sm_scale,
+                                void* o_state, pkc_dtype o_dtype, float* lse_state,
+                                void* dev_ws, size_t dev_bytes, void* stream) {
+  PKC_TRY_BEGIN
+  pkc_status st = check_shapes(batch, num_qo_heads, num_kv_heads, head_dim, page_size, dtype, sm_scale);
+  if (st != PKC_OK) return st;
+  if ((st = check_prefix_supported(dtype, page_size)) != PKC_OK) return st;
+  if (!dtype_ok(o_dtype)) return fail(PKC_ERR_UNSUPPORTED, "unknown o_dtype");
+  if (!plan || !level_dev) return fail(PKC_ERR_INVALID_ARG, "plan and level_dev are required");
+  if ((st = check_plan(plan, batch, num_qo_heads, num_kv_heads, head_dim, page_size, dev_ws, dev_bytes)) != PKC_OK)
+    return st;
+  if (level < 0 || level >= plan->num_levels) return fail(PKC_ERR_INVALID_ARG, "level out of range");
+  if (batch == 0) return PKC_OK;
+  if (!q || !k_pool || !v_pool || !o_state || !lse_state) return fail(PKC_ERR_INVALID_ARG, "NULL tensor pointer");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if ((st = run_level(plan, level, q, k_pool, v_pool, num_pages, level_dev, dtype, sm_scale, dev_ws, s)) != PKC_OK)
+    return st;
+  pkc::MergePlanParams m = merge_params(plan, dev_ws, level, level + 1, false, o_state, lse_state);
+  return timed(2, s, "merge kernel launch", [&] { return pkc::launch_merge_plan(o_dtype, head_dim, m, s); });
+  PKC_TRY_END("pkc_prefix_attention")
+}
+
+pkc_status pkc_merge_states(const void* o_states, pkc_dtype in_dtype, const float* lse_states,
+                            int32_t num_states, const int32_t* indptr, const int32_t* indices,
+                            int32_t num_outputs, int32_t states_per_output, int32_t num_heads,
+                            int32_t head_dim, void* o_out, pkc_dtype out_dtype, float* lse_out,
+                            void* stream) {
+  PKC_TRY_BEGIN
+  if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return fail(PKC_ERR_UNSUPPORTED, "unknown dtype");
+  if (!(head_dim == 64 || head_dim == 128)) return fail(PKC_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (num_states < 0 || num_outputs < 0 || num_heads <= 0)
+    return fail(PKC_ERR_INVALID_ARG, "bad num_states / num_outputs / num_heads");
+  if (num_outputs == 0) return PKC_OK;
+  if (!o_out || !lse_out) return fail(PKC_ERR_INVALID_ARG, "NULL output pointer");
+  if (num_states > 0 && (!o_states || !lse_states)) return fail(PKC_ERR_INVALID_ARG, "NULL state pointer");
+  if (!indptr) {
+    if (indices) return fail(PKC_ERR_INVALID_ARG, "indices without indptr");
+    if (states_per_output < 0 || (int64_t)states_per_output * num_outputs > num_states)
+      return fail(PKC_ERR_INVALID_ARG, "states_per_output * num_outputs exceeds num_states");
+  }
+  pkc::MergeGenericParams p{};
+  p.o_states = o_states;
+  p.lse_states = lse_states;
+  p.num_states = num_states;
+  p.indptr = indptr;
+  p.indices = indices;
+  p.num_outputs = num_outputs;
+  p.states_per_output = states_per_output;
+  p.num_heads = num_heads;
+  p.o_out = o_out;
+  p.lse_out = lse_out;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return timed(3, s, "merge kernel launch", [&] { return pkc::launch_merge_generic(in_dtype, out_dtype, head_dim, p, s); });
+  PKC_TRY_END("pkc_merge_states")
+}
+
+pkc_status pkc_merge_state_inplace(void* o_a, float* lse_a, const void* o_b, const float* lse_b,
+                                   int32_t num_rows, int32_t num_heads, int32_t head_dim,
+                                   pkc_dtype dtype, void* stream) {
+  PKC_TRY_BEGIN
+  if (!dtype_ok(dtype)) return fail(PKC_ERR_UNSUPPORTED, "unknown dtype");
+  if (!(head_dim == 64 || head_dim == 128)) return fail(PKC_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (num_rows < 0 || num_heads <= 0) return fail(PKC_ERR_INVALID_ARG, "bad num_rows / num_heads");
+  if (num_rows == 0) return PKC_OK;
+  if (!o_a || !lse_a || !o_b || !lse_b) return fail(PKC_ERR_INVALID_ARG, "NULL pointer");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return timed(3, s, "merge kernel launch", [&] {
+    return pkc::launch_merge_inplace(dtype, head_dim, o_a, lse_a, o_b, lse_b, (int64_t)num_rows * num_heads, s);
+  });
+  PKC_TRY_END("pkc_merge_state_inplace")
+}
+
+pkc_status pkc_cascade_decode(const pkc_plan_info* plan, const void* q, const void* k_pool,
+                              const void* v_pool, int64_t num_pages,
+                              const pkc_level_dev* levels, int32_t num_levels,
+                              const int32_t* block_table, int32_t max_blocks,
+                              const int32_t* suffix_seqlens, int32_t batch, int32_t num_qo_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                              pkc_dtype dtype, float sm_scale, void* o, float* lse, void* dev_ws,
+                              size_t dev_bytes, void* stream) {
+  PKC_TRY_BEGIN
+  pkc_status st = check_shapes(batch, num_qo_heads, num_kv_heads, head_dim, page_size, dtype, sm_scale);
+  if (st != PKC_OK) return st;
+  if (!plan) return fail(PKC_ERR_INVALID_ARG, "cascade decode needs a plan");
+  if ((st = check_plan(plan, batch, num_qo_heads, num_kv_heads, head_dim, page_size, dev_ws, dev_bytes)) != PKC_OK)
+    return st;
+  if (num_levels != plan->num_levels) return fail(PKC_ERR_PLAN_MISMATCH, "num_levels differs from the plan");
+  if (num_levels > 0) {
+    if (!levels) return fail(PKC_ERR_INVALID_ARG, "levels is NULL");
+    if ((st = check_prefix_supported(dtype, page_size)) != PKC_OK) return st;
+  }
+  if (batch == 0) return PKC_OK;
+  if (!q || !k_pool || !v_pool || !o || !lse) return fail(PKC_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (plan->dec_items > 0 && !block_table) return fail(PKC_ERR_INVALID_ARG, "block_table is NULL");
+  if (num_pages < 0 || max_blocks < 0) return fail(PKC_ERR_INVALID_ARG, "negative num_pages / max_blocks");
+  if ((int64_t)max_blocks * page_size > INT32_MAX)
+    return fail(PKC_ERR_INVALID_ARG, "max_blocks * page_size exceeds int32");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  for (int32_t l = 0; l < num_levels; ++l)
+    if ((st = run_level(plan, l, q, k_pool, v_pool, num_pages, &levels[l], dtype, sm_scale, dev_ws, s)) != PKC_OK)
+      return st;
+  pkc::DecodeParams p = decode_params(q, k_pool, v_pool, num_pages, block_table, max_blocks,
+                                      suffix_seqlens, nullptr, num_qo_heads, num_kv_heads,
+                                      page_size, sm_scale, o, lse);
+  p.st_o = at<float>(dev_ws, plan->off_state_o);
+  p.st_lse = at<float>(dev_ws, plan->off_state_lse);
+  p.indptr = at<int32_t>(dev_ws, plan->off_dec_indptr);
+  p.items = at<int32_t>(dev_ws, plan->off_dec_items);
+  const int g = num_qo_heads / num_kv_heads;
+  if ((st = timed(0, s, "decode kernel launch", [&] { return pkc::launch_decode(dtype, head_dim, g, p, plan->num_ctas, s); })) != PKC_OK)
+    return st;
+  if (plan->num_merge > 0) {
+    pkc::MergePlanParams m = merge_params(plan, dev_ws, 0, num_levels + 1, true, o, lse);
+    if ((st = timed(2, s, "merge kernel launch", [&] { return pkc::launch_merge_plan(dtype, head_dim, m, s); })) != PKC_OK)
+      return st;
+  }
+  return PKC_OK;
+  PKC_TRY_END("pkc_cascade_decode")
+}
+
+pkc_status pkc_debug_gather_rows(const int32_t* block_table, int32_t max_blocks,
+                                 const int32_t* cache_seqlens, const int32_t* kv_start,
+                                 int32_t batch, int32_t page_size, int64_t num_pages,
+                                 int32_t* rows_out, int32_t max_tokens, void* stream) {
+  PKC_TRY_BEGIN
+  if (batch < 0 || max_blocks < 0 || max_tokens < 0 || num_pages < 0)
+    return fail(PKC_ERR_INVALID_ARG, "bad sizes");
+  if (!pkc::is_pow2(page_size) || page_size > 1024) return fail(PKC_ERR_UNSUPPORTED, "bad page_size");
+  if ((int64_t)max_blocks * page_size > INT32_MAX) return fail(PKC_ERR_INVALID_ARG, "table too large");
+  if (batch == 0 || max_tokens == 0) return PKC_OK;
+  if (!block_table || !cache_seqlens || !rows_out) return fail(PKC_ERR_INVALID_ARG, "NULL pointer");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = pkc::launch_debug_gather(block_table, max_blocks, cache_seqlens, kv_start, batch,
+                                          log2i(page_size), num_pages, rows_out, max_tokens, s);
+  if (e != hipSuccess) return hip_fail(e, "debug gather launch");
+  return PKC_OK;
+  PKC_TRY_END("pkc_debug_gather_rows")
+}
+
+pkc_status pkc_debug_cta_trace(const pkc_plan_info* plan, int32_t stage, const void* dev_ws,
+                               int32_t* trace_out, int64_t trace_len,
+                               int32_t max_items_per_cta, void* stream) {
+  PKC_TRY_BEGIN
+  if (!plan || plan->magic != PKC_PLAN_MAGIC) return fail(PKC_ERR_INVALID_ARG, "bad plan");
+  if (!dev_ws || plan->dev_ws != (uint64_t)(uintptr_t)dev_ws)
+    return fail(PKC_ERR_PLAN_MISMATCH, "plan was copied to another device workspace");
+  if (stage < 0 || stage > plan->num_levels) return fail(PKC_ERR_INVALID_ARG, "stage out of range");
+  if (max_items_per_cta <= 0 || !trace_out) return fail(PKC_ERR_INVALID_ARG, "bad trace buffer");
+  const bool dec = stage == plan->num_levels;
+  const int32_t ctas = dec ? plan->num_ctas : plan->level_ctas;
+  if (trace_len < (int64_t)ctas * max_items_per_cta * 8)
+    return fail(PKC_ERR_WORKSPACE_TOO_SMALL, "trace buffer too small");
+  void* ws = const_cast<void*>(dev_ws);
+  const int32_t* indptr = at<int32_t>(ws, dec ? plan->off_dec_indptr : plan->off_lvl_indptr[stage]);
+  const int32_t* items = at<int32_t>(ws, dec ? plan->off_dec_items : plan->off_lvl_items[stage]);
+  hipError_t e = pkc::launch_debug_trace(indptr, items, ctas, trace_out, max_items_per_cta,
+                                         reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "debug trace launch");
+  return PKC_OK;
+  PKC_TRY_END("pkc_debug_cta_trace")
+}
+
+pkc_status pkc_timing_enable(int32_t enable) {
+  g_timing = enable != 0;
+  return PKC_OK;
+}
+
+pkc_status pkc_timing_reset(void) {
+  PKC_TRY_BEGIN
+  std::lock_guard<std::mutex> lk(g_mu);
+  for (auto& t : g_pending) {
+    (void)hipEventSynchronize(t.stop);
+    g_free_events.push_back(t.start);
+    g_free_events.push_back(t.stop);
+  }
+  g_pending.clear();
+  for (int i = 0; i < 4; ++i) {
+    g_launches[i] = 0;
+    g_ms[i] = 0;
+  }
+  return PKC_OK;
+  PKC_TRY_END("pkc_timing_reset")
+}
+
+pkc_status pkc_timing_read(int32_t kind, int64_t* launches, double* total_ms) {
+  PKC_TRY_BEGIN
+  if (kind < 0 || kind > 3) return fail(PKC_ERR_INVALID_ARG, "kind must be 0..3");
+  std::lock_guard<std::mutex> lk(g_mu);
+  for (auto& t : g_pending) {
+    hipError_t e = hipEventSynchronize(t.stop);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    float ms = 0.f;
+    if ((e = hipEventElapsedTime(&ms, t.start, t.stop)) != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    g_launches[t.kind] += 1;
+    g_ms[t.kind] += ms;
+    g_free_events.push_back(t.start);
+    g_free_events.push_back(t.stop);
+  }
+  g_pending.clear();
+  if (launches) *launches = g_launches[kind];
+  if (total_ms) *total_ms = g_ms[kind];
+  return PKC_OK;
+  PKC_TRY_END("pkc_timing_read")
+}
+
+}  // extern "C"

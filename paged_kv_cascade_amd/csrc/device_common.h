@@ -1,0 +1,157 @@
+// Device helpers shared by the gfx950 kernels: element types, 16-byte vectors, conversions,
+// wave64 reductions inside 16-lane DPP rows, and the base-2 online-softmax primitives.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkc {
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 b8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+
+// Storage tags: the kernels move raw bits and convert explicitly.
+struct F32 {};
+struct F16 {};
+struct BF16 {};
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t u16) { return __uint_as_float(u16 << 16); }
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t u16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)u16);
+}
+// Round-to-nearest-even float -> bf16 bits (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)f);  // RNE
+}
+
+template <typename T> __device__ __forceinline__ uint16_t bits16(float x);
+template <> __device__ __forceinline__ uint16_t bits16<struct F16>(float x) { return f32_to_f16_bits(x); }
+template <> __device__ __forceinline__ uint16_t bits16<struct BF16>(float x) { return f32_to_bf16_bits(x); }
+
+template <typename T> struct Elem;
+template <> struct Elem<F32> {
+  static constexpr int kBytes = 4;
+  __device__ static float lo(uint32_t w) { return __uint_as_float(w); }
+  __device__ static void store(void* p, int64_t i, float x) { static_cast<float*>(p)[i] = x; }
+};
+template <> struct Elem<F16> {
+  static constexpr int kBytes = 2;
+  __device__ static float lo(uint32_t w) { return f16_bits_to_f32(w & 0xffffu); }
+  __device__ static float hi(uint32_t w) { return f16_bits_to_f32(w >> 16); }
+  __device__ static void store(void* p, int64_t i, float x) { static_cast<uint16_t*>(p)[i] = f32_to_f16_bits(x); }
+};
+template <> struct Elem<BF16> {
+  static constexpr int kBytes = 2;
+  __device__ static float lo(uint32_t w) { return __uint_as_float(w << 16); }
+  __device__ static float hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+  __device__ static void store(void* p, int64_t i, float x) { static_cast<uint16_t*>(p)[i] = f32_to_bf16_bits(x); }
+};
+
+// 16 bytes = one 128-bit load.
+struct alignas(16) V16 {
+  uint32_t w[4];
+};
+
+__device__ __forceinline__ V16 load16(const void* p) {
+  V16 r;
+  const uint4 x = *static_cast<const uint4*>(p);
+  r.w[0] = x.x; r.w[1] = x.y; r.w[2] = x.z; r.w[3] = x.w;
+  return r;
+}
+__device__ __forceinline__ V16 zero16() {
+  V16 r;
+  r.w[0] = r.w[1] = r.w[2] = r.w[3] = 0u;
+  return r;
+}
+
+// Partial dot product of the 16-byte slices of q and k (fp32 accumulate; products exact).
+__device__ __forceinline__ float dot16(F32, const V16& a, const V16& b) {
+  float s = __uint_as_float(a.w[0]) * __uint_as_float(b.w[0]);
+  s = fmaf(__uint_as_float(a.w[1]), __uint_as_float(b.w[1]), s);
+  s = fmaf(__uint_as_float(a.w[2]), __uint_as_float(b.w[2]), s);
+  s = fmaf(__uint_as_float(a.w[3]), __uint_as_float(b.w[3]), s);
+  return s;
+}
+__device__ __forceinline__ float dot16(F16, const V16& a, const V16& b) {
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    s = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, a.w[i]), __builtin_bit_cast(h2_t, b.w[i]), s, false);
+  return s;
+}
+__device__ __forceinline__ float dot16(BF16, const V16& a, const V16& b) {
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2_t, a.w[i]), __builtin_bit_cast(b2_t, b.w[i]), s, false);
+  return s;
+}
+
+// Unpack a 16-byte slice to floats (VEC = 4 for f32, 8 for 16-bit types).
+__device__ __forceinline__ void unpack16(F32, const V16& a, float* out) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(a.w[i]);
+}
+template <typename T>
+__device__ __forceinline__ void unpack16(T, const V16& a, float* out) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = Elem<T>::lo(a.w[i]);
+    out[2 * i + 1] = Elem<T>::hi(a.w[i]);
+  }
+}
+
+// DPP lane permutations inside 16-lane rows.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppQuadSwap1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppQuadSwap2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+// All-reduce sum over aligned groups of N lanes (N = 4, 8, 16, 32, 64).
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 4 || N == 8 || N == 16 || N == 32 || N == 64, "group size");
+  x += dpp_f<kDppQuadSwap1>(x);
+  x += dpp_f<kDppQuadSwap2>(x);
+  if constexpr (N >= 8) x += dpp_f<kDppRowHalfMirror>(x);
+  if constexpr (N >= 16) x += dpp_f<kDppRowMirror>(x);
+  if constexpr (N >= 32) x += __shfl_xor(x, 16);
+  if constexpr (N >= 64) x += __shfl_xor(x, 32);
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Base-2 attention state of one row: running max m, sum l, unnormalised accumulator.
+// Merges state (m2, l2, acc2) into (m, l, acc) over n accumulator values.
+template <int N>
+__device__ __forceinline__ void merge_state2(float& m, float& l, float* acc, float m2, float l2,
+                                             const float* acc2) {
+  const float mn = fmaxf(m, m2);
+  const float mu = (mn == kNegInf) ? 0.f : mn;
+  const float a = fast_exp2(m - mu);
+  const float b = fast_exp2(m2 - mu);
+  l = l * a + l2 * b;
+#pragma unroll
+  for (int e = 0; e < N; ++e) acc[e] = acc[e] * a + acc2[e] * b;
+  m = mn;
+}
+
+}  // namespace pkc

@@ -1,0 +1,99 @@
+// Internal launch interface between the C ABI (api.cpp) and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pkc.h"
+
+namespace pkc {
+
+// Decode / suffix stage.  One workgroup per (CTA or request, KV head).
+struct DecodeParams {
+  const void* q;             // [B, Hq, D]
+  const void* k;             // [num_pages, P, Hkv, D]
+  const void* v;
+  int64_t num_pages;
+  const int32_t* block_table;  // [B, max_blocks]
+  int32_t max_blocks;
+  const int32_t* seqlens;    // [B] (plan == nullptr only)
+  const int32_t* kv_start;   // [B] or nullptr
+  int32_t hq, hkv, page_size, page_shift;
+  float scale_log2;          // sm_scale * log2(e)
+  void* o;                   // [B, Hq, D] dtype
+  float* lse;                // [B, Hq]
+  float* st_o;               // partial states [rows, Hq, D] fp32
+  float* st_lse;             // [rows, Hq] natural-log LSE
+  const int32_t* indptr;     // plan stage indptr [#CTA + 1] or nullptr (one item per request)
+  const int32_t* items;      // plan items, 8 int32 each
+};
+
+// Multi-query (MFMA) stage of one cascade level.
+struct PrefixParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  int64_t num_pages;
+  const int32_t* page_indptr;   // [G+1]
+  const int32_t* page_indices;  // [nnz]
+  int32_t num_page_indices;
+  int32_t hq, hkv, page_size, page_shift;
+  float scale_log2;
+  float* st_o;
+  float* st_lse;
+  const int32_t* indptr;        // [#CTA + 1]
+  const int32_t* items;
+};
+
+// Plan-driven merge: request b merges merge_rows[merge_ptr[b*NL2 + l0] .. merge_ptr[b*NL2 + l1]).
+struct MergePlanParams {
+  const float* st_o;
+  const float* st_lse;
+  const int32_t* merge_ptr;
+  const int32_t* merge_rows;
+  const int32_t* req_flags;  // skip requests with flag 1 (nullptr: never skip)
+  int32_t nl2, l0, l1;
+  int32_t batch, hq;
+  void* o;
+  float* lse;
+};
+
+struct MergeGenericParams {
+  const void* o_states;
+  const float* lse_states;
+  int32_t num_states;
+  const int32_t* indptr;
+  const int32_t* indices;
+  int32_t num_outputs, states_per_output, num_heads;
+  void* o_out;
+  float* lse_out;
+};
+
+hipError_t launch_decode(pkc_dtype dt, int head_dim, int group, const DecodeParams& p, int grid_x,
+                         hipStream_t s);
+hipError_t launch_prefix(pkc_dtype dt, int head_dim, int group, int tile_q, const PrefixParams& p,
+                         int grid_x, hipStream_t s);
+hipError_t launch_merge_plan(pkc_dtype out_dt, int head_dim, const MergePlanParams& p,
+                             hipStream_t s);
+hipError_t launch_merge_generic(pkc_dtype in_dt, pkc_dtype out_dt, int head_dim,
+                                const MergeGenericParams& p, hipStream_t s);
+hipError_t launch_merge_inplace(pkc_dtype dt, int head_dim, void* o_a, float* lse_a,
+                                const void* o_b, const float* lse_b, int64_t num_states,
+                                hipStream_t s);
+hipError_t launch_debug_gather(const int32_t* block_table, int32_t max_blocks,
+                               const int32_t* seqlens, const int32_t* kv_start, int32_t batch,
+                               int32_t page_shift, int64_t num_pages, int32_t* rows_out,
+                               int32_t max_tokens, hipStream_t s);
+hipError_t launch_debug_trace(const int32_t* indptr, const int32_t* items, int32_t ctas,
+                              int32_t* trace_out, int32_t max_items_per_cta, hipStream_t s);
+
+// Physical row (page * P + slot) of token t through a page list, or -1 (shared by the decode
+// kernel's address computation and the gather debug export).
+__device__ __forceinline__ int64_t token_row(const int32_t* pages, int32_t t, int32_t page_shift,
+                                             int64_t num_pages) {
+  const int32_t pg = pages[t >> page_shift];
+  if (pg < 0 || pg >= num_pages) return -1;
+  return ((int64_t)pg << page_shift) + (t & ((1 << page_shift) - 1));
+}
+
+}  // namespace pkc

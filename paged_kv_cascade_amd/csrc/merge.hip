@@ -1,0 +1,226 @@
+// Merge kernels: n-ary merge operator over attention states ("Attention States and Recursive
+// Attention", n-ary merge equation; the maximum LSE is subtracted for stability) and the
+// binary merge in place.  One thread owns 4 consecutive head_dim elements of one (output,
+// head); states stream through in order with a running maximum, so any number of states is
+// merged in one pass.  The identity (0, -inf) results when there is nothing to merge.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace pkc {
+
+template <typename T>
+__device__ __forceinline__ void load4(const void* base, int64_t idx, float* out) {
+  if constexpr (Elem<T>::kBytes == 4) {
+    const float4 x = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx);
+    out[0] = x.x; out[1] = x.y; out[2] = x.z; out[3] = x.w;
+  } else {
+    const uint2 x = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + idx);
+    out[0] = Elem<T>::lo(x.x); out[1] = Elem<T>::hi(x.x);
+    out[2] = Elem<T>::lo(x.y); out[3] = Elem<T>::hi(x.y);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void store4(void* base, int64_t idx, const float* v) {
+  if constexpr (Elem<T>::kBytes == 4) {
+    *reinterpret_cast<float4*>(static_cast<float*>(base) + idx) = make_float4(v[0], v[1], v[2], v[3]);
+  } else {
+    uint2 x;
+    x.x = (uint32_t)bits16<T>(v[0]) | ((uint32_t)bits16<T>(v[1]) << 16);
+    x.y = (uint32_t)bits16<T>(v[2]) | ((uint32_t)bits16<T>(v[3]) << 16);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + idx) = x;
+  }
+}
+
+// Running merge of one more state (natural-log LSE `lse`, values o4) into (m, l, acc) kept in
+// base 2.
+__device__ __forceinline__ void absorb(float& m, float& l, float* acc, float lse, const float* o4) {
+  const float s = lse * kLog2e;
+  const float mn = fmaxf(m, s);
+  const float mu = (mn == kNegInf) ? 0.f : mn;
+  const float a = fast_exp2(m - mu);
+  const float w = fast_exp2(s - mu);
+  l = l * a + w;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc[e] = acc[e] * a + o4[e] * w;
+  m = mn;
+}
+
+__device__ __forceinline__ void finish(float m, float l, float* acc, float* lse_out) {
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc[e] = l > 0.f ? acc[e] * inv : 0.f;
+  *lse_out = l > 0.f ? (m + log2f(l)) * kLn2 : kNegInf;
+}
+
+template <typename TO, int D>
+__global__ __launch_bounds__(256) void merge_plan_kernel(const MergePlanParams p) {
+  constexpr int TPH = D / 4;          // threads per head
+  constexpr int HPB = 256 / TPH;      // heads per block
+  const int b = blockIdx.x;
+  if (p.req_flags && p.req_flags[b]) return;
+  const int h = blockIdx.y * HPB + threadIdx.x / TPH;
+  if (h >= p.hq) return;
+  const int d0 = (threadIdx.x % TPH) * 4;
+  const int beg = p.merge_ptr[(int64_t)b * p.nl2 + p.l0];
+  const int end = p.merge_ptr[(int64_t)b * p.nl2 + p.l1];
+  float m = kNegInf, l = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int k = beg; k < end; ++k) {
+    const int64_t r = p.merge_rows[k];
+    float o4[4];
+    load4<F32>(p.st_o, (r * p.hq + h) * D + d0, o4);
+    absorb(m, l, acc, p.st_lse[r * p.hq + h], o4);
+  }
+  float lse;
+  finish(m, l, acc, &lse);
+  store4<TO>(p.o, ((int64_t)b * p.hq + h) * D + d0, acc);
+  if (d0 == 0) p.lse[(int64_t)b * p.hq + h] = lse;
+}
+
+template <typename TI, typename TO, int D>
+__global__ __launch_bounds__(256) void merge_generic_kernel(const MergeGenericParams p) {
+  constexpr int TPH = D / 4;
+  constexpr int HPB = 256 / TPH;
+  const int i = blockIdx.x;
+  const int h = blockIdx.y * HPB + threadIdx.x / TPH;
+  if (h >= p.num_heads) return;
+  const int d0 = (threadIdx.x % TPH) * 4;
+  int beg, end;
+  if (p.indptr) {
+    beg = p.indptr[i];
+    end = p.indptr[i + 1];
+  } else {
+    beg = i * p.states_per_output;
+    end = beg + p.states_per_output;
+  }
+  float m = kNegInf, l = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int k = beg; k < end; ++k) {
+    const int64_t s = p.indices ? (int64_t)p.indices[k] : (int64_t)k;
+    if (s < 0 || s >= p.num_states) continue;
+    float o4[4];
+    load4<TI>(p.o_states, (s * p.num_heads + h) * D + d0, o4);
+    absorb(m, l, acc, p.lse_states[s * p.num_heads + h], o4);
+  }
+  float lse;
+  finish(m, l, acc, &lse);
+  store4<TO>(p.o_out, ((int64_t)i * p.num_heads + h) * D + d0, acc);
+  if (d0 == 0) p.lse_out[(int64_t)i * p.num_heads + h] = lse;
+}
+
+// Binary merge in place; written symmetrically in its two operands.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void merge_inplace_kernel(void* o_a, float* lse_a,
+                                                            const void* o_b,
+                                                            const float* lse_b, int64_t n) {
+  constexpr int TPH = D / 4;
+  const int64_t sidx = ((int64_t)blockIdx.x * 256 + threadIdx.x) / TPH;
+  if (sidx >= n) return;
+  const int d0 = (threadIdx.x % TPH) * 4;
+  float a4[4], b4[4];
+  load4<T>(o_a, sidx * D + d0, a4);
+  load4<T>(o_b, sidx * D + d0, b4);
+  const float sa = lse_a[sidx] * kLog2e, sb = lse_b[sidx] * kLog2e;
+  const float mn = fmaxf(sa, sb);
+  const float mu = (mn == kNegInf) ? 0.f : mn;
+  const float wa = fast_exp2(sa - mu), wb = fast_exp2(sb - mu);
+  const float den = wa + wb;
+  // Separately rounded products (no fused multiply-add across the operands) keep the result
+  // bit-identical when a and b are swapped.
+  float out[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    out[e] = den > 0.f ? (__fmul_rn(a4[e], wa) + __fmul_rn(b4[e], wb)) / den : 0.f;
+  // All lanes of one state sit in one wave and read lse_a in the same load instruction;
+  // the store below depends on that load, so no lane can overwrite it early.
+  store4<T>(o_a, sidx * D + d0, out);
+  if (d0 == 0) lse_a[sidx] = den > 0.f ? (mu + log2f(den)) * kLn2 : kNegInf;
+}
+
+template <typename TO>
+static hipError_t merge_plan_d(int head_dim, const MergePlanParams& p, hipStream_t s) {
+  if (p.batch <= 0) return hipSuccess;
+  if (head_dim == 64) {
+    dim3 grid(p.batch, (p.hq + 15) / 16);
+    hipLaunchKernelGGL((merge_plan_kernel<TO, 64>), grid, dim3(256), 0, s, p);
+  } else if (head_dim == 128) {
+    dim3 grid(p.batch, (p.hq + 7) / 8);
+    hipLaunchKernelGGL((merge_plan_kernel<TO, 128>), grid, dim3(256), 0, s, p);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_plan(pkc_dtype out_dt, int head_dim, const MergePlanParams& p,
+                             hipStream_t s) {
+  switch (out_dt) {
+    case PKC_F32: return merge_plan_d<F32>(head_dim, p, s);
+    case PKC_F16: return merge_plan_d<F16>(head_dim, p, s);
+    case PKC_BF16: return merge_plan_d<BF16>(head_dim, p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename TI, typename TO>
+static hipError_t merge_generic_d(int head_dim, const MergeGenericParams& p, hipStream_t s) {
+  if (p.num_outputs <= 0) return hipSuccess;
+  if (head_dim == 64) {
+    dim3 grid(p.num_outputs, (p.num_heads + 15) / 16);
+    hipLaunchKernelGGL((merge_generic_kernel<TI, TO, 64>), grid, dim3(256), 0, s, p);
+  } else if (head_dim == 128) {
+    dim3 grid(p.num_outputs, (p.num_heads + 7) / 8);
+    hipLaunchKernelGGL((merge_generic_kernel<TI, TO, 128>), grid, dim3(256), 0, s, p);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <typename TI>
+static hipError_t merge_generic_o(pkc_dtype out_dt, int head_dim, const MergeGenericParams& p,
+                                  hipStream_t s) {
+  switch (out_dt) {
+    case PKC_F32: return merge_generic_d<TI, F32>(head_dim, p, s);
+    case PKC_F16: return merge_generic_d<TI, F16>(head_dim, p, s);
+    case PKC_BF16: return merge_generic_d<TI, BF16>(head_dim, p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_merge_generic(pkc_dtype in_dt, pkc_dtype out_dt, int head_dim,
+                                const MergeGenericParams& p, hipStream_t s) {
+  switch (in_dt) {
+    case PKC_F32: return merge_generic_o<F32>(out_dt, head_dim, p, s);
+    case PKC_F16: return merge_generic_o<F16>(out_dt, head_dim, p, s);
+    case PKC_BF16: return merge_generic_o<BF16>(out_dt, head_dim, p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+static hipError_t merge_inplace_d(int head_dim, void* o_a, float* lse_a, const void* o_b,
+                                  const float* lse_b, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t threads = n * (head_dim / 4);
+  dim3 grid((unsigned)((threads + 255) / 256));
+  if (head_dim == 64)
+    hipLaunchKernelGGL((merge_inplace_kernel<T, 64>), grid, dim3(256), 0, s, o_a, lse_a, o_b, lse_b, n);
+  else if (head_dim == 128)
+    hipLaunchKernelGGL((merge_inplace_kernel<T, 128>), grid, dim3(256), 0, s, o_a, lse_a, o_b, lse_b, n);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_inplace(pkc_dtype dt, int head_dim, void* o_a, float* lse_a,
+                                const void* o_b, const float* lse_b, int64_t num_states,
+                                hipStream_t s) {
+  switch (dt) {
+    case PKC_F32: return merge_inplace_d<F32>(head_dim, o_a, lse_a, o_b, lse_b, num_states, s);
+    case PKC_F16: return merge_inplace_d<F16>(head_dim, o_a, lse_a, o_b, lse_b, num_states, s);
+    case PKC_BF16: return merge_inplace_d<BF16>(head_dim, o_a, lse_a, o_b, lse_b, num_states, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pkc

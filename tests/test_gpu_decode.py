@@ -1,0 +1,258 @@
+"""GPU parity of the paged decode kernel and the merge kernels against the fp64 oracle.
+
+Covers the "Paged attention" worked example (fp32, NaN-poisoned unreferenced
+rows, two-chunk split merged in both orders), the integer gather (bit-exact),
+the LLaMA2-7B-shaped decode at full size (sampled requests), closed-form
+checks (uniform scores count tokens, a dominant key picks its row), and a
+matrix of small ragged cases over dtype, head_dim, group size and page size.
+"""
+
+import math
+import random
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as oatt
+from oracle import indexing as oidx
+from oracle import merge as omerge
+from paged_kv_cascade_amd import workloads
+from tests.gpu_helpers import PoolView, check_state, gpu, host, needs_gpu, say
+
+pytestmark = [gpu, needs_gpu]
+
+
+@pytest.fixture(scope="module")
+def api():
+    from paged_kv_cascade_amd import api as _api
+    return _api
+
+
+def _oracle_decode(w, requests=None, kv_start=None, seqlens=None):
+    bt = w.block_table.cpu().numpy()
+    lens = (w.cache_seqlens if seqlens is None else seqlens).cpu().numpy()
+    ks = None if kv_start is None else kv_start.cpu().numpy()
+    return oatt.batch_decode(host(w.q), PoolView(w.k_pool), PoolView(w.v_pool), bt, lens,
+                             w.page_size, w.sm_scale, kv_start=ks, requests=requests)
+
+
+def test_tiny_worked_example(api):
+    say("case: tiny paged decode, HF worked example, fp32, NaN-poisoned unreferenced rows")
+    w = workloads.tiny_paged(device="cuda")
+    api.validate_block_table(w.block_table, w.cache_seqlens, w.page_size, w.num_pages)
+    o, lse = api.batch_decode_paged(w.q, w.k_pool, w.v_pool, w.block_table, w.cache_seqlens,
+                                    sm_scale=w.sm_scale)
+    torch.cuda.synchronize()
+    O, L = _oracle_decode(w)
+    check_state(o, lse, O, L, torch.float32, "tiny example")
+
+
+def test_tiny_two_chunks_merged_both_orders(api):
+    say("case: tiny example split into two chunks per sequence, merged both orders")
+    w = workloads.tiny_paged(device="cuda")
+    cuts = torch.tensor(w.extra["cuts"], dtype=torch.int32, device="cuda")
+    oa, la = api.batch_decode_paged(w.q, w.k_pool, w.v_pool, w.block_table, cuts, sm_scale=w.sm_scale)
+    ob, lb = api.batch_decode_paged(w.q, w.k_pool, w.v_pool, w.block_table, w.cache_seqlens,
+                                    kv_start=cuts, sm_scale=w.sm_scale)
+    O, L = _oracle_decode(w)
+    Oa, La = _oracle_decode(w, seqlens=cuts)
+    check_state(oa, la, Oa, La, torch.float32, "chunk [0, cut)")
+    Ob, Lb = _oracle_decode(w, kv_start=cuts)
+    check_state(ob, lb, Ob, Lb, torch.float32, "chunk [cut, len)")
+    B, H, D = w.q.shape
+    ab = torch.stack([oa, ob], 1).reshape(2 * B, H, D).contiguous()
+    lab = torch.stack([la, lb], 1).reshape(2 * B, H).contiguous()
+    ba = torch.stack([ob, oa], 1).reshape(2 * B, H, D).contiguous()
+    lba = torch.stack([lb, la], 1).reshape(2 * B, H).contiguous()
+    o1, l1 = api.merge_states(ab, lab, states_per_output=2)
+    o2, l2 = api.merge_states(ba, lba, states_per_output=2)
+    check_state(o1, l1, O, L, torch.float32, "merge (a, b)")
+    check_state(o2, l2, O, L, torch.float32, "merge (b, a)")
+    x_o, x_l = oa.clone(), la.clone()
+    api.merge_state_inplace(x_o, x_l, ob, lb)
+    y_o, y_l = ob.clone(), lb.clone()
+    api.merge_state_inplace(y_o, y_l, oa, la)
+    check_state(x_o, x_l, O, L, torch.float32, "in-place a <- a + b")
+    assert torch.equal(x_o, y_o) and torch.equal(x_l, y_l), "binary merge not bitwise commutative"
+
+
+def test_gather_rows_worked_example_bit_exact(api):
+    say("case: integer gather of the HF worked example (bit-exact)")
+    w = workloads.tiny_paged(device="cuda")
+    T = 4 * w.page_size + 3
+    rows = api.debug_gather_rows(w.block_table, w.cache_seqlens, w.page_size, w.num_pages, T).cpu().numpy()
+    bt = w.block_table.cpu().numpy()
+    for b in range(w.batch):
+        L = int(w.cache_seqlens[b])
+        pages, slots = oidx.token_pages(bt[b], 0, L, w.page_size)
+        exp = np.full(T, -1)
+        exp[:L] = pages * w.page_size + slots
+        assert np.array_equal(rows[b], exp), f"request {b}"
+    # a kv_start window
+    ks = torch.tensor([3, 31, 40], dtype=torch.int32, device="cuda")
+    rows = api.debug_gather_rows(w.block_table, w.cache_seqlens, w.page_size, w.num_pages, T, kv_start=ks).cpu().numpy()
+    for b in range(w.batch):
+        L, s = int(w.cache_seqlens[b]), int(ks[b])
+        pages, slots = oidx.token_pages(bt[b], s, L, w.page_size)
+        exp = np.full(T, -1)
+        exp[s:L] = pages * w.page_size + slots
+        assert np.array_equal(rows[b], exp)
+
+
+def test_llama_shape_decode_full_size(api):
+    say("case: paged decode b64 h32 d128 len4096 p16 fp16, permuted pages (full size, sampled oracle)")
+    w = workloads.paged_decode(device="cuda")
+    api.validate_block_table(w.block_table.cpu(), w.cache_seqlens.cpu(), w.page_size, w.num_pages)
+    o, lse = api.batch_decode_paged(w.q, w.k_pool, w.v_pool, w.block_table, w.cache_seqlens,
+                                    sm_scale=w.sm_scale)
+    o2, lse2 = api.batch_decode_paged(w.q, w.k_pool, w.v_pool, w.block_table, w.cache_seqlens,
+                                      sm_scale=w.sm_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2), "repeat run differs"
+    reqs = [0, 17, 42, 63]
+    O, L = _oracle_decode(w, requests=reqs)
+    check_state(o, lse, O, L, torch.float16, "decode b64 len4096", rows=reqs)
+
+
+def test_uniform_scores_count_tokens(api):
+    """q = 0: every score is 0, so LSE = ln(number of tokens read) -- a closed form that
+    exposes a wrong token count -- and O = mean of the gathered values."""
+    say("case: uniform scores (q = 0), ragged lengths, fp16")
+    w = workloads.paged_decode(batch=6, heads=4, kv_len=1000, page_size=16, seed=77, device="cuda")
+    lens = torch.tensor([1000, 999, 17, 16, 1, 0], dtype=torch.int32, device="cuda")
+    q0 = torch.zeros_like(w.q)
+    o, lse = api.batch_decode_paged(q0, w.k_pool, w.v_pool, w.block_table, lens, sm_scale=w.sm_scale)
+    torch.cuda.synchronize()
+    L = lse.cpu().double().numpy()
+    for b, n in enumerate(lens.tolist()):
+        if n == 0:
+            assert np.all(np.isneginf(L[b]))
+            assert torch.all(o[b] == 0)
+        else:
+            assert np.max(np.abs(L[b] - math.log(n))) < 1e-5, f"request {b}"
+    O, Lr = oatt.batch_decode(np.zeros(tuple(w.q.shape)), PoolView(w.k_pool), PoolView(w.v_pool),
+                              w.block_table.cpu().numpy(), lens.cpu().numpy(), w.page_size, w.sm_scale)
+    check_state(o, lse, O, Lr, torch.float16, "uniform scores")
+
+
+def test_dominant_key_selects_its_row(api):
+    """One key aligned with q dominates: O equals that token's value row."""
+    say("case: dominant key, fp16")
+    w = workloads.paged_decode(batch=3, heads=2, kv_len=300, page_size=16, seed=78, device="cuda")
+    q = torch.zeros_like(w.q)
+    q[..., 0] = 4.0
+    k = w.k_pool.clone()
+    k[..., 0] = 0.0
+    targets = [5, 257, 299]
+    for b, t in enumerate(targets):
+        page = int(w.block_table[b, t // 16])
+        k[page, t % 16, :, 0] = 16.0
+    o, lse = api.batch_decode_paged(q, k, w.v_pool, w.block_table, w.cache_seqlens, sm_scale=1.0)
+    torch.cuda.synchronize()
+    for b, t in enumerate(targets):
+        page = int(w.block_table[b, t // 16])
+        v = w.v_pool[page, t % 16].float()
+        assert torch.max(torch.abs(o[b].float() - v)) < 2e-3
+    O, L = oatt.batch_decode(host(q), PoolView(k), PoolView(w.v_pool), w.block_table.cpu().numpy(),
+                             w.cache_seqlens.cpu().numpy(), 16, 1.0)
+    check_state(o, lse, O, L, torch.float16, "dominant key")
+
+
+def _ragged_case(dtype, D, g, P, seed, hkv=2, with_start=False):
+    rng = random.Random(seed)
+    B = 7
+    lens = [0, 1, P - 1 if P > 1 else 2, P, P + 1, rng.randint(100, 700), rng.randint(1, 300)]
+    npg = [-(-n // P) for n in lens]
+    num_pages = sum(npg) + 5
+    perm = torch.randperm(num_pages, generator=torch.Generator().manual_seed(seed)).tolist()
+    maxb = max(npg) + 1
+    bt = torch.full((B, maxb), -1, dtype=torch.int32)
+    used = torch.zeros(num_pages, P, dtype=torch.bool)
+    off = 0
+    for b, n in enumerate(npg):
+        bt[b, :n] = torch.tensor(perm[off:off + n], dtype=torch.int32)
+        off += n
+        for t in range(lens[b]):
+            used[int(bt[b, t // P]), t % P] = True
+    gen = torch.Generator(device="cuda").manual_seed(seed)
+    q = torch.randn(B, hkv * g, D, generator=gen, device="cuda").to(dtype)
+    k = torch.randn(num_pages, P, hkv, D, generator=gen, device="cuda").to(dtype)
+    v = torch.randn(num_pages, P, hkv, D, generator=gen, device="cuda").to(dtype)
+    k[~used.cuda()] = float("nan")
+    v[~used.cuda()] = float("nan")
+    ks = None
+    if with_start:
+        ks = torch.tensor([min(n, rng.randint(0, n)) for n in lens], dtype=torch.int32)
+    return q, k, v, bt, torch.tensor(lens, dtype=torch.int32), ks
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("g", [1, 2, 4, 8])
+@pytest.mark.parametrize("P", [1, 4, 16, 64])
+def test_ragged_decode_matrix(api, dtype, D, g, P):
+    seed = {torch.float32: 1, torch.float16: 2, torch.bfloat16: 3}[dtype] * 10000 + D * 10 + g * 1000 + P
+    with_start = (D + g + P) % 2 == 0
+    say(f"case: ragged decode dtype={dtype} D={D} g={g} P={P} kv_start={with_start}")
+    q, k, v, bt, lens, ks = _ragged_case(dtype, D, g, P, seed, with_start=with_start)
+    api.validate_block_table(bt, lens, P, k.shape[0], kv_start=ks)
+    btd, ld = bt.cuda(), lens.cuda()
+    ksd = ks.cuda() if ks is not None else None
+    o, lse = api.batch_decode_paged(q, k, v, btd, ld, kv_start=ksd, sm_scale=1.0 / math.sqrt(D))
+    torch.cuda.synchronize()
+    O, L = oatt.batch_decode(host(q), PoolView(k), PoolView(v), bt.numpy(), lens.numpy(), P,
+                             1.0 / math.sqrt(D), kv_start=None if ks is None else ks.numpy())
+    check_state(o, lse, O, L, dtype, f"ragged {dtype} D{D} g{g} P{P}")
+
+
+@pytest.mark.parametrize("in_dt,out_dt", [(torch.float32, torch.float32), (torch.float32, torch.float16),
+                                          (torch.float16, torch.float32), (torch.bfloat16, torch.bfloat16)])
+@pytest.mark.parametrize("D", [64, 128])
+def test_merge_states_matches_oracle(api, in_dt, out_dt, D):
+    say(f"case: merge_states {in_dt}->{out_dt} D={D}")
+    gen = torch.Generator(device="cuda").manual_seed(D)
+    S, H = 40, 5
+    o = torch.randn(S, H, D, generator=gen, device="cuda").to(in_dt)
+    lse = (torch.randn(S, H, generator=gen, device="cuda") * 3).float()
+    lse[3] = float("-inf")
+    lse[7, 2] = float("-inf")
+    # CSR: output i merges a list of state indices (with repeats, an empty list, and -inf states)
+    lists = [[0, 1, 2], [3], [], [4, 5, 6, 7, 8, 9, 10], [39, 0], [3, 7], list(range(11, 39))]
+    indptr = torch.tensor(np.cumsum([0] + [len(x) for x in lists]), dtype=torch.int32, device="cuda")
+    indices = torch.tensor(sum(lists, []), dtype=torch.int32, device="cuda")
+    mo, ml = api.merge_states(o, lse, indptr=indptr, indices=indices, out_dtype=out_dt)
+    torch.cuda.synchronize()
+    O = host(o)
+    Ls = lse.cpu().double().numpy()
+    ref_o = np.zeros((len(lists), H, D))
+    ref_l = np.zeros((len(lists), H))
+    for i, idx in enumerate(lists):
+        ref_o[i], ref_l[i] = omerge.merge_many(O[idx], Ls[idx]) if idx else omerge.merge_many(np.zeros((0, H, D)), np.zeros((0, H)))
+    tol = torch.float32 if (in_dt == torch.float32 and out_dt == torch.float32) else torch.float16
+    check_state(mo, ml, ref_o, ref_l, tol, "merge csr")
+    # dense form: 8 outputs x 5 states each
+    mo, ml = api.merge_states(o, lse, states_per_output=5, out_dtype=out_dt)
+    ref = [omerge.merge_many(O[5 * i:5 * i + 5], Ls[5 * i:5 * i + 5]) for i in range(8)]
+    check_state(mo, ml, np.stack([r[0] for r in ref]), np.stack([r[1] for r in ref]), tol, "merge dense")
+
+
+def test_merge_inplace_matches_oracle_and_is_symmetric(api):
+    say("case: binary in-place merge fp32/bf16")
+    gen = torch.Generator(device="cuda").manual_seed(3)
+    for dt in (torch.float32, torch.bfloat16):
+        a = torch.randn(9, 4, 128, generator=gen, device="cuda").to(dt)
+        b = torch.randn(9, 4, 128, generator=gen, device="cuda").to(dt)
+        la = torch.randn(9, 4, generator=gen, device="cuda") * 4
+        lb = torch.randn(9, 4, generator=gen, device="cuda") * 4
+        la[0] = float("-inf")
+        lb[1] = float("-inf")
+        la[2] = lb[2] = float("-inf")
+        ro, rl = omerge.merge_pair(host(a), la.cpu().double().numpy(), host(b), lb.cpu().double().numpy())
+        x, xl = a.clone(), la.clone()
+        api.merge_state_inplace(x, xl, b, lb)
+        y, yl = b.clone(), lb.clone()
+        api.merge_state_inplace(y, yl, a, la)
+        torch.cuda.synchronize()
+        check_state(x, xl, ro, rl, torch.float32 if dt == torch.float32 else torch.float16, f"inplace {dt}")
+        assert torch.equal(x, y) and torch.equal(xl, yl)
