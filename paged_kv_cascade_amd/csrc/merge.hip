@@ -124,12 +124,18 @@ __global__ __launch_bounds__(256) void merge_inplace_kernel(void* o_a, float* ls
   const float mu = (mn == kNegInf) ? 0.f : mn;
   const float wa = fast_exp2(sa - mu), wb = fast_exp2(sb - mu);
   const float den = wa + wb;
-  // Separately rounded products (no fused multiply-add across the operands) keep the result
-  // bit-identical when a and b are swapped.
+  // Separately rounded products (contraction into a fused multiply-add is switched off) keep
+  // the result bit-identical when a and b are swapped.
   float out[4];
+  {
+#pragma clang fp contract(off)
 #pragma unroll
-  for (int e = 0; e < 4; ++e)
-    out[e] = den > 0.f ? (__fmul_rn(a4[e], wa) + __fmul_rn(b4[e], wb)) / den : 0.f;
+    for (int e = 0; e < 4; ++e) {
+      const float x = a4[e] * wa;
+      const float y = b4[e] * wb;
+      out[e] = den > 0.f ? (x + y) / den : 0.f;
+    }
+  }
   // All lanes of one state sit in one wave and read lse_a in the same load instruction;
   // the store below depends on that load, so no lane can overwrite it early.
   store4<T>(o_a, sidx * D + d0, out);

@@ -237,6 +237,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefix_kernel(const PrefixParams 
           for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
+              // P enters the PV product rounded to the operand type, but the denominator
+              // (and so the LSE) sums the fp32 weights: with bf16, summing rounded weights
+              // would move LSE by up to 2^-9.
               pr[mt][i] = fast_exp2(fmaf(s[mt][nt][i], p.scale_log2, -mu));
               psum += pr[mt][i];
             }
