@@ -1,0 +1,302 @@
+"""Benchmark of the cascade decode step on one MI355X.
+
+Workload: shared prefix of 32768 tokens (one contiguous run of page-size-16 pages) plus 256
+unique tokens per request in randomly permuted pages, batch 128, 32 heads x 128, fp16, q/k/v
+~ N(0,1) * 0.5 -- the LLaMA2-7B-shaped setting of the "Cascade Inference" blog's evaluation.
+
+One step = what a serving loop does per generated token for one layer: the CPU plan of the
+step (load-balancing plan + level work lists, copied asynchronously to the device workspace)
+and the cascade run (MFMA prefix kernel, suffix decode kernel, merge).  Inputs are resident in
+HBM before the timed region.  Printed: one JSON line with the achieved algorithmic KV bytes/s
+(prefix read once + every suffix), steps/s, the dominant kernel's roofline (HIP events around
+each launch on the launch stream), HBM traffic from rocprofv3 counters when profiles/ holds
+them for the current kernel sources, and the fp64 CPU oracle timed on a bounded sample.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KV bytes/s from HBM (% of peak) + decode steps/s, cascade 32K prefix, batch 128"
+PEAK_HBM_GBPS = 8000.0
+KERNEL_SOURCES = ["paged_kv_cascade_amd/csrc/prefix.hip", "paged_kv_cascade_amd/csrc/decode.hip",
+                  "paged_kv_cascade_amd/csrc/merge.hip", "paged_kv_cascade_amd/csrc/device_common.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "cascade32k_b128_hbm_traffic.json")
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-requests", type=int, default=16,
+                    help="requests of the CPU oracle sample (all 32 heads each)")
+    ap.add_argument("--cpu-baseline-only", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="run only a 1 GiB device copy (counter calibration under rocprofv3)")
+    return ap.parse_args()
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    a = torch.ones(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+
+
+class Step:
+    """Buffers and per-step calls of the serving loop."""
+
+    def __init__(self, api, w):
+        import torch
+        self.api, self.w = api, w
+        self.levels = [{"qo_indptr": lv["qo_indptr"], "kv_lens": lv["kv_lens"]} for lv in w.levels]
+        self.params = api.make_params(w.batch, w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size)
+        # Two pinned host buffers used alternately: the CPU may write step i+1's plan while
+        # the copy of step i's plan is still queued.  One device workspace (fixed pointers).
+        self.ws = [api.Workspace(self.params, self.levels) for _ in range(2)]
+        for k in (1,):
+            self.ws[k].device = self.ws[0].device
+        self.copy_done = [None, None]
+        self.kv_lens = w.cache_seqlens.cpu().tolist()
+        self.devs, self.keep = [], []
+        for lv in w.levels:
+            d, k = api.level_dev(lv)
+            self.devs.append(d)
+            self.keep.append(k)
+        self.out = torch.empty_like(w.q)
+        self.lse = torch.empty(w.batch, w.num_qo_heads, dtype=torch.float32, device="cuda")
+        self.i = 0
+        self.info = self.plan()
+
+    def plan(self):
+        import torch
+        k = self.i % 2
+        if self.copy_done[k] is not None:
+            self.copy_done[k].synchronize()
+        info = self.api.plan(self.params, self.kv_lens, self.levels, workspace=self.ws[k])
+        ev = torch.cuda.Event()
+        ev.record()
+        self.copy_done[k] = ev
+        self.i += 1
+        return info
+
+    def run(self, info):
+        w = self.w
+        self.api.cascade_decode(info, w.q, w.k_pool, w.v_pool, self.devs, w.block_table, w.cache_seqlens,
+                                sm_scale=w.sm_scale, out=self.out, lse=self.lse)
+
+    def __call__(self):
+        self.run(self.plan())
+
+
+def cpu_oracle_baseline(n_req):
+    """The fp64 oracle (one softmax over each request's 33,024 gathered tokens, every head) on a
+    sample of requests of the same workload generated on the host, one worker process per host
+    core (BLAS pinned to one thread per worker); scaled to a full 128-request step.  Runs in a
+    process that never touches the GPU."""
+    import multiprocessing as mp
+
+    import numpy as np
+
+    from paged_kv_cascade_amd import workloads
+
+    w = workloads.cascade_two_level(device="cpu")
+    alg_bytes = w.algorithmic_kv_bytes()
+    global _CPU_CTX
+    _CPU_CTX = (w.q.float().double().numpy(), w.k_pool.numpy(), w.v_pool.numpy(), w.page_size,
+                w.sm_scale, w.levels, w.block_table.numpy(), w.cache_seqlens.numpy())
+    cores = max(1, min(16, os.cpu_count() or 1))
+    reqs = list(range(0, w.batch, max(1, w.batch // n_req)))[:n_req]
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(cores, initializer=_cpu_worker_init) as pool:
+        outs = pool.map(_cpu_one_request, reqs)
+    dt = time.perf_counter() - t0
+    assert all(np.all(np.isfinite(o)) for o in outs)
+    step_s = dt * w.batch / len(reqs)
+    return {"value": round(alg_bytes / step_s / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "steps_per_s": round(1.0 / step_s, 5), "seconds_per_step": round(step_s, 3),
+            "sample": f"{len(reqs)} of {w.batch} requests x all {w.num_qo_heads} heads "
+                      f"(33,024 tokens each) in {dt:.1f} s wall on {cores} worker processes, "
+                      f"scaled to one 128-request step"}
+
+
+_CPU_CTX = None
+
+
+def _cpu_worker_init():
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:
+        pass
+
+
+def _cpu_one_request(b):
+    from oracle import attention as oatt
+    q, k, v, P, scale, levels, bt, sl = _CPU_CTX
+    O, L = oatt.cascade_decode(q, k, v, P, scale, levels, bt, sl, requests=[b])
+    return O[b]
+
+
+def run_cpu_baseline_child(n_req):
+    """Starts the CPU-oracle leg as a child process (before this process uses the GPU)."""
+    import subprocess
+    r = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-baseline-only",
+                        "--cpu-requests", str(n_req)], capture_output=True, text=True, timeout=900)
+    if r.returncode != 0:
+        print(r.stderr[-2000:], file=sys.stderr, flush=True)
+        return None
+    return json.loads(r.stdout.strip().splitlines()[-1])
+
+
+def load_traffic(src_hash):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None when it is
+    missing or was taken on other kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != src_hash:
+        return None
+    return t
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+                          "n_gpus_requested": args.gpus}), flush=True)
+        sys.exit(2)
+    if args.cpu_baseline_only:
+        print(json.dumps(cpu_oracle_baseline(args.cpu_requests)), flush=True)
+        return
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("# cpu oracle baseline (child process, host only) ...", file=sys.stderr, flush=True)
+        cpu = run_cpu_baseline_child(args.cpu_requests)
+    import torch
+
+    if args.copy_calib:
+        copy_calibration()
+        return
+    from paged_kv_cascade_amd import api, workloads
+
+    t_setup = time.perf_counter()
+    w = workloads.cascade_two_level(device="cuda")
+    alg_bytes = w.algorithmic_kv_bytes()                  # 1,073,741,824
+    prefix_bytes = sum(w.levels[0]["kv_lens"]) * w.num_kv_heads * w.head_dim * 2 * w.esize
+    suffix_bytes = alg_bytes - prefix_bytes
+    step = Step(api, w)
+    torch.cuda.synchronize()
+    print(f"# setup {time.perf_counter() - t_setup:.1f}s; workload {w.name}; "
+          f"{alg_bytes} algorithmic KV bytes per step", file=sys.stderr, flush=True)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Timed region: exactly K serving-loop steps.
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = 1e3 * elapsed / args.steps
+
+    # Device-only steps (one plan, K runs) -- the cost of the kernels alone.
+    info = step.plan()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step.run(info)
+    torch.cuda.synchronize()
+    ms_dev = 1e3 * (time.perf_counter() - t0) / args.steps
+
+    # Plan CPU time alone.
+    t0 = time.perf_counter()
+    for _ in range(50):
+        step.plan()
+    ms_plan = 1e3 * (time.perf_counter() - t0) / 50
+    torch.cuda.synchronize()
+
+    # Per-kernel durations with HIP events recorded around each launch on its stream.
+    api.timing_reset()
+    api.timing_enable(True)
+    for _ in range(args.steps):
+        step.run(info)
+    torch.cuda.synchronize()
+    kern = {}
+    for kind, name in ((api.KIND_PREFIX, "prefix_mfma"), (api.KIND_DECODE, "suffix_decode"),
+                       (api.KIND_MERGE_PLAN, "merge")):
+        n, ms = api.timing_read(kind)
+        kern[name] = {"launches": n, "avg_us": round(1e3 * ms / max(1, n), 2)}
+    api.timing_enable(False)
+    kern["prefix_mfma"]["alg_bytes"] = prefix_bytes
+    kern["suffix_decode"]["alg_bytes"] = suffix_bytes
+    for name in ("prefix_mfma", "suffix_decode"):
+        k = kern[name]
+        k["achieved_GBps"] = round(k["alg_bytes"] / (k["avg_us"] * 1e-6) / 1e9, 1)
+        k["frac_of_peak"] = round(k["achieved_GBps"] / PEAK_HBM_GBPS, 4)
+    dom = max(("prefix_mfma", "suffix_decode"), key=lambda n: kern[n]["avg_us"])
+    src_hash = kernel_source_hash()
+    traffic = load_traffic(src_hash)
+    roof = {"bound": "hbm", "kernel": dom, "achieved": kern[dom]["achieved_GBps"], "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s", "frac": kern[dom]["frac_of_peak"],
+            "traffic": (traffic or {}).get(dom, {}).get("hbm_bytes_per_launch") if traffic else None,
+            "alg_bytes_per_launch": kern[dom]["alg_bytes"], "avg_launch_us": kern[dom]["avg_us"]}
+
+    value = alg_bytes / (ms_step * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "prefix_len": w.levels[0]["kv_lens"][0],
+                   "suffix_len": int(w.cache_seqlens[0]), "heads": w.num_qo_heads, "head_dim": w.head_dim,
+                   "page_size": w.page_size, "alg_kv_bytes_per_step": alg_bytes},
+        "steps_per_s": round(1e3 / ms_step, 1),
+        "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBPS, 2),
+        "ms_per_step_device_only": round(ms_dev, 4),
+        "ms_plan_cpu": round(ms_plan, 4),
+        "kernels": kern,
+        "roofline": roof,
+        "kernel_source_hash": src_hash,
+    }
+    line["cpu_baseline"] = cpu
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

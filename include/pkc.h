@@ -105,8 +105,9 @@ typedef struct pkc_plan_params {
   int32_t num_kv_heads; /* Hkv (divides Hq) */
   int32_t head_dim;     /* D */
   int32_t page_size;    /* P */
-  int32_t num_ctas;     /* #CTA of the decode stage; 0 -> 2 x compute units of the current device */
-  int32_t level_ctas;   /* #CTA of every cascade level; 0 -> max(1, ceil(2 x CUs / Hkv)) */
+  int32_t num_ctas;     /* #CTA of the decode stage; 0 -> ceil(8 x compute units / Hkv), so the
+                           stage launches about 8 workgroups per compute unit */
+  int32_t level_ctas;   /* #CTA of every cascade level; 0 -> ceil(2 x compute units / Hkv) */
   int32_t level_tile_q; /* T_q of the cascade levels (queries per tile); 0 -> 128 / (Hq/Hkv) */
   int32_t chunk_align;  /* round L_kv up to a multiple of this; 0 or 1 -> no rounding */
   int32_t enable_split; /* 0 -> L_kv = longest KV length (one chunk per tile, no split-KV) */
@@ -148,6 +149,7 @@ typedef struct pkc_plan_info {
   int32_t dec_items;       /* work items of the decode stage */
   int32_t dec_slots;       /* partial slots of the decode stage */
   int32_t dec_kv_chunk;    /* L_kv of the decode stage */
+  int32_t dec_waves;       /* waves per decode workgroup (1, 2 or 4) chosen from the item sizes */
   int32_t lvl_groups[PKC_MAX_LEVELS];
   int32_t lvl_tile_q[PKC_MAX_LEVELS];
   int32_t lvl_items[PKC_MAX_LEVELS];
@@ -198,7 +200,10 @@ pkc_status pkc_plan_buffer_sizes(const pkc_plan_params* params, const pkc_level_
  *   merge_ptr    [B, num_levels + 2]: the merge rows of request b for level l are
  *                merge_rows[merge_ptr[b][l] .. merge_ptr[b][l+1]) (level num_levels = the
  *                request's own KV), in merge order: levels ascending, chunks ascending;
- *   merge_rows   state rows; req_flags [B]: 1 when the decode stage writes the output.
+ *   merge_rows   state rows; req_flags [B]: 1 when the decode stage writes the output (the
+ *                request's own KV is a single chunk; that chunk's workgroup first folds in
+ *                the request's level states listed in merge_rows), 0 when the merge kernel
+ *                does.
  */
 pkc_status pkc_plan(const pkc_plan_params* params, const int32_t* kv_lens_h,
                     const pkc_level_host* levels_h, int32_t num_levels, void* host_buf,
@@ -276,8 +281,8 @@ pkc_status pkc_merge_state_inplace(void* o_a, float* lse_a, const void* o_b, con
  * kernel over every request's own KV (block_table rows, tokens [0, suffix_seqlens[b]) per the
  * plan); then one merge per request of all its states in the order levels ascending, chunks
  * ascending, own KV last.  The plan must have been built with the same levels and with
- * kv_lens_h == suffix_seqlens.  Requests that no level covers and whose own KV is a single
- * chunk are written directly by the decode kernel.
+ * kv_lens_h == suffix_seqlens.  A request whose own KV is a single chunk is finished by the
+ * decode kernel (which folds in its level states); the merge kernel finishes the others.
  */
 pkc_status pkc_cascade_decode(const pkc_plan_info* plan, const void* q, const void* k_pool,
                               const void* v_pool, int64_t num_pages,

@@ -154,8 +154,10 @@ def cascade_plan(batch, levels, suffix_kv_lens, num_ctas, level_ctas,
     Each level is one stage: the query tile of a group is T_q consecutive
     requests of the group, its KV is the group's shared run.  Level items
     always write partial states.  The decode stage has one query per request
-    (T_q = 1); one of its items writes through only when it is its request's
-    only chunk and no level covers the request.
+    (T_q = 1); an item that is its request's only chunk writes the final
+    output (write-through), after folding in the request's level states
+    listed in its merge list (reading R24); every other request is finished
+    by the merge pass.
 
     Merge order (reading R9): levels in order, chunks ascending, then the
     request's own chunks ascending.  A merge entry is (stage, slot, row):
@@ -163,22 +165,17 @@ def cascade_plan(batch, levels, suffix_kv_lens, num_ctas, level_ctas,
     tile.
     """
     lvl_plans = []
-    covered = [False] * batch
     for li, lv in enumerate(levels):
         qi = [int(x) for x in lv["qo_indptr"]]
         qo_lens = [qi[g + 1] - qi[g] for g in range(len(qi) - 1)]
         st = lpt_plan(qo_lens, lv["kv_lens"], level_tile_q[li], level_ctas, alpha,
                       beta, chunk_align, enable_split)
         assign_slots(st, lambda r: False)
-        for it in st.items:
-            b0 = qi[it.req] + it.tile * level_tile_q[li]
-            for b in range(b0, b0 + it.lq):
-                covered[b] = True
         lvl_plans.append(st)
 
     suf = lpt_plan([1] * batch, suffix_kv_lens, 1, num_ctas, alpha, beta,
                    chunk_align, enable_split)
-    assign_slots(suf, lambda r: not covered[r])
+    assign_slots(suf, lambda r: True)
 
     merge = [[] for _ in range(batch)]
     wt = [False] * batch

@@ -66,6 +66,7 @@ class PlanInfo(ctypes.Structure):
                 ("num_levels", ctypes.c_int32), ("num_ctas", ctypes.c_int32),
                 ("level_ctas", ctypes.c_int32), ("dec_items", ctypes.c_int32),
                 ("dec_slots", ctypes.c_int32), ("dec_kv_chunk", ctypes.c_int32),
+                ("dec_waves", ctypes.c_int32),
                 ("lvl_groups", _L8), ("lvl_tile_q", _L8), ("lvl_items", _L8),
                 ("lvl_kv_chunk", _L8), ("lvl_row_base", _L8),
                 ("dec_row_base", ctypes.c_int32), ("state_rows", ctypes.c_int32),

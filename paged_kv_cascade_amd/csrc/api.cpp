@@ -194,15 +194,19 @@ pkc_status run_level(const pkc_plan_info* plan, int level, const void* q, const 
   });
 }
 
-// Checks the parameters and fills #CTA defaults from the current device: 2 x compute units
-// for the decode stage, ceil(2 x compute units / Hkv) for every level.
+// Checks the parameters and fills #CTA defaults from the current device.  A stage launches
+// #CTA x Hkv workgroups.  Decode workgroups are small (4 waves, a few dozen VGPRs each) and
+// several fit on a compute unit, so the decode default is about 8 workgroups per compute
+// unit, #CTA = ceil(8 x CUs / Hkv); a level's MFMA workgroup holds 70 KB of LDS, two fit on a
+// compute unit, so the level default is #CTA = ceil(2 x CUs / Hkv).
 pkc_status resolve_params(const pkc_plan_params* params, pkc::Resolved* r) {
   pkc_status st = pkc::check_params(params, false, r);
   if (st != PKC_OK) return st;
   if (r->p.num_ctas == 0 || r->p.level_ctas == 0) {
     int32_t cus = 0;
     if ((st = device_cus(&cus)) != PKC_OK) return st;
-    if (r->p.num_ctas == 0) r->p.num_ctas = 2 * cus;
+    if (r->p.num_ctas == 0)
+      r->p.num_ctas = (int32_t)std::max<int64_t>(1, pkc::ceil_div(8 * (int64_t)cus, r->p.num_kv_heads));
     if (r->p.level_ctas == 0)
       r->p.level_ctas = (int32_t)std::max<int64_t>(1, pkc::ceil_div(2 * (int64_t)cus, r->p.num_kv_heads));
   }
@@ -339,7 +343,8 @@ pkc_status pkc_batch_decode_paged(const pkc_plan_info* plan, const void* q, cons
     p.items = at<int32_t>(dev_ws, plan->off_dec_items);
     grid_x = plan->num_ctas;
   }
-  if ((st = timed(0, s, "decode kernel launch", [&] { return pkc::launch_decode(dtype, head_dim, g, p, grid_x, s); })) != PKC_OK)
+  const int waves = plan ? plan->dec_waves : 4;
+  if ((st = timed(0, s, "decode kernel launch", [&] { return pkc::launch_decode(dtype, head_dim, g, waves, p, grid_x, s); })) != PKC_OK)
     return st;
   if (plan && plan->num_merge > 0) {
     pkc::MergePlanParams m = merge_params(plan, dev_ws, 0, 1, true, o, lse);
@@ -462,8 +467,15 @@ pkc_status pkc_cascade_decode(const pkc_plan_info* plan, const void* q, const vo
   p.st_lse = at<float>(dev_ws, plan->off_state_lse);
   p.indptr = at<int32_t>(dev_ws, plan->off_dec_indptr);
   p.items = at<int32_t>(dev_ws, plan->off_dec_items);
+  if (num_levels > 0) {
+    // Items that finish their request fold in the request's level states.
+    p.merge_ptr = at<int32_t>(dev_ws, plan->off_merge_ptr);
+    p.merge_rows = at<int32_t>(dev_ws, plan->off_merge_rows);
+    p.nl2 = num_levels + 2;
+    p.num_levels = num_levels;
+  }
   const int g = num_qo_heads / num_kv_heads;
-  if ((st = timed(0, s, "decode kernel launch", [&] { return pkc::launch_decode(dtype, head_dim, g, p, plan->num_ctas, s); })) != PKC_OK)
+  if ((st = timed(0, s, "decode kernel launch", [&] { return pkc::launch_decode(dtype, head_dim, g, plan->dec_waves, p, plan->num_ctas, s); })) != PKC_OK)
     return st;
   if (plan->num_merge > 0) {
     pkc::MergePlanParams m = merge_params(plan, dev_ws, 0, num_levels + 1, true, o, lse);

@@ -26,6 +26,11 @@ struct DecodeParams {
   float* st_lse;             // [rows, Hq] natural-log LSE
   const int32_t* indptr;     // plan stage indptr [#CTA + 1] or nullptr (one item per request)
   const int32_t* items;      // plan items, 8 int32 each
+  // Level states a finishing item folds in: merge_rows[merge_ptr[b*nl2] .. merge_ptr[b*nl2 +
+  // num_levels]) (merge_ptr == nullptr: none).
+  const int32_t* merge_ptr;
+  const int32_t* merge_rows;
+  int32_t nl2, num_levels;
 };
 
 // Multi-query (MFMA) stage of one cascade level.
@@ -69,8 +74,8 @@ struct MergeGenericParams {
   float* lse_out;
 };
 
-hipError_t launch_decode(pkc_dtype dt, int head_dim, int group, const DecodeParams& p, int grid_x,
-                         hipStream_t s);
+hipError_t launch_decode(pkc_dtype dt, int head_dim, int group, int waves, const DecodeParams& p,
+                         int grid_x, hipStream_t s);
 hipError_t launch_prefix(pkc_dtype dt, int head_dim, int group, int tile_q, const PrefixParams& p,
                          int grid_x, hipStream_t s);
 hipError_t launch_merge_plan(pkc_dtype out_dt, int head_dim, const MergePlanParams& p,

@@ -236,7 +236,6 @@ pkc_status build_plan_host(const Resolved& r, const int32_t* kv_lens_h,
 
   // Levels: every item gets a state block of T_q rows; rows numbered level by level.
   std::vector<Stage> lv(num_levels);
-  std::vector<char> covered(B, 0);
   int32_t row = 0;
   for (int32_t l = 0; l < num_levels; ++l) {
     const pkc_level_host& h = levels[l];
@@ -254,7 +253,6 @@ pkc_status build_plan_host(const Resolved& r, const int32_t* kv_lens_h,
       it.q0 += h.qo_indptr[it.req];
       it.row = row;
       row += p.level_tile_q;
-      for (int32_t q = it.q0; q < it.q0 + it.nq; ++q) covered[q] = 1;
     }
   }
   // Decode stage over every request's own KV (one query per request, T_q = 1).
@@ -267,9 +265,11 @@ pkc_status build_plan_host(const Resolved& r, const int32_t* kv_lens_h,
   P.dec_row_base = row;
   int32_t slots = 0;
   std::vector<int32_t> flags(B, 0);
+  // A request whose own KV is a single chunk is finished by that chunk's workgroup: it folds
+  // in the request's level states (its merge list) and writes the final output.
   for (Item& it : dec.items) {
     it.q0 = it.req;
-    if (chunks[it.req] == 1 && !covered[it.req]) {
+    if (chunks[it.req] == 1) {
       it.row = -1;
       flags[it.req] = 1;
     } else {
@@ -278,6 +278,14 @@ pkc_status build_plan_host(const Resolved& r, const int32_t* kv_lens_h,
   }
   row += slots;
   P.dec_items = (int32_t)dec.items.size();
+  // Waves per decode workgroup: a workgroup splits its item's pages over its waves, so short
+  // items run on fewer waves (less merging, more steps per wave) and long ones on four.
+  {
+    int64_t tokens = 0;
+    for (const Item& it : dec.items) tokens += it.ke - it.kb;
+    const int64_t avg = dec.items.empty() ? 0 : tokens / (int64_t)dec.items.size();
+    P.dec_waves = avg >= 256 ? 4 : (avg >= 64 ? 2 : 1);
+  }
   P.dec_slots = slots;
   P.dec_kv_chunk = dec.kv_chunk;
   P.state_rows = row;

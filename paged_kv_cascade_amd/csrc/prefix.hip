@@ -9,16 +9,17 @@
 //
 // Workgroup = 4 waves = 128 query rows (a row is one (query, head) pair of the KV head's
 // group; heads of one query are adjacent rows).  Per 64-token KV tile:
-//   * the 256 threads gather the tile's K rows and V rows (128-bit loads of head_dim-contiguous
-//     rows, pages through the level's page list), K is stored row-major in LDS and V is stored
-//     transposed (V^T, head_dim-major) so both MFMA operands are 16-byte LDS reads;
+//   * the 256 threads gather the tile's K and V rows (128-bit loads of head_dim-contiguous
+//     rows, pages through the level's page list) into LDS, both row-major;
 //   * S^T = K Q^T on v_mfma_f32_16x16x32_{f16,bf16} (tokens are the M dimension, so each lane
 //     owns one query column and the softmax reductions are mostly in-lane);
 //   * online softmax in base 2 (running max / sum per query);
-//   * O^T += V^T P^T on the same MFMA; P^T comes straight from the S^T accumulators, and the
-//     order of tokens along the contraction is permuted consistently in V^T's LDS layout.
-// The tile loop is double buffered: the global loads of tile i+1 are in flight while tile i
-// is computed.  Output: one fp32 state (O normalised, natural-log LSE) per (query, head, item).
+//   * O^T += V^T P^T on the same MFMA: P^T comes straight from the S^T accumulators, and V^T's
+//     operand is read with the gfx950 LDS transpose read (ds_read_b64_tr_b16), which hands
+//     each lane one head_dim column of four consecutive token rows.
+// The tile loop is double buffered: the global loads of tile i+1 are in flight while tile i is
+// computed, and the page ids of tile i+2 are fetched one iteration before they are needed.
+// Output: one fp32 state (O normalised, natural-log LSE) per (query, head, item).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -30,13 +31,19 @@ constexpr int kTK = 64;        // KV tokens per tile
 constexpr int kThreads = 256;  // 4 waves
 constexpr int kRowsPerWave = 32;
 
+typedef short s4_t __attribute__((ext_vector_type(4)));
+
+typedef float f2_t __attribute__((ext_vector_type(2)));
+
+// Round-to-nearest-even packing of two floats into the operand type is one gfx950
+// instruction (v_cvt_pk_f16_f32 / v_cvt_pk_bf16_f32).
 template <typename T> struct Mfma;
 template <> struct Mfma<F16> {
   __device__ static f4_t run(const V16& a, const V16& b, f4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, a), __builtin_bit_cast(h8_t, b), c, 0, 0, 0);
   }
   __device__ static uint32_t pack(float lo, float hi) {
-    return (uint32_t)f32_to_f16_bits(lo) | ((uint32_t)f32_to_f16_bits(hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_t{lo, hi}, h2_t));
   }
 };
 template <> struct Mfma<BF16> {
@@ -44,9 +51,14 @@ template <> struct Mfma<BF16> {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8_t, a), __builtin_bit_cast(b8_t, b), c, 0, 0, 0);
   }
   __device__ static uint32_t pack(float lo, float hi) {
-    return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_t{lo, hi}, b2_t));
   }
 };
+
+// True on every lane when `pred` holds on every active lane of the wave.
+__device__ __forceinline__ bool wave_all(bool pred) {
+  return __builtin_amdgcn_ballot_w64(!pred) == 0;
+}
 
 __device__ __forceinline__ V16 lds_load16(const char* p) {
   const uint4 x = *reinterpret_cast<const uint4*>(p);
@@ -55,12 +67,11 @@ __device__ __forceinline__ V16 lds_load16(const char* p) {
   return r;
 }
 
-// Position of token t (0..63) of a tile inside V^T's rows: within each 32-token contraction
-// step, the 8 tokens a lane group g holds in its S^T accumulators ({16h + 4g + i}) are stored
-// at 8 consecutive positions 8g + 4h + i.
-__device__ __forceinline__ int vt_pos(int t) {
-  const int ks = t >> 5, tl = t & 31;
-  return ks * 32 + 8 * ((tl & 15) >> 2) + 4 * (tl >> 4) + (tl & 3);
+// Transpose read: within each 16-lane group, lanes 4i .. 4i+3 name the four 8-byte pieces of
+// row i (16 consecutive 16-bit values); lane j of the group receives element j of rows 0..3.
+__device__ __forceinline__ uint2 lds_read_tr(const char* p) {
+  const s4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4_t*)(p));
+  return __builtin_bit_cast(uint2, r);
 }
 
 }  // namespace
@@ -68,11 +79,9 @@ __device__ __forceinline__ int vt_pos(int t) {
 template <typename T, int D, int G>
 __global__ __launch_bounds__(kThreads, 2) void prefix_kernel(const PrefixParams p) {
   constexpr int ES = 2;
-  constexpr int KSTRIDE = D * ES + 16;     // bytes per K row in LDS (padded)
-  constexpr int VSTRIDE = kTK * ES + 16;   // bytes per V^T row in LDS (padded)
-  constexpr int KBYTES = kTK * KSTRIDE;
-  constexpr int VBYTES = D * VSTRIDE;
-  constexpr int BUF = KBYTES + VBYTES + kTK;   // + one valid flag byte per token
+  constexpr int STRIDE = D * ES + 16;          // bytes per K / V row in LDS (padded)
+  constexpr int KBYTES = kTK * STRIDE;
+  constexpr int BUF = 2 * KBYTES + kTK;        // K, V, one valid flag byte per token
   constexpr int CPR = D * ES / 16;             // 16-byte chunks per row
   constexpr int NPT = kTK * CPR / kThreads;    // tokens per loading thread (4 for D=128)
   constexpr int KS = D / 32;                   // contraction steps of S^T
@@ -92,9 +101,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefix_kernel(const PrefixParams 
   const char* kg = static_cast<const char*>(p.k);
   const char* vg = static_cast<const char*>(p.v);
   const int64_t row_stride = (int64_t)p.hkv * D * ES;   // bytes between consecutive slots
-  // Loader role: chunk c of tokens tg*NPT .. tg*NPT+NPT-1 of the tile.
+  // Loader role: chunk c of tokens tg*NPT .. tg*NPT+NPT-1 of the tile (one page: P >= NPT).
   const int ld_c = tid % CPR;
   const int ld_tg = tid / CPR;
+  // Transpose-read role inside the lane group: row (4 tokens apart) and 8-byte column piece.
+  const int tr_row = (lane & 15) >> 2;
+  const int tr_piece = lane & 3;
 
   const int it_begin = p.indptr[blockIdx.x], it_end = p.indptr[blockIdx.x + 1];
   for (int it = it_begin; it < it_end; ++it) {
@@ -128,16 +140,21 @@ __global__ __launch_bounds__(kThreads, 2) void prefix_kernel(const PrefixParams 
     float m_run[2] = {kNegInf, kNegInf};
     float l_run[2] = {0.f, 0.f};
 
-    // Global -> register staging of one tile.
-    V16 kst[NPT], vst[NPT];
-    uint32_t vflags = 0;
-    auto gather = [&](int tile) {
-      const int tbase = t0 + tile * kTK + ld_tg * NPT;   // first token of this thread's group
+    // Page of this thread's token group in a tile (-1: no token of the group is in range).
+    auto page_of = [&](int tile) -> int {
+      const int tbase = t0 + tile * kTK + ld_tg * NPT;
       int page = -1;
-      if (tbase < ke && tbase + NPT > kb) {
+      if (tile < ntiles && tbase < ke && tbase + NPT > kb) {
         const int j = tbase >> shift;
         if (j < npages_grp) page = pages[j];
       }
+      return page;
+    };
+    // Global -> register staging of one tile.
+    V16 kst[NPT], vst[NPT];
+    uint32_t vflags = 0;
+    auto gather = [&](int tile, int page) {
+      const int tbase = t0 + tile * kTK + ld_tg * NPT;
       const bool page_ok = page >= 0 && page < p.num_pages;
       vflags = 0;
 #pragma unroll
@@ -150,32 +167,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefix_kernel(const PrefixParams 
         vst[u] = v ? load16(vg + off) : zero16();
       }
     };
-    // Registers -> LDS buffer: K row-major, V transposed, flags.
+    // Registers -> LDS buffer: K and V row-major, flags.
     auto stash = [&](int buf) {
-      char* kb_s = smem + buf * BUF;
-      char* vt_s = kb_s + KBYTES;
-      char* fl_s = vt_s + VBYTES;
+      char* ks_s = smem + buf * BUF;
+      char* vs_s = ks_s + KBYTES;
+      char* fl_s = vs_s + KBYTES;
 #pragma unroll
-      for (int u = 0; u < NPT; ++u)
-        *reinterpret_cast<uint4*>(kb_s + (ld_tg * NPT + u) * KSTRIDE + ld_c * 16) =
-            make_uint4(kst[u].w[0], kst[u].w[1], kst[u].w[2], kst[u].w[3]);
-      const int pos = vt_pos(ld_tg * NPT);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int d = ld_c * 8 + 2 * k;
-        if constexpr (NPT == 4) {
-          const uint2 lo = make_uint2(__builtin_amdgcn_perm(vst[1].w[k], vst[0].w[k], 0x05040100u),
-                                      __builtin_amdgcn_perm(vst[3].w[k], vst[2].w[k], 0x05040100u));
-          const uint2 hi = make_uint2(__builtin_amdgcn_perm(vst[1].w[k], vst[0].w[k], 0x07060302u),
-                                      __builtin_amdgcn_perm(vst[3].w[k], vst[2].w[k], 0x07060302u));
-          *reinterpret_cast<uint2*>(vt_s + d * VSTRIDE + pos * ES) = lo;
-          *reinterpret_cast<uint2*>(vt_s + (d + 1) * VSTRIDE + pos * ES) = hi;
-        } else {
-          *reinterpret_cast<uint32_t*>(vt_s + d * VSTRIDE + pos * ES) =
-              __builtin_amdgcn_perm(vst[1].w[k], vst[0].w[k], 0x05040100u);
-          *reinterpret_cast<uint32_t*>(vt_s + (d + 1) * VSTRIDE + pos * ES) =
-              __builtin_amdgcn_perm(vst[1].w[k], vst[0].w[k], 0x07060302u);
-        }
+      for (int u = 0; u < NPT; ++u) {
+        const int off = (ld_tg * NPT + u) * STRIDE + ld_c * 16;
+        *reinterpret_cast<uint4*>(ks_s + off) = make_uint4(kst[u].w[0], kst[u].w[1], kst[u].w[2], kst[u].w[3]);
+        *reinterpret_cast<uint4*>(vs_s + off) = make_uint4(vst[u].w[0], vst[u].w[1], vst[u].w[2], vst[u].w[3]);
       }
       if (ld_c == 0) {
         if constexpr (NPT == 4)
@@ -185,18 +186,25 @@ __global__ __launch_bounds__(kThreads, 2) void prefix_kernel(const PrefixParams 
       }
     };
 
+    int pg_next = -1;
     if (ntiles > 0) {
-      gather(0);
+      const int pg0 = page_of(0);
+      pg_next = page_of(1);
+      gather(0, pg0);
       stash(0);
       __syncthreads();
     }
     for (int ti = 0; ti < ntiles; ++ti) {
       const int cur = ti & 1;
-      if (ti + 1 < ntiles) gather(ti + 1);
+      if (ti + 1 < ntiles) {
+        const int pg = pg_next;
+        pg_next = page_of(ti + 2);   // consumed next iteration: its latency hides behind this one
+        gather(ti + 1, pg);
+      }
       if (wave_active) {
-        const char* kb_s = smem + cur * BUF;
-        const char* vt_s = kb_s + KBYTES;
-        const char* fl_s = vt_s + VBYTES;
+        const char* ks_s = smem + cur * BUF;
+        const char* vs_s = ks_s + KBYTES;
+        const char* fl_s = vs_s + KBYTES;
         // S^T[mt][nt]: tokens mt*16 + 4*lg + i, query column nt*16 + l16.
         f4_t s[4][2];
 #pragma unroll
@@ -205,7 +213,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefix_kernel(const PrefixParams 
           s[mt][1] = f4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {
-            const V16 a = lds_load16(kb_s + (mt * 16 + l16) * KSTRIDE + (ks * 32 + 8 * lg) * ES);
+            const V16 a = lds_load16(ks_s + (mt * 16 + l16) * STRIDE + (ks * 32 + 8 * lg) * ES);
             s[mt][0] = Mfma<T>::run(a, qb[0][ks], s[mt][0]);
             s[mt][1] = Mfma<T>::run(a, qb[1][ks], s[mt][1]);
           }
@@ -213,6 +221,18 @@ __global__ __launch_bounds__(kThreads, 2) void prefix_kernel(const PrefixParams 
         uint32_t fl[4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) fl[mt] = *reinterpret_cast<const uint32_t*>(fl_s + mt * 16 + 4 * lg);
+        // Tiles whose 64 tokens are all valid (every tile but the ragged ends) skip masking.
+        const bool full = wave_all((fl[0] & fl[1] & fl[2] & fl[3]) == 0x01010101u);
+        if (!full) {
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const bool v = (fl[mt] >> (8 * i)) & 1u;
+              s[mt][0][i] = v ? s[mt][0][i] : kNegInf;
+              s[mt][1][i] = v ? s[mt][1][i] : kNegInf;
+            }
+        }
         V16 pb[2][2];   // P^T operands [nt][contraction step]
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
@@ -220,11 +240,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefix_kernel(const PrefixParams 
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float x = ((fl[mt] >> (8 * i)) & 1u) ? s[mt][nt][i] : kNegInf;
-              s[mt][nt][i] = x;
-              mx = fmaxf(mx, x);
-            }
+            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[mt][nt][i]);
           mx = fmaxf(mx, __shfl_xor(mx, 16));
           mx = fmaxf(mx, __shfl_xor(mx, 32));
           const float mn = fmaxf(m_run[nt], mx * p.scale_log2);
@@ -244,8 +260,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefix_kernel(const PrefixParams 
               psum += pr[mt][i];
             }
           l_run[nt] = l_run[nt] * alpha + psum;
+          // Once the running maxima settle, alpha is 1 on every lane: skip the rescale.
+          if (!wave_all(alpha == 1.f)) {
 #pragma unroll
-          for (int dm = 0; dm < DM; ++dm) oacc[dm][nt] *= alpha;
+            for (int dm = 0; dm < DM; ++dm) oacc[dm][nt] *= alpha;
+          }
 #pragma unroll
           for (int kk = 0; kk < 2; ++kk) {
             pb[nt][kk].w[0] = Mfma<T>::pack(pr[2 * kk][0], pr[2 * kk][1]);
@@ -254,12 +273,19 @@ __global__ __launch_bounds__(kThreads, 2) void prefix_kernel(const PrefixParams 
             pb[nt][kk].w[3] = Mfma<T>::pack(pr[2 * kk + 1][2], pr[2 * kk + 1][3]);
           }
         }
-        // O^T[dm][nt] += V^T[dm rows][32 positions] * P^T.
+        // O^T[dm][nt] += V^T * P^T.  Contraction step kk covers tokens kk*32 .. +32; lane
+        // group g supplies contraction elements 8g .. 8g+7 = tokens kk*32 + 16h + 4g + i
+        // (h = 0, 1; i = 0..3), the order of the S^T accumulators; each half is one
+        // transpose read of rows kk*32 + 16h + 4g + tr_row, columns dm*16 + 4*tr_piece.
 #pragma unroll
         for (int dm = 0; dm < DM; ++dm)
 #pragma unroll
           for (int kk = 0; kk < 2; ++kk) {
-            const V16 a = lds_load16(vt_s + (dm * 16 + l16) * VSTRIDE + (kk * 32 + 8 * lg) * ES);
+            const char* base = vs_s + (kk * 32 + 4 * lg + tr_row) * STRIDE + (dm * 16 + 4 * tr_piece) * ES;
+            const uint2 lo = lds_read_tr(base);
+            const uint2 hi = lds_read_tr(base + 16 * STRIDE);
+            V16 a;
+            a.w[0] = lo.x; a.w[1] = lo.y; a.w[2] = hi.x; a.w[3] = hi.y;
             oacc[dm][0] = Mfma<T>::run(a, pb[0][kk], oacc[dm][0]);
             oacc[dm][1] = Mfma<T>::run(a, pb[1][kk], oacc[dm][1]);
           }

@@ -157,10 +157,13 @@ def test_cascade_plan_merge_lists():
     assert cp.suffix.kv_chunk == 12
     assert [(it.req, it.kv_begin, it.kv_end) for it in cp.suffix.items] == \
         [(0, 0, 8), (2, 0, 12), (2, 12, 24), (2, 24, 30), (3, 0, 3), (4, 0, 4)]
-    assert cp.suffix.slots == [0, 1, 2, 3, 4, -1]
-    assert cp.write_through == [False, False, False, False, True]
-    assert cp.merge[0] == [(0, 0, 0), (1, 0, 0), ("suffix", 0, 0)]
+    # single-chunk requests (0, 3, 4) are finished by their decode item, which folds in the
+    # level states of their merge list; request 2 (3 chunks) and request 1 (no own KV) are
+    # finished by the merge pass
+    assert cp.suffix.slots == [-1, 0, 1, 2, -1, -1]
+    assert cp.write_through == [True, False, False, True, True]
+    assert cp.merge[0] == [(0, 0, 0), (1, 0, 0)]
     assert cp.merge[1] == [(0, 0, 1), (1, 1, 0)]
-    assert cp.merge[2] == [(0, 1, 0), ("suffix", 1, 0), ("suffix", 2, 0), ("suffix", 3, 0)]
-    assert cp.merge[3] == [(0, 1, 1), ("suffix", 4, 0)]
+    assert cp.merge[2] == [(0, 1, 0), ("suffix", 0, 0), ("suffix", 1, 0), ("suffix", 2, 0)]
+    assert cp.merge[3] == [(0, 1, 1)]
     assert cp.merge[4] == []
