@@ -39,8 +39,9 @@
  * no tokens) and pkc_validate_block_table reports it.
  *
  * Supported: dtype f32 / f16 / bf16 (q, k, v share it); head_dim 64 or 128; page size a power
- * of two in [1, 1024]; Hq / Hkv in {1, 2, 4, 8}.  The multi-query prefix kernel needs
- * f16 or bf16 and page size >= 4; other combinations return PKC_ERR_UNSUPPORTED.
+ * of two in [1, 1024] with one page (page_size x Hkv x head_dim elements) under 2 GiB;
+ * Hq / Hkv in {1, 2, 4, 8}.  The multi-query prefix kernel needs f16 or bf16 and page size
+ * >= 4; other combinations return PKC_ERR_UNSUPPORTED.
  *
  * Conventions
  * -----------
@@ -166,6 +167,7 @@ typedef struct pkc_plan_info {
   int64_t off_merge_ptr;
   int64_t off_merge_rows;
   int64_t off_req_flags;
+  int64_t off_req_levels;
   int64_t int_bytes;       /* bytes of integer plan data (copied host -> device) */
   int64_t off_state_o;     /* fp32 [state_rows, Hq, D] */
   int64_t off_state_lse;   /* fp32 [state_rows, Hq] */
@@ -185,7 +187,9 @@ pkc_status pkc_plan_buffer_sizes(const pkc_plan_params* params, const pkc_level_
                                  int32_t num_levels, size_t* host_bytes, size_t* device_bytes);
 
 /*
- * Build a plan on the CPU and enqueue its copy into the device workspace.
+ * Build a plan on the CPU and enqueue its copy into the device workspace.  For a page-locked
+ * host buffer the copy is a small kernel on `stream` that reads the buffer directly (no
+ * copy-engine synchronisation between steps); other host memory goes through hipMemcpyAsync.
  *   kv_lens_h: [B] host, tokens each request attends over in its own KV (the suffix in a
  *              cascade; cache_seqlens - kv_start for a plain decode).
  *   levels_h:  num_levels cascade levels (0 for a plain split-KV decode).
@@ -203,7 +207,11 @@ pkc_status pkc_plan_buffer_sizes(const pkc_plan_params* params, const pkc_level_
  *   merge_rows   state rows; req_flags [B]: 1 when the decode stage writes the output (the
  *                request's own KV is a single chunk; that chunk's workgroup first folds in
  *                the request's level states listed in merge_rows), 0 when the merge kernel
- *                does.
+ *                does;
+ *   req_levels   [B, num_levels, 2]: {first state row, count} of request b's rows at level
+ *                l; they are first + c * lvl_tile_q[l] for c < count (the chunks of one query
+ *                tile hold consecutive slots), the same rows merge_rows lists; 8 ints of
+ *                padding follow.
  */
 pkc_status pkc_plan(const pkc_plan_params* params, const int32_t* kv_lens_h,
                     const pkc_level_host* levels_h, int32_t num_levels, void* host_buf,

@@ -74,7 +74,8 @@ class PlanInfo(ctypes.Structure):
                 ("off_dec_indptr", ctypes.c_int64), ("off_dec_items", ctypes.c_int64),
                 ("off_lvl_indptr", _O8), ("off_lvl_items", _O8),
                 ("off_merge_ptr", ctypes.c_int64), ("off_merge_rows", ctypes.c_int64),
-                ("off_req_flags", ctypes.c_int64), ("int_bytes", ctypes.c_int64),
+                ("off_req_flags", ctypes.c_int64), ("off_req_levels", ctypes.c_int64),
+                ("int_bytes", ctypes.c_int64),
                 ("off_state_o", ctypes.c_int64), ("off_state_lse", ctypes.c_int64),
                 ("dev_bytes", ctypes.c_int64), ("dev_ws", ctypes.c_uint64)]
 
@@ -433,4 +434,7 @@ def read_plan_arrays(info: PlanInfo, host_buf: torch.Tensor):
     out["merge_ptr"] = [mptr[b * nl2:(b + 1) * nl2] for b in range(info.batch)]
     out["merge_rows"] = rows
     out["req_flags"] = ints(info.off_req_flags, info.batch)
+    rl = ints(info.off_req_levels, info.batch * info.num_levels * 2)
+    out["req_levels"] = [[tuple(rl[(b * info.num_levels + l) * 2:(b * info.num_levels + l) * 2 + 2])
+                          for l in range(info.num_levels)] for b in range(info.batch)]
     return out

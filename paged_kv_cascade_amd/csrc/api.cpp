@@ -101,6 +101,9 @@ pkc_status check_shapes(int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim
   if (!pkc::is_pow2(page_size) || page_size > 1024)
     return fail(PKC_ERR_UNSUPPORTED, "page_size must be a power of two in [1, 1024]");
   if (!dtype_ok(dtype)) return fail(PKC_ERR_UNSUPPORTED, "unknown dtype");
+  // Kernels address inside one page with 32-bit byte offsets.
+  if ((int64_t)page_size * hkv * head_dim * (dtype == PKC_F32 ? 4 : 2) > INT32_MAX)
+    return fail(PKC_ERR_UNSUPPORTED, "one page (page_size * num_kv_heads * head_dim elements) must be under 2 GiB");
   if (!(sm_scale > 0.f) || !std::isfinite(sm_scale))
     return fail(PKC_ERR_INVALID_ARG, "sm_scale must be positive and finite");
   return PKC_OK;
@@ -192,6 +195,21 @@ pkc_status run_level(const pkc_plan_info* plan, int level, const void* q, const 
     return pkc::launch_prefix(dtype, plan->head_dim, g, plan->lvl_tile_q[level], p,
                               plan->level_ctas, s);
   });
+}
+
+// True when host_buf is page-locked host memory the device can read (hipHostMalloc / torch
+// pin_memory); the last answer is cached per pointer.
+bool host_buf_is_pinned(const void* host_buf) {
+  static thread_local const void* last = nullptr;
+  static thread_local bool last_pinned = false;
+  if (host_buf == last) return last_pinned;
+  hipPointerAttribute_t attr{};
+  bool pinned = false;
+  if (hipPointerGetAttributes(&attr, host_buf) == hipSuccess) pinned = attr.type == hipMemoryTypeHost;
+  (void)hipGetLastError();  // a pageable pointer leaves an error behind; clear it
+  last = host_buf;
+  last_pinned = pinned;
+  return pinned;
 }
 
 // Checks the parameters and fills #CTA defaults from the current device.  A stage launches
@@ -301,9 +319,16 @@ pkc_status pkc_plan(const pkc_plan_params* params, const int32_t* kv_lens_h,
     return st;
   if (dev_bytes < (size_t)out->dev_bytes)
     return fail(PKC_ERR_WORKSPACE_TOO_SMALL, "device workspace smaller than " + std::to_string(out->dev_bytes) + " bytes");
-  hipError_t e = hipMemcpyAsync(dev_ws, host_buf, (size_t)out->int_bytes, hipMemcpyHostToDevice,
-                                reinterpret_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(plan)");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (host_buf_is_pinned(host_buf)) {
+    // A kernel on the caller's queue reads the pinned buffer: no copy-engine synchronisation.
+    e = pkc::launch_plan_upload(host_buf, dev_ws, out->int_bytes, s);
+    if (e != hipSuccess) return hip_fail(e, "plan upload launch");
+  } else {
+    e = hipMemcpyAsync(dev_ws, host_buf, (size_t)out->int_bytes, hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(plan)");
+  }
   out->dev_ws = (uint64_t)(uintptr_t)dev_ws;
   return PKC_OK;
   PKC_TRY_END("pkc_plan")
@@ -324,7 +349,8 @@ pkc_status pkc_batch_decode_paged(const pkc_plan_info* plan, const void* q, cons
   if (!q || !k_pool || !v_pool || !block_table || !o || !lse)
     return fail(PKC_ERR_INVALID_ARG, "NULL tensor pointer");
   if (!plan && !cache_seqlens) return fail(PKC_ERR_INVALID_ARG, "cache_seqlens is NULL");
-  if (num_pages < 0 || max_blocks < 0) return fail(PKC_ERR_INVALID_ARG, "negative num_pages / max_blocks");
+  if (num_pages < 1 || max_blocks < 0)
+    return fail(PKC_ERR_INVALID_ARG, "num_pages must be >= 1 (masked lanes read row 0 of page 0) and max_blocks >= 0");
   if ((int64_t)max_blocks * page_size > INT32_MAX)
     return fail(PKC_ERR_INVALID_ARG, "max_blocks * page_size exceeds int32");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -373,6 +399,7 @@ pkc_status pkc_prefix_attention(const pkc_plan_info* plan, int32_t level, const 
   if (level < 0 || level >= plan->num_levels) return fail(PKC_ERR_INVALID_ARG, "level out of range");
   if (batch == 0) return PKC_OK;
   if (!q || !k_pool || !v_pool || !o_state || !lse_state) return fail(PKC_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (num_pages < 1) return fail(PKC_ERR_INVALID_ARG, "num_pages must be >= 1 (masked lanes read row 0 of page 0)");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if ((st = run_level(plan, level, q, k_pool, v_pool, num_pages, level_dev, dtype, sm_scale, dev_ws, s)) != PKC_OK)
     return st;
@@ -453,7 +480,8 @@ pkc_status pkc_cascade_decode(const pkc_plan_info* plan, const void* q, const vo
   if (batch == 0) return PKC_OK;
   if (!q || !k_pool || !v_pool || !o || !lse) return fail(PKC_ERR_INVALID_ARG, "NULL tensor pointer");
   if (plan->dec_items > 0 && !block_table) return fail(PKC_ERR_INVALID_ARG, "block_table is NULL");
-  if (num_pages < 0 || max_blocks < 0) return fail(PKC_ERR_INVALID_ARG, "negative num_pages / max_blocks");
+  if (num_pages < 1 || max_blocks < 0)
+    return fail(PKC_ERR_INVALID_ARG, "num_pages must be >= 1 (masked lanes read row 0 of page 0) and max_blocks >= 0");
   if ((int64_t)max_blocks * page_size > INT32_MAX)
     return fail(PKC_ERR_INVALID_ARG, "max_blocks * page_size exceeds int32");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -473,6 +501,13 @@ pkc_status pkc_cascade_decode(const pkc_plan_info* plan, const void* q, const vo
     p.merge_rows = at<int32_t>(dev_ws, plan->off_merge_rows);
     p.nl2 = num_levels + 2;
     p.num_levels = num_levels;
+    for (int32_t l = 0; l < num_levels; ++l) p.lvl_tile_q[l] = plan->lvl_tile_q[l];
+    p.req_levels = at<int32_t>(dev_ws, plan->off_req_levels);
+    const int64_t o_bytes = (int64_t)plan->state_rows * num_qo_heads * head_dim * 4;
+    if (o_bytes <= INT32_MAX) {
+      p.fold_o_bytes = (int32_t)o_bytes;
+      p.fold_lse_bytes = plan->state_rows * num_qo_heads * 4;
+    }
   }
   const int g = num_qo_heads / num_kv_heads;
   if ((st = timed(0, s, "decode kernel launch", [&] { return pkc::launch_decode(dtype, head_dim, g, plan->dec_waves, p, plan->num_ctas, s); })) != PKC_OK)

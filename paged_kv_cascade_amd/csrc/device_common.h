@@ -77,6 +77,42 @@ __device__ __forceinline__ V16 zero16() {
   return r;
 }
 
+// Wave-uniform read of read-only int32 data (block tables, page lists, plan records) through
+// the scalar cache.  A vector load would share the in-order vmcnt queue with the K/V stream,
+// so waiting for a table entry would mean waiting for every K/V load issued before it.
+__device__ __forceinline__ int32_t scalar_load(const int32_t* p) {
+  return *(const __attribute__((address_space(4))) int32_t*)(p);
+}
+
+// 16 bytes at base + off when `valid`, else zeros.  The load is issued unconditionally (an
+// invalid lane reads base + 0, which the caller guarantees is in bounds) and the zeros are
+// selected afterwards: a branch around a load makes the compiler wait for every outstanding
+// load at the branch, which would serialise a software pipeline.
+__device__ __forceinline__ V16 load16_or_zero(const char* base, int64_t off, bool valid) {
+  const V16 x = load16(base + (valid ? off : 0));
+  V16 r;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) r.w[k] = valid ? x.w[k] : 0u;
+  return r;
+}
+
+// Buffer resource over `bytes` bytes at `base` (raw addressing, no swizzle, 32-bit data
+// format, the gfx9 word-3 encoding).  A buffer load whose offset is at or past `bytes` returns
+// zeros without touching memory, so masked lanes need no select and no branch.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int32_t kOffsetNone = INT32_MIN;   // 0x80000000: past any range a kernel builds
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kBufferWord3);
+}
+__device__ __forceinline__ V16 buffer_load16(rsrc_t r, int32_t off) {
+  typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
+  const u4_t x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  V16 v;
+  v.w[0] = x[0]; v.w[1] = x[1]; v.w[2] = x[2]; v.w[3] = x[3];
+  return v;
+}
+
 // Partial dot product of the 16-byte slices of q and k (fp32 accumulate; products exact).
 __device__ __forceinline__ float dot16(F32, const V16& a, const V16& b) {
   float s = __uint_as_float(a.w[0]) * __uint_as_float(b.w[0]);

@@ -27,10 +27,16 @@ struct DecodeParams {
   const int32_t* indptr;     // plan stage indptr [#CTA + 1] or nullptr (one item per request)
   const int32_t* items;      // plan items, 8 int32 each
   // Level states a finishing item folds in: merge_rows[merge_ptr[b*nl2] .. merge_ptr[b*nl2 +
-  // num_levels]) (merge_ptr == nullptr: none).
+  // num_levels]) (merge_ptr == nullptr: none).  At level l the rows of one request are
+  // first + c * lvl_tile_q[l], c = 0, 1, ... (consecutive chunks of one query tile).
   const int32_t* merge_ptr;
   const int32_t* merge_rows;
   int32_t nl2, num_levels;
+  int32_t lvl_tile_q[PKC_MAX_LEVELS];
+  const int32_t* req_levels;  // [B, num_levels, 2] {first row, count} per request and level
+  // Bytes of st_o / st_lse a finishing item may prefetch level states from through 32-bit
+  // buffer offsets (0: states beyond 2 GiB, read directly at the end instead).
+  int32_t fold_o_bytes, fold_lse_bytes;
 };
 
 // Multi-query (MFMA) stage of one cascade level.
@@ -85,6 +91,8 @@ hipError_t launch_merge_generic(pkc_dtype in_dt, pkc_dtype out_dt, int head_dim,
 hipError_t launch_merge_inplace(pkc_dtype dt, int head_dim, void* o_a, float* lse_a,
                                 const void* o_b, const float* lse_b, int64_t num_states,
                                 hipStream_t s);
+// Copies `bytes` (a multiple of 16, 16-byte aligned) from pinned host memory to the device.
+hipError_t launch_plan_upload(const void* host_src, void* dev_dst, int64_t bytes, hipStream_t s);
 hipError_t launch_debug_gather(const int32_t* block_table, int32_t max_blocks,
                                const int32_t* seqlens, const int32_t* kv_start, int32_t batch,
                                int32_t page_shift, int64_t num_pages, int32_t* rows_out,

@@ -142,6 +142,22 @@ __global__ __launch_bounds__(256) void merge_inplace_kernel(void* o_a, float* ls
   if (d0 == 0) lse_a[sidx] = den > 0.f ? (mu + log2f(den)) * kLn2 : kNegInf;
 }
 
+// Plan upload: the GPU reads the pinned host buffer directly and writes the workspace.  Being a
+// kernel on the caller's queue, it needs no synchronisation with a copy engine.
+__global__ __launch_bounds__(256) void plan_upload_kernel(const uint4* __restrict__ src,
+                                                          uint4* __restrict__ dst, int64_t n16) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n16) dst[i] = src[i];
+}
+
+hipError_t launch_plan_upload(const void* host_src, void* dev_dst, int64_t bytes, hipStream_t s) {
+  const int64_t n16 = (bytes + 15) / 16;
+  if (n16 <= 0) return hipSuccess;
+  hipLaunchKernelGGL(plan_upload_kernel, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, s,
+                     static_cast<const uint4*>(host_src), static_cast<uint4*>(dev_dst), n16);
+  return hipGetLastError();
+}
+
 template <typename TO>
 static hipError_t merge_plan_d(int head_dim, const MergePlanParams& p, hipStream_t s) {
   if (p.batch <= 0) return hipSuccess;

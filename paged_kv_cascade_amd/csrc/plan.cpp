@@ -192,6 +192,7 @@ pkc_status compute_layout(const Resolved& r, const pkc_level_host* levels, int32
   L.max_merge_rows = merge_rows;
   L.off_merge_rows = take(merge_rows);
   L.off_req_flags = take(B);
+  L.off_req_levels = take(B * NL * 2 + 8);   // + padding: the decode kernel reads 4 levels' entries
   L.int_bytes = off;
   L.max_state_rows = rows + L.max_dec_rows;
   const int64_t hd = (int64_t)p.num_qo_heads * p.head_dim;
@@ -320,11 +321,22 @@ pkc_status build_plan_host(const Resolved& r, const int32_t* kv_lens_h,
         per_req_lvl[(size_t)(it.q0 + q) * (num_levels + 1) + l].push_back(it.row + q);
   for (const Item& it : dec.items)
     if (it.row >= 0) per_req_lvl[(size_t)it.req * (num_levels + 1) + num_levels].push_back(it.row);
+  int32_t* rlev = reinterpret_cast<int32_t*>(base + L.off_req_levels);
   int32_t n = 0, num_merge = 0;
   for (int32_t b = 0; b < B; ++b) {
     for (int32_t l = 0; l <= num_levels; ++l) {
       mptr[b * NL2 + l] = n;
-      for (int32_t rr : per_req_lvl[(size_t)b * (num_levels + 1) + l]) mrows[n++] = rr;
+      const std::vector<int32_t>& rows_bl = per_req_lvl[(size_t)b * (num_levels + 1) + l];
+      if (l < num_levels) {
+        // The decode kernel computes a request's level rows as first + c * T_q (the chunks of
+        // one query tile hold consecutive slots); keep that invariant checked.
+        for (size_t c = 1; c < rows_bl.size(); ++c)
+          if (rows_bl[c] != rows_bl[0] + (int32_t)c * p.level_tile_q)
+            return fail(PKC_ERR_INTERNAL, "level rows of a request are not one query tile's chunks");
+        rlev[(b * num_levels + l) * 2] = rows_bl.empty() ? 0 : rows_bl[0];
+        rlev[(b * num_levels + l) * 2 + 1] = (int32_t)rows_bl.size();
+      }
+      for (int32_t rr : rows_bl) mrows[n++] = rr;
     }
     mptr[b * NL2 + num_levels + 1] = n;
     if (!flags[b]) ++num_merge;
@@ -343,6 +355,7 @@ pkc_status build_plan_host(const Resolved& r, const int32_t* kv_lens_h,
   P.off_merge_ptr = L.off_merge_ptr;
   P.off_merge_rows = L.off_merge_rows;
   P.off_req_flags = L.off_req_flags;
+  P.off_req_levels = L.off_req_levels;
   P.int_bytes = L.int_bytes;
   P.off_state_o = L.off_state_o;
   P.off_state_lse = L.off_state_lse;

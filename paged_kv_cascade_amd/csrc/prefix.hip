@@ -163,8 +163,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefix_kernel(const PrefixParams 
         const bool v = page_ok && t >= kb && t < ke;
         vflags |= (v ? 1u : 0u) << (8 * u);
         const int64_t off = (((int64_t)page << shift) + (t & (P - 1))) * row_stride + hk * D * ES + ld_c * 16;
-        kst[u] = v ? load16(kg + off) : zero16();
-        vst[u] = v ? load16(vg + off) : zero16();
+        kst[u] = load16_or_zero(kg, off, v);
+        vst[u] = load16_or_zero(vg, off, v);
       }
     };
     // Registers -> LDS buffer: K and V row-major, flags.

@@ -90,6 +90,11 @@ def _compare_plan(api, info, hb, o, levels, tile_q):
                 elif stage == l:
                     want.append(info.lvl_row_base[l] + slot * tile_q + row)
             assert got == want, f"request {b} stage {l}"
+            if l < nl:
+                # {first row, count}: the same rows, as first + c * T_q
+                first, cnt = arr["req_levels"][b][l]
+                assert cnt == len(want)
+                assert want == [first + c * tile_q for c in range(cnt)]
         assert arr["req_flags"][b] == (1 if o.write_through[b] else 0)
     assert info.num_merge == sum(1 for w in o.write_through if not w)
 
@@ -198,14 +203,17 @@ def test_validation_errors_before_any_launch(api):
     p = api.make_params(2, 4, 4, 128, 16, num_ctas=4, level_ctas=1)
     info, _ = api.plan_host(p, [10, 20])
     d = ctypes.c_void_p(0x1000)
-    assert lib.pkc_batch_decode_paged(ctypes.byref(info), d, d, d, 0, d, 0, d, None, 2, 4,
+    assert lib.pkc_batch_decode_paged(ctypes.byref(info), d, d, d, 1, d, 0, d, None, 2, 4,
                                       4, 128, 16, 1, 1.0, d, d, None, 0, None) == 4
     assert "workspace" in lib.pkc_last_error().decode()
     info.magic = 0
-    assert lib.pkc_batch_decode_paged(ctypes.byref(info), d, d, d, 0, d, 0, d, None, 2, 4,
+    assert lib.pkc_batch_decode_paged(ctypes.byref(info), d, d, d, 1, d, 0, d, None, 2, 4,
                                       4, 128, 16, 1, 1.0, d, d, None, 0, None) == 4
-    assert lib.pkc_batch_decode_paged(None, d, d, d, 0, d, 0, None, None, 2, 4, 4, 128, 16, 1, 1.0,
+    assert lib.pkc_batch_decode_paged(None, d, d, d, 1, d, 0, None, None, 2, 4, 4, 128, 16, 1, 1.0,
                                       d, d, None, 0, None) == 1   # no cache_seqlens without a plan
+    # an empty pool: masked lanes could not read row 0 of page 0
+    assert lib.pkc_batch_decode_paged(None, d, d, d, 0, d, 0, d, None, 2, 4, 4, 128, 16, 1, 1.0,
+                                      d, d, None, 0, None) == 1
     # merge: bad head_dim, dense range beyond the states
     assert lib.pkc_merge_states(None, 1, None, 4, None, None, 1, 2, 4, 80, None, 1, None, None) == 2
     assert lib.pkc_merge_states(None, 1, None, 4, None, None, 3, 2, 4, 64, None, 1, None, None) == 1
