@@ -8,18 +8,29 @@
 // real dense contraction, so both products run on matrix cores.
 //
 // Workgroup = 4 waves = 128 query rows (a row is one (query, head) pair of the KV head's
-// group; heads of one query are adjacent rows).  Per 64-token KV tile:
-//   * the 256 threads gather the tile's K and V rows (128-bit loads of head_dim-contiguous
-//     rows, pages through the level's page list) into LDS, both row-major;
+// group; heads of one query are adjacent rows); two workgroups per compute unit.
+//
+// KV streaming: 32-token tiles go straight from HBM into a 4-stage LDS ring with buffer loads
+// that write LDS (no register staging), so three tiles (48 KB per workgroup) are in flight
+// while one is computed.  Each load instruction moves 1 KB: whole 16-byte chunks of a few
+// head_dim-contiguous K (or V) rows of one page, through a buffer resource over that page.
+// Rows outside the item's token range and pages outside [0, num_pages) are out of the
+// resource's range, so the hardware writes zeros to LDS and reads nothing.  Chunk positions
+// inside a row are XOR-swizzled by the row so that the matrix-core operand reads below hit
+// distinct LDS banks; the swizzle is applied on the global side (each lane fetches the chunk
+// that belongs at its LDS position).
+//
+// Per tile and wave (32 query rows):
 //   * S^T = K Q^T on v_mfma_f32_16x16x32_{f16,bf16} (tokens are the M dimension, so each lane
 //     owns one query column and the softmax reductions are mostly in-lane);
-//   * online softmax in base 2 (running max / sum per query);
+//   * online softmax in base 2 (running max / sum per query), masked by the tile's valid-token
+//     bits (range and page validity, computed on the scalar unit);
 //   * O^T += V^T P^T on the same MFMA: P^T comes straight from the S^T accumulators, and V^T's
 //     operand is read with the gfx950 LDS transpose read (ds_read_b64_tr_b16), which hands
 //     each lane one head_dim column of four consecutive token rows.
-// The tile loop is double buffered: the global loads of tile i+1 are in flight while tile i is
-// computed, and the page ids of tile i+2 are fetched one iteration before they are needed.
 // Output: one fp32 state (O normalised, natural-log LSE) per (query, head, item).
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -27,12 +38,11 @@ namespace pkc {
 
 namespace {
 
-constexpr int kTK = 64;        // KV tokens per tile
+constexpr int kTK = 32;        // KV tokens per tile
 constexpr int kThreads = 256;  // 4 waves
 constexpr int kRowsPerWave = 32;
 
 typedef short s4_t __attribute__((ext_vector_type(4)));
-
 typedef float f2_t __attribute__((ext_vector_type(2)));
 
 // Round-to-nearest-even packing of two floats into the operand type is one gfx950
@@ -74,21 +84,52 @@ __device__ __forceinline__ uint2 lds_read_tr(const char* p) {
   return __builtin_bit_cast(uint2, r);
 }
 
+// Buffer load of 16 bytes per lane into LDS: lane l writes lds + 16 * l.
+__device__ __forceinline__ void load_lds16(rsrc_t r, char* lds, int32_t voff, int32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+
+// s_waitcnt on the vector-memory count only (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt in
+// 6:4, lgkmcnt in 11:8; the others at their maxima).
+#define PKC_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x70 | 0xF00)
+
+// Workgroup barrier that the compiler may not move memory accesses across (the builtin alone
+// is not a memory operation); the ring's waits are explicit.
+__device__ __forceinline__ void ring_barrier() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
+// Physical 16-byte chunk of logical chunk c in LDS row r: c ^ swz(r).  D = 128 (16 chunks per
+// 256-byte row): the 16 rows read by one K operand load and the 8 rows x 2 chunks of one
+// transpose read land on distinct banks.  D = 64 (8 chunks per 128-byte row, two rows per bank
+// sweep): the same property with the row parity selecting the bank half.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return 2 * (r & 7) + ((r >> 3) & 1);
+  else return 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
+}
+
 }  // namespace
 
 template <typename T, int D, int G>
 __global__ __launch_bounds__(kThreads, 2) void prefix_kernel(const PrefixParams p) {
   constexpr int ES = 2;
-  constexpr int STRIDE = D * ES + 16;          // bytes per K / V row in LDS (padded)
-  constexpr int KBYTES = kTK * STRIDE;
-  constexpr int BUF = 2 * KBYTES + kTK;        // K, V, one valid flag byte per token
-  constexpr int CPR = D * ES / 16;             // 16-byte chunks per row
-  constexpr int NPT = kTK * CPR / kThreads;    // tokens per loading thread (4 for D=128)
-  constexpr int KS = D / 32;                   // contraction steps of S^T
-  constexpr int DM = D / 16;                   // 16-row tiles of O^T
-  static_assert(NPT == 2 || NPT == 4, "loader layout");
+  constexpr int RB = D * ES;                 // bytes per K / V row
+  constexpr int CPR = RB / 16;               // 16-byte chunks per row
+  constexpr int NDMA = 4;                    // load instructions per wave per tile (K and V)
+  constexpr int STB = kTK * RB;              // bytes of K (or V) per stage
+  constexpr int KS = D / 32;                 // contraction steps of S^T
+  constexpr int DM = D / 16;                 // 16-row tiles of O^T
+  static_assert(kTK == 32 && kThreads == 256 && (D == 64 || D == 128), "tile layout");
 
-  __shared__ __attribute__((aligned(16))) char smem[2 * BUF];
+  // One array per stage and operand: the compiler tracks LDS-writing loads per array, so a
+  // read of one stage waits only for that stage's loads.
+  __shared__ __attribute__((aligned(16))) char sk0[STB], sk1[STB], sk2[STB], sk3[STB];
+  __shared__ __attribute__((aligned(16))) char sv0[STB], sv1[STB], sv2[STB], sv3[STB];
+  // Valid-row bits of the tile in each stage: byte w is written by wave w for its 8 rows.
+  __shared__ uint32_t sflag[4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -100,38 +141,105 @@ __global__ __launch_bounds__(kThreads, 2) void prefix_kernel(const PrefixParams 
   const int P = p.page_size;
   const char* kg = static_cast<const char*>(p.k);
   const char* vg = static_cast<const char*>(p.v);
-  const int64_t row_stride = (int64_t)p.hkv * D * ES;   // bytes between consecutive slots
-  // Loader role: chunk c of tokens tg*NPT .. tg*NPT+NPT-1 of the tile (one page: P >= NPT).
-  const int ld_c = tid % CPR;
-  const int ld_tg = tid / CPR;
+  const int32_t row_stride = p.hkv * RB;        // bytes between consecutive slots of a page
+  const int32_t page_bytes = P * row_stride;    // < 2 GiB (checked on the host)
+  const int32_t npool = (int32_t)min<int64_t>(p.num_pages, INT32_MAX);
   // Transpose-read role inside the lane group: row (4 tokens apart) and 8-byte column piece.
   const int tr_row = (lane & 15) >> 2;
   const int tr_piece = lane & 3;
 
-  const int it_begin = p.indptr[blockIdx.x], it_end = p.indptr[blockIdx.x + 1];
+  // Loader role.  Wave wv loads tile rows 8wv .. 8wv+7 of K and of V as two 4-row groups
+  // (rows 8wv + 4g .., one page each since pages hold a multiple of 4 slots).  D = 128: one
+  // 1 KB instruction per group, lane l -> row 8wv + 4g + l/16, LDS chunk l%16.  D = 64: one
+  // 1 KB instruction covers both groups as two exec-masked halves, lane l -> row 8wv + l/8,
+  // LDS chunk l%8.  Each lane fetches logical chunk (LDS chunk) ^ swz(row); voff is its byte
+  // offset from its group's first row in the page.
+  constexpr int NI = D == 128 ? 2 : 1;   // instructions per operand per tile
+  int32_t voff[NI];
+  int lrow[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    lrow[i] = 8 * wv + (D == 128 ? 4 * i + lane / 16 : lane / 8);
+    const int cg = (lane % CPR) ^ swz<D>(lrow[i]);
+    voff[i] = ((lrow[i] - 8 * wv) & 3) * row_stride + hk * RB + cg * 16;
+  }
+
+  const int it_begin = scalar_load(p.indptr + blockIdx.x);
+  const int it_end = scalar_load(p.indptr + blockIdx.x + 1);
   for (int it = it_begin; it < it_end; ++it) {
     const int32_t* rec = p.items + 8 * (int64_t)it;
-    const int grp = rec[0], q0 = rec[1], nq = rec[2], kb = rec[3], ke = rec[4], srow = rec[5];
+    const int grp = scalar_load(rec);
+    const int q0 = scalar_load(rec + 1), nq = scalar_load(rec + 2);
+    const int kb = scalar_load(rec + 3), ke = scalar_load(rec + 4), srow = scalar_load(rec + 5);
     const int nrows = nq * G;
-    const int32_t* pages = p.page_indices + p.page_indptr[grp];
-    const int npages_grp = p.page_indptr[grp + 1] - p.page_indptr[grp];
+    const int pbeg = scalar_load(p.page_indptr + grp);
+    const int npages_grp = scalar_load(p.page_indptr + grp + 1) - pbeg;
+    const int32_t* pages = p.page_indices + pbeg;
     const int t0 = (kb / kTK) * kTK;
-    const int ntiles = ke > kb ? (ke - t0 + kTK - 1) / kTK : 0;
+    // A group without pages holds no tokens (its kv_len is then a caller error).
+    const int ntiles = (ke > kb && npages_grp > 0) ? (ke - t0 + kTK - 1) / kTK : 0;
+    const int last_page = max(npages_grp - 1, 0);
     const bool wave_active = wv * kRowsPerWave < nrows;
 
-    // Q^T operands: lane owns query row r = wv*32 + nt*16 + l16, head_dim slice
-    // ks*32 + 8*lg .. +8 per contraction step.
-    V16 qb[2][KS];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int r = wv * kRowsPerWave + nt * 16 + l16;
-      const bool ok = r < nrows;
-      const int64_t qoff = ((int64_t)(q0 + r / G) * p.hq + hk * G + r % G) * D;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        qb[nt][ks] = ok ? load16(static_cast<const char*>(p.q) + (qoff + ks * 32 + 8 * lg) * ES) : zero16();
-    }
+    // Page-list entries of this wave's two row groups in tile tt (scalar loads, clamped into
+    // the list; a group past the list is rejected when the tile is issued).  They are fetched
+    // one step before use, so their latency hides behind a tile's arithmetic.
+    struct Pg { int e0, e1; };
+    auto fetch = [&](int tt) -> Pg {
+      const int rb = t0 + tt * kTK + 8 * wv;
+      Pg r;
+      r.e0 = scalar_load(pages + min(rb >> shift, last_page));
+      r.e1 = scalar_load(pages + min((rb + 4) >> shift, last_page));
+      return r;
+    };
 
+    // Loads of tile tt into stage (sk, sv) and the stage's valid-row byte of this wave; a tile
+    // past the end reads nothing (zeros) and marks no row valid.
+    auto issue = [&](int tt, const Pg& pg, char* sk, char* sv, uint32_t* flag) {
+      const int rb = t0 + tt * kTK + 8 * wv;      // token of the wave's first row
+      const bool in_tiles = tt < ntiles;
+      const int e[2] = {pg.e0, pg.e1};
+      rsrc_t rk[2], rw[2];
+      int32_t soff[2];
+      bool ok[2];
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const int tg = rb + 4 * g;
+        ok[g] = in_tiles & ((tg >> shift) < npages_grp) & (e[g] >= 0) & (e[g] < npool);
+        const int64_t pofs = ok[g] ? (int64_t)e[g] * page_bytes : 0;
+        rk[g] = make_rsrc(kg + pofs, ok[g] ? page_bytes : 0);
+        rw[g] = make_rsrc(vg + pofs, ok[g] ? page_bytes : 0);
+        soff[g] = (tg & (P - 1)) * row_stride;
+      }
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int t = t0 + tt * kTK + lrow[i];
+        const int32_t off = (t >= kb) & (t < ke) ? voff[i] : kOffsetNone;
+        char* dk = sk + (8 * wv + 4 * i) * RB;
+        char* dv = sv + (8 * wv + 4 * i) * RB;
+        if constexpr (D == 128) {
+          load_lds16(rk[i], dk, off, soff[i]);
+          load_lds16(rw[i], dv, off, soff[i]);
+        } else {
+          // Two exec-masked halves (their rows may sit in different pages); both write the
+          // block's 1 KB, lane l at 16 * l.
+          if (lane < 32) {
+            load_lds16(rk[0], dk, off, soff[0]);
+            load_lds16(rw[0], dv, off, soff[0]);
+          } else {
+            load_lds16(rk[1], dk, off, soff[1]);
+            load_lds16(rw[1], dv, off, soff[1]);
+          }
+        }
+      }
+      // Valid rows: inside [kb, ke) and in a valid page.
+      const int lo = min(max(kb - rb, 0), 8), hi = min(max(ke - rb, 0), 8);
+      uint32_t bits = hi > lo ? (((1u << hi) - 1u) & ~((1u << lo) - 1u)) : 0u;
+      bits &= (ok[0] ? 0x0Fu : 0u) | (ok[1] ? 0xF0u : 0u);
+      reinterpret_cast<uint8_t*>(flag)[wv] = (uint8_t)bits;
+    };
+
+    V16 qb[2][KS];   // Q^T operands: query row wv*32 + nt*16 + l16, head_dim ks*32 + 8*lg .. +8
     f4_t oacc[DM][2];
 #pragma unroll
     for (int dm = 0; dm < DM; ++dm)
@@ -140,158 +248,142 @@ __global__ __launch_bounds__(kThreads, 2) void prefix_kernel(const PrefixParams 
     float m_run[2] = {kNegInf, kNegInf};
     float l_run[2] = {0.f, 0.f};
 
-    // Page of this thread's token group in a tile (-1: no token of the group is in range).
-    auto page_of = [&](int tile) -> int {
-      const int tbase = t0 + tile * kTK + ld_tg * NPT;
-      int page = -1;
-      if (tile < ntiles && tbase < ke && tbase + NPT > kb) {
-        const int j = tbase >> shift;
-        if (j < npages_grp) page = pages[j];
-      }
-      return page;
-    };
-    // Global -> register staging of one tile.
-    V16 kst[NPT], vst[NPT];
-    uint32_t vflags = 0;
-    auto gather = [&](int tile, int page) {
-      const int tbase = t0 + tile * kTK + ld_tg * NPT;
-      const bool page_ok = page >= 0 && page < p.num_pages;
-      vflags = 0;
+    auto compute = [&](const char* ks_s, const char* vs_s, uint32_t mask) {
+      if (!wave_active) return;
+      // S^T[mt][nt]: tokens mt*16 + 4*lg + i, query column nt*16 + l16.
+      f4_t s[2][2];
 #pragma unroll
-      for (int u = 0; u < NPT; ++u) {
-        const int t = tbase + u;
-        const bool v = page_ok && t >= kb && t < ke;
-        vflags |= (v ? 1u : 0u) << (8 * u);
-        const int64_t off = (((int64_t)page << shift) + (t & (P - 1))) * row_stride + hk * D * ES + ld_c * 16;
-        kst[u] = load16_or_zero(kg, off, v);
-        vst[u] = load16_or_zero(vg, off, v);
-      }
-    };
-    // Registers -> LDS buffer: K and V row-major, flags.
-    auto stash = [&](int buf) {
-      char* ks_s = smem + buf * BUF;
-      char* vs_s = ks_s + KBYTES;
-      char* fl_s = vs_s + KBYTES;
+      for (int mt = 0; mt < 2; ++mt) {
+        s[mt][0] = f4_t{0.f, 0.f, 0.f, 0.f};
+        s[mt][1] = f4_t{0.f, 0.f, 0.f, 0.f};
+        const int r = mt * 16 + l16;
 #pragma unroll
-      for (int u = 0; u < NPT; ++u) {
-        const int off = (ld_tg * NPT + u) * STRIDE + ld_c * 16;
-        *reinterpret_cast<uint4*>(ks_s + off) = make_uint4(kst[u].w[0], kst[u].w[1], kst[u].w[2], kst[u].w[3]);
-        *reinterpret_cast<uint4*>(vs_s + off) = make_uint4(vst[u].w[0], vst[u].w[1], vst[u].w[2], vst[u].w[3]);
+        for (int ks = 0; ks < KS; ++ks) {
+          const int c = (ks * 4 + lg) ^ swz<D>(r);
+          const V16 a = lds_load16(ks_s + r * RB + c * 16);
+          s[mt][0] = Mfma<T>::run(a, qb[0][ks], s[mt][0]);
+          s[mt][1] = Mfma<T>::run(a, qb[1][ks], s[mt][1]);
+        }
       }
-      if (ld_c == 0) {
-        if constexpr (NPT == 4)
-          *reinterpret_cast<uint32_t*>(fl_s + ld_tg * NPT) = vflags;
-        else
-          *reinterpret_cast<uint16_t*>(fl_s + ld_tg * NPT) = (uint16_t)vflags;
+      // Tiles whose 32 tokens are all valid (every tile but the ragged ends) skip masking.
+      if (mask != ~0u) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const bool v = (mask >> (mt * 16 + 4 * lg + i)) & 1u;
+            s[mt][0][i] = v ? s[mt][0][i] : kNegInf;
+            s[mt][1][i] = v ? s[mt][1][i] : kNegInf;
+          }
+      }
+      V16 pb[2];   // P^T operands per query tile nt (the tile's 32 tokens are one step)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        float mx = kNegInf;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[mt][nt][i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mn = fmaxf(m_run[nt], mx * p.scale_log2);
+        const float mu = (mn == kNegInf) ? 0.f : mn;
+        const float alpha = fast_exp2(m_run[nt] - mu);
+        m_run[nt] = mn;
+        float psum = 0.f;
+        float pr[2][4];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            // P enters the PV product rounded to the operand type, but the denominator
+            // (and so the LSE) sums the fp32 weights: with bf16, summing rounded weights
+            // would move LSE by up to 2^-9.
+            pr[mt][i] = fast_exp2(fmaf(s[mt][nt][i], p.scale_log2, -mu));
+            psum += pr[mt][i];
+          }
+        l_run[nt] = l_run[nt] * alpha + psum;
+        // Once the running maxima settle, alpha is 1 on every lane: skip the rescale.
+        if (!wave_all(alpha == 1.f)) {
+#pragma unroll
+          for (int dm = 0; dm < DM; ++dm) oacc[dm][nt] *= alpha;
+        }
+        pb[nt].w[0] = Mfma<T>::pack(pr[0][0], pr[0][1]);
+        pb[nt].w[1] = Mfma<T>::pack(pr[0][2], pr[0][3]);
+        pb[nt].w[2] = Mfma<T>::pack(pr[1][0], pr[1][1]);
+        pb[nt].w[3] = Mfma<T>::pack(pr[1][2], pr[1][3]);
+      }
+      // O^T[dm][nt] += V^T * P^T over the tile's 32 tokens.  Lane group g supplies contraction
+      // elements 8g .. 8g+7 = tokens 16h + 4g + i (h = 0, 1; i = 0..3), the order of the S^T
+      // accumulators; each half is one transpose read of rows 16h + 4g + tr_row, elements
+      // dm*16 + 4*tr_piece .. +4 (logical chunk 2*dm + tr_piece/2, swizzled by row).
+#pragma unroll
+      for (int dm = 0; dm < DM; ++dm) {
+        V16 a;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int r = 16 * h + 4 * lg + tr_row;
+          const int c = (2 * dm + (tr_piece >> 1)) ^ swz<D>(r);
+          const uint2 x = lds_read_tr(vs_s + r * RB + c * 16 + (tr_piece & 1) * 8);
+          a.w[2 * h] = x.x;
+          a.w[2 * h + 1] = x.y;
+        }
+        oacc[dm][0] = Mfma<T>::run(a, pb[0], oacc[dm][0]);
+        oacc[dm][1] = Mfma<T>::run(a, pb[1], oacc[dm][1]);
       }
     };
 
-    int pg_next = -1;
     if (ntiles > 0) {
-      const int pg0 = page_of(0);
-      pg_next = page_of(1);
-      gather(0, pg0);
-      stash(0);
-      __syncthreads();
-    }
-    for (int ti = 0; ti < ntiles; ++ti) {
-      const int cur = ti & 1;
-      if (ti + 1 < ntiles) {
-        const int pg = pg_next;
-        pg_next = page_of(ti + 2);   // consumed next iteration: its latency hides behind this one
-        gather(ti + 1, pg);
+      // Q^T operands first, so that the ring's waits below also cover them.  Rows past the
+      // tile read the tile's first row: their columns are computed but never stored.
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int r = wv * kRowsPerWave + nt * 16 + l16;
+        const int rr = r < nrows ? r : 0;
+        const int64_t qoff = ((int64_t)(q0 + rr / G) * p.hq + hk * G + rr % G) * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          qb[nt][ks] = load16(static_cast<const char*>(p.q) + (qoff + ks * 32 + 8 * lg) * ES);
       }
-      if (wave_active) {
-        const char* ks_s = smem + cur * BUF;
-        const char* vs_s = ks_s + KBYTES;
-        const char* fl_s = vs_s + KBYTES;
-        // S^T[mt][nt]: tokens mt*16 + 4*lg + i, query column nt*16 + l16.
-        f4_t s[4][2];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          s[mt][0] = f4_t{0.f, 0.f, 0.f, 0.f};
-          s[mt][1] = f4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            const V16 a = lds_load16(ks_s + (mt * 16 + l16) * STRIDE + (ks * 32 + 8 * lg) * ES);
-            s[mt][0] = Mfma<T>::run(a, qb[0][ks], s[mt][0]);
-            s[mt][1] = Mfma<T>::run(a, qb[1][ks], s[mt][1]);
-          }
-        }
-        uint32_t fl[4];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) fl[mt] = *reinterpret_cast<const uint32_t*>(fl_s + mt * 16 + 4 * lg);
-        // Tiles whose 64 tokens are all valid (every tile but the ragged ends) skip masking.
-        const bool full = wave_all((fl[0] & fl[1] & fl[2] & fl[3]) == 0x01010101u);
-        if (!full) {
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const bool v = (fl[mt] >> (8 * i)) & 1u;
-              s[mt][0][i] = v ? s[mt][0][i] : kNegInf;
-              s[mt][1][i] = v ? s[mt][1][i] : kNegInf;
-            }
-        }
-        V16 pb[2][2];   // P^T operands [nt][contraction step]
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          float mx = kNegInf;
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[mt][nt][i]);
-          mx = fmaxf(mx, __shfl_xor(mx, 16));
-          mx = fmaxf(mx, __shfl_xor(mx, 32));
-          const float mn = fmaxf(m_run[nt], mx * p.scale_log2);
-          const float mu = (mn == kNegInf) ? 0.f : mn;
-          const float alpha = fast_exp2(m_run[nt] - mu);
-          m_run[nt] = mn;
-          float psum = 0.f;
-          float pr[4][4];
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              // P enters the PV product rounded to the operand type, but the denominator
-              // (and so the LSE) sums the fp32 weights: with bf16, summing rounded weights
-              // would move LSE by up to 2^-9.
-              pr[mt][i] = fast_exp2(fmaf(s[mt][nt][i], p.scale_log2, -mu));
-              psum += pr[mt][i];
-            }
-          l_run[nt] = l_run[nt] * alpha + psum;
-          // Once the running maxima settle, alpha is 1 on every lane: skip the rescale.
-          if (!wave_all(alpha == 1.f)) {
-#pragma unroll
-            for (int dm = 0; dm < DM; ++dm) oacc[dm][nt] *= alpha;
-          }
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk) {
-            pb[nt][kk].w[0] = Mfma<T>::pack(pr[2 * kk][0], pr[2 * kk][1]);
-            pb[nt][kk].w[1] = Mfma<T>::pack(pr[2 * kk][2], pr[2 * kk][3]);
-            pb[nt][kk].w[2] = Mfma<T>::pack(pr[2 * kk + 1][0], pr[2 * kk + 1][1]);
-            pb[nt][kk].w[3] = Mfma<T>::pack(pr[2 * kk + 1][2], pr[2 * kk + 1][3]);
-          }
-        }
-        // O^T[dm][nt] += V^T * P^T.  Contraction step kk covers tokens kk*32 .. +32; lane
-        // group g supplies contraction elements 8g .. 8g+7 = tokens kk*32 + 16h + 4g + i
-        // (h = 0, 1; i = 0..3), the order of the S^T accumulators; each half is one
-        // transpose read of rows kk*32 + 16h + 4g + tr_row, columns dm*16 + 4*tr_piece.
-#pragma unroll
-        for (int dm = 0; dm < DM; ++dm)
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk) {
-            const char* base = vs_s + (kk * 32 + 4 * lg + tr_row) * STRIDE + (dm * 16 + 4 * tr_piece) * ES;
-            const uint2 lo = lds_read_tr(base);
-            const uint2 hi = lds_read_tr(base + 16 * STRIDE);
-            V16 a;
-            a.w[0] = lo.x; a.w[1] = lo.y; a.w[2] = hi.x; a.w[3] = hi.y;
-            oacc[dm][0] = Mfma<T>::run(a, pb[0][kk], oacc[dm][0]);
-            oacc[dm][1] = Mfma<T>::run(a, pb[1][kk], oacc[dm][1]);
-          }
+      // Ring prologue: tiles 0..2 in flight; page entries of tile 3 requested.
+      Pg pg = fetch(0);
+      issue(0, pg, sk0, sv0, &sflag[0]);
+      pg = fetch(1);
+      issue(1, pg, sk1, sv1, &sflag[1]);
+      pg = fetch(2);
+      issue(2, pg, sk2, sv2, &sflag[2]);
+      pg = fetch(3);
+
+      // Step for tile tt in stage S: wait for this wave's loads of tile tt (tiles tt+1 and
+      // tt+2 stay in flight), barrier (every wave's loads of tt have landed and every wave is
+      // done reading stage S-1), refill stage S-1 with tile tt+3, request tile tt+4's page
+      // entries, compute tile tt.  No LDS wait is needed before the barrier: a wave's LDS
+      // operations complete in order, and the compiler waits for the last operand read of a
+      // tile before its final products, so by the end of a step the wave's valid-row byte is
+      // written and its reads of the stage are done.
+      auto step = [&](auto stage, int tt) {
+        constexpr int S = decltype(stage)::value;
+        constexpr int N = (S + 3) & 3;
+        char* const sk = S == 0 ? sk0 : S == 1 ? sk1 : S == 2 ? sk2 : sk3;
+        char* const sv = S == 0 ? sv0 : S == 1 ? sv1 : S == 2 ? sv2 : sv3;
+        char* const nk = N == 0 ? sk0 : N == 1 ? sk1 : N == 2 ? sk2 : sk3;
+        char* const nv = N == 0 ? sv0 : N == 1 ? sv1 : N == 2 ? sv2 : sv3;
+        PKC_WAIT_VMCNT(2 * NDMA);
+        ring_barrier();
+        const uint32_t mask = __builtin_amdgcn_readfirstlane(sflag[S]);
+        issue(tt + 3, pg, nk, nv, &sflag[N]);
+        pg = fetch(tt + 4);
+        compute(sk, sv, mask);
+      };
+      for (int tt = 0; tt < ntiles; tt += 4) {
+        step(std::integral_constant<int, 0>(), tt);
+        if (tt + 1 >= ntiles) break;
+        step(std::integral_constant<int, 1>(), tt + 1);
+        if (tt + 2 >= ntiles) break;
+        step(std::integral_constant<int, 2>(), tt + 2);
+        if (tt + 3 >= ntiles) break;
+        step(std::integral_constant<int, 3>(), tt + 3);
       }
-      if (ti + 1 < ntiles) stash(cur ^ 1);
-      __syncthreads();
     }
 
     // Finish: total sum over the 4 lane groups, normalise, write the fp32 state.
@@ -317,6 +409,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefix_kernel(const PrefixParams 
         }
       }
     }
+    // Every load (including the empty ones past the last tile) and store of this item is done
+    // and every wave has left the ring before the next item refills it.
+    __builtin_amdgcn_s_waitcnt(0);
+    ring_barrier();
   }
 }
 
@@ -350,6 +446,7 @@ hipError_t launch_prefix(pkc_dtype dt, int head_dim, int group, int tile_q, cons
                          int grid_x, hipStream_t s) {
   if (grid_x <= 0) return hipSuccess;
   if (tile_q * group > 4 * kRowsPerWave) return hipErrorInvalidValue;
+  if (p.page_size < 4) return hipErrorInvalidValue;
   switch (dt) {
     case PKC_F16: return launch_prefix_d<F16>(head_dim, group, p, grid_x, s);
     case PKC_BF16: return launch_prefix_d<BF16>(head_dim, group, p, grid_x, s);
