@@ -229,8 +229,8 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(const DecodeParams p) {
           const rsrc_t rk = make_rsrc(kbase + pofs, pv ? page_bytes : 0);
           const rsrc_t rv = make_rsrc(vbase + pofs, pv ? page_bytes : 0);
           const int32_t off = v ? (t & (P - 1)) * slot_stride32 + head_off32 : kOffsetNone;
-          kr[i] = buffer_load16(rk, off);
-          vr[i] = buffer_load16(rv, off);
+          kr[i] = buffer_load16<kCachePolicyStream>(rk, off);
+          vr[i] = buffer_load16<kCachePolicyStream>(rv, off);
         } else {
           bool v = (t >= tb) && (t < te);
           const int page = v ? bt[t >> shift] : -1;

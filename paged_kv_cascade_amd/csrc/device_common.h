@@ -105,9 +105,14 @@ constexpr int32_t kOffsetNone = INT32_MIN;   // 0x80000000: past any range a ker
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kBufferWord3);
 }
+// Cache-policy operand of buffer loads: the nontemporal hint (read once, do not keep).  KV
+// rows are streamed exactly once per step, and on MI355X a read stream with the hint runs
+// about 10% faster than without it.
+constexpr int kCachePolicyStream = 2;
+template <int AUX = 0>
 __device__ __forceinline__ V16 buffer_load16(rsrc_t r, int32_t off) {
   typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
-  const u4_t x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  const u4_t x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX);
   V16 v;
   v.w[0] = x[0]; v.w[1] = x[1]; v.w[2] = x[2]; v.w[3] = x[3];
   return v;

@@ -84,9 +84,10 @@ __device__ __forceinline__ uint2 lds_read_tr(const char* p) {
   return __builtin_bit_cast(uint2, r);
 }
 
-// Buffer load of 16 bytes per lane into LDS: lane l writes lds + 16 * l.
+// Buffer load of 16 bytes per lane into LDS (nontemporal): lane l writes lds + 16 * l.
 __device__ __forceinline__ void load_lds16(rsrc_t r, char* lds, int32_t voff, int32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0,
+                                           kCachePolicyStream);
 }
 
 // s_waitcnt on the vector-memory count only (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt in
