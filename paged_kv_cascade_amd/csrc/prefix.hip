@@ -41,6 +41,7 @@ namespace {
 constexpr int kTK = 32;        // KV tokens per tile
 constexpr int kThreads = 256;  // 4 waves
 constexpr int kRowsPerWave = 32;
+constexpr float kSlack = 8.f;  // lazy-rescale margin of the running maximum, log2 units
 
 typedef short s4_t __attribute__((ext_vector_type(4)));
 typedef float f2_t __attribute__((ext_vector_type(2)));
@@ -65,9 +66,26 @@ template <> struct Mfma<BF16> {
   }
 };
 
-// True on every lane when `pred` holds on every active lane of the wave.
-__device__ __forceinline__ bool wave_all(bool pred) {
-  return __builtin_amdgcn_ballot_w64(!pred) == 0;
+// True on every lane when `pred` holds on some active lane of the wave.
+__device__ __forceinline__ bool wave_any(bool pred) {
+  return __builtin_amdgcn_ballot_w64(pred) != 0;
+}
+
+// Reductions over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the lane groups that hold one
+// query column of an S^T tile), with the gfx950 lane-swap instructions: permlane32_swap of a
+// value with itself leaves lanes l and l ^ 32 in the two results, permlane16_swap likewise
+// for l ^ 16.
+__device__ __forceinline__ float lane_groups_max(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float lane_groups_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 __device__ __forceinline__ V16 lds_load16(const char* p) {
@@ -285,12 +303,22 @@ __global__ __launch_bounds__(kThreads, 2) void prefix_kernel(const PrefixParams 
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[mt][nt][i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mn = fmaxf(m_run[nt], mx * p.scale_log2);
-        const float mu = (mn == kNegInf) ? 0.f : mn;
-        const float alpha = fast_exp2(m_run[nt] - mu);
-        m_run[nt] = mn;
+        mx = lane_groups_max(mx) * p.scale_log2;
+        // Lazy reference maximum: m_run moves only when a score exceeds it by more than
+        // kSlack (log2 units), so O and l are rescaled only on such tiles (in practice the
+        // first ones).  Weights stay below 2^kSlack, which fp32 and the 16-bit operand types
+        // hold with their usual relative precision, and the final state (O / l, m + log2 l)
+        // does not depend on the reference used.  A fully masked column (mx = -inf) never
+        // raises its reference.
+        const bool raise = mx > m_run[nt] + kSlack;
+        if (wave_any(raise)) {
+          const float alpha = raise ? fast_exp2(m_run[nt] - mx) : 1.f;
+          m_run[nt] = raise ? mx : m_run[nt];
+          l_run[nt] *= alpha;
+#pragma unroll
+          for (int dm = 0; dm < DM; ++dm) oacc[dm][nt] *= alpha;
+        }
+        const float mu = (m_run[nt] == kNegInf) ? 0.f : m_run[nt];
         float psum = 0.f;
         float pr[2][4];
 #pragma unroll
@@ -303,12 +331,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefix_kernel(const PrefixParams 
             pr[mt][i] = fast_exp2(fmaf(s[mt][nt][i], p.scale_log2, -mu));
             psum += pr[mt][i];
           }
-        l_run[nt] = l_run[nt] * alpha + psum;
-        // Once the running maxima settle, alpha is 1 on every lane: skip the rescale.
-        if (!wave_all(alpha == 1.f)) {
-#pragma unroll
-          for (int dm = 0; dm < DM; ++dm) oacc[dm][nt] *= alpha;
-        }
+        l_run[nt] += psum;
         pb[nt].w[0] = Mfma<T>::pack(pr[0][0], pr[0][1]);
         pb[nt].w[1] = Mfma<T>::pack(pr[0][2], pr[0][3]);
         pb[nt].w[2] = Mfma<T>::pack(pr[1][0], pr[1][1]);
@@ -371,7 +394,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefix_kernel(const PrefixParams 
         char* const nv = N == 0 ? sv0 : N == 1 ? sv1 : N == 2 ? sv2 : sv3;
         PKC_WAIT_VMCNT(2 * NDMA);
         ring_barrier();
-        const uint32_t mask = __builtin_amdgcn_readfirstlane(sflag[S]);
+        const uint32_t mask = sflag[S];   // the same on every lane; first needed after S^T
         issue(tt + 3, pg, nk, nv, &sflag[N]);
         pg = fetch(tt + 4);
         compute(sk, sv, mask);
@@ -391,9 +414,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefix_kernel(const PrefixParams 
     if (wave_active) {
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        float lt = l_run[nt];
-        lt += __shfl_xor(lt, 16);
-        lt += __shfl_xor(lt, 32);
+        const float lt = lane_groups_sum(l_run[nt]);
         const int r = wv * kRowsPerWave + nt * 16 + l16;
         if (r < nrows) {
           const float inv = lt > 0.f ? 1.f / lt : 0.f;

@@ -178,3 +178,34 @@ def test_cascade_equals_flat_decode(api):
     O, L = _oracle(w)
     check_state(o, lse, O, L, torch.float16, "cascade")
     check_state(o2, lse2, O, L, torch.float16, "flat decode")
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+def test_cascade_growing_and_spiking_scores(api, dtype):
+    """Scores whose maximum keeps rising along the prefix (by ~32 in log2 units) plus one
+    spike in a middle tile: the prefix kernel's running reference maximum must move on
+    later tiles, not only on the first one."""
+    say(f"case: cascade with rising prefix scores and a spike, {dtype}")
+    w = workloads.cascade_two_level(batch=24, prefix_len=3000, suffix_len=70, device="cuda", seed=21,
+                                    dtype=dtype)
+    D, P = w.head_dim, w.page_size
+    gen = torch.Generator(device="cuda").manual_seed(77)
+    u = torch.ones(D, device="cuda") / math.sqrt(D)
+    # token t of the pool (prefix pages are the run 0..: t = page * P + slot) gets a key along u
+    # with amplitude rising from -8 to 8 over the prefix; one token in the middle gets 20.
+    npg = w.k_pool.shape[0]
+    t = torch.arange(npg * P, device="cuda", dtype=torch.float32).view(npg, P)
+    amp = -8.0 + 16.0 * t / 3000.0
+    amp[(t >= 3000)] = 0.5
+    amp.view(-1)[1543] = 20.0
+    noise = torch.randn(npg, P, w.num_kv_heads, D, generator=gen, device="cuda") * 0.05
+    k = amp[:, :, None, None] * u + noise
+    keep_nan = torch.isnan(w.k_pool)
+    w.k_pool.copy_(k.to(dtype))
+    w.k_pool[keep_nan] = float("nan")
+    q = 16.0 * u + torch.randn(w.batch, w.num_qo_heads, D, generator=gen, device="cuda") * 0.05
+    w.q.copy_(q.to(dtype))
+    o, lse, *_ = _run_cascade(api, w, level_ctas=3)
+    torch.cuda.synchronize()
+    O, L = _oracle(w)
+    check_state(o, lse, O, L, dtype, "rising scores")
