@@ -106,8 +106,9 @@ typedef struct pkc_plan_params {
   int32_t num_kv_heads; /* Hkv (divides Hq) */
   int32_t head_dim;     /* D */
   int32_t page_size;    /* P */
-  int32_t num_ctas;     /* #CTA of the decode stage; 0 -> ceil(8 x compute units / Hkv), so the
-                           stage launches about 8 workgroups per compute unit */
+  int32_t num_ctas;     /* #CTA of the decode stage; 0 -> max(ceil(8 x compute units / Hkv),
+                           batch): about 8 workgroups per compute unit, at least one CTA per
+                           request */
   int32_t level_ctas;   /* #CTA of every cascade level; 0 -> ceil(2 x compute units / Hkv) */
   int32_t level_tile_q; /* T_q of the cascade levels (queries per tile); 0 -> 128 / (Hq/Hkv) */
   int32_t chunk_align;  /* round L_kv up to a multiple of this; 0 or 1 -> no rounding */

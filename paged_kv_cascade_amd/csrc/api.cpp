@@ -215,8 +215,10 @@ bool host_buf_is_pinned(const void* host_buf) {
 // Checks the parameters and fills #CTA defaults from the current device.  A stage launches
 // #CTA x Hkv workgroups.  Decode workgroups are small (4 waves, a few dozen VGPRs each) and
 // several fit on a compute unit, so the decode default is about 8 workgroups per compute
-// unit, #CTA = ceil(8 x CUs / Hkv); a level's MFMA workgroup holds 70 KB of LDS, two fit on a
-// compute unit, so the level default is #CTA = ceil(2 x CUs / Hkv).
+// unit and at least one CTA per request, #CTA = max(ceil(8 x CUs / Hkv), batch): a CTA that
+// walks two requests pays its start-up and drain twice, which costs more than an extra
+// round of workgroups.  A level's MFMA workgroup holds 64 KB of LDS, two fit on a compute
+// unit, so the level default is #CTA = ceil(2 x CUs / Hkv).
 pkc_status resolve_params(const pkc_plan_params* params, pkc::Resolved* r) {
   pkc_status st = pkc::check_params(params, false, r);
   if (st != PKC_OK) return st;
@@ -224,7 +226,8 @@ pkc_status resolve_params(const pkc_plan_params* params, pkc::Resolved* r) {
     int32_t cus = 0;
     if ((st = device_cus(&cus)) != PKC_OK) return st;
     if (r->p.num_ctas == 0)
-      r->p.num_ctas = (int32_t)std::max<int64_t>(1, pkc::ceil_div(8 * (int64_t)cus, r->p.num_kv_heads));
+      r->p.num_ctas = (int32_t)std::max<int64_t>(
+          std::max<int64_t>(1, r->p.batch), pkc::ceil_div(8 * (int64_t)cus, r->p.num_kv_heads));
     if (r->p.level_ctas == 0)
       r->p.level_ctas = (int32_t)std::max<int64_t>(1, pkc::ceil_div(2 * (int64_t)cus, r->p.num_kv_heads));
   }
