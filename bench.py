@@ -269,6 +269,23 @@ def main():
             "traffic": (traffic or {}).get(dom, {}).get("hbm_bytes_per_launch") if traffic else None,
             "alg_bytes_per_launch": kern[dom]["alg_bytes"], "avg_launch_us": kern[dom]["avg_us"]}
 
+    # The device's achievable read rate: one nontemporal 16-byte-load stream over 2 GiB.
+    buf = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = api.read_stream_probe(buf)
+    for _ in range(2):
+        api.read_stream_probe(buf, sink)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(10):
+        api.read_stream_probe(buf, sink)
+    ev1.record()
+    torch.cuda.synchronize()
+    stream_gbps = buf.numel() / (ev0.elapsed_time(ev1) / 10 * 1e-3) / 1e9
+    del buf, sink
+    for name in ("prefix_mfma", "suffix_decode"):
+        kern[name]["frac_of_read_stream_peak"] = round(kern[name]["achieved_GBps"] / stream_gbps, 4)
+
     value = alg_bytes / (ms_step * 1e-3) / 1e9
     line = {
         "metric": METRIC,
@@ -288,6 +305,8 @@ def main():
                    "page_size": w.page_size, "alg_kv_bytes_per_step": alg_bytes},
         "steps_per_s": round(1e3 / ms_step, 1),
         "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBPS, 2),
+        "read_stream_peak_GBps": round(stream_gbps, 1),
+        "pct_of_read_stream_peak": round(100 * value / stream_gbps, 2),
         "ms_per_step_device_only": round(ms_dev, 4),
         "ms_plan_cpu": round(ms_plan, 4),
         "kernels": kern,

@@ -333,6 +333,17 @@ pkc_status pkc_debug_cta_trace(const pkc_plan_info* plan, int32_t stage, const v
                                int32_t max_items_per_cta, void* stream);
 
 /*
+ * Measurement export: reads `bytes` bytes of device memory at `src` once, as a stream of
+ * 16-byte nontemporal loads with 16 loads in flight per lane (the load form the attention
+ * kernels use for K and V), so that its duration gives the device's achievable HBM read
+ * rate.  `bytes` must be a positive multiple of 1 MiB and `src` 16-byte aligned; `sink`
+ * (device, caller-owned) receives bytes / 1 MiB * 256 uint32 values (sink_len counts them).
+ * Enqueued on `stream`; returns PKC_ERR_INVALID_ARG on bad sizes or alignment.
+ */
+pkc_status pkc_read_stream_probe(const void* src, int64_t bytes, uint32_t* sink, int64_t sink_len,
+                                 void* stream);
+
+/*
  * Per-kernel timing with HIP events (for measurements): when enabled, every kernel launch
  * of the calls above is bracketed by events recorded on the same stream.  pkc_timing_read
  * waits for the recorded events and returns, per kernel kind, the number of launches and the

@@ -116,6 +116,7 @@ SIGNATURES = {
     "pkc_timing_enable": (_I32, [_I32]),
     "pkc_timing_reset": (_I32, []),
     "pkc_timing_read": (_I32, [_I32, ctypes.POINTER(_I64), ctypes.POINTER(ctypes.c_double)]),
+    "pkc_read_stream_probe": (_I32, [_P, _I64, _P, _I64, _P]),
 }
 
 
@@ -408,6 +409,17 @@ def timing_read(kind):
     n, ms = _I64(), ctypes.c_double()
     _check(lib.pkc_timing_read(kind, ctypes.byref(n), ctypes.byref(ms)))
     return n.value, ms.value
+
+
+def read_stream_probe(buf: torch.Tensor, sink: torch.Tensor = None):
+    """pkc_read_stream_probe: one nontemporal read pass over `buf` (a device tensor whose byte
+    size is a multiple of 1 MiB), on torch's current stream.  Returns the sink tensor."""
+    nbytes = buf.numel() * buf.element_size()
+    n = nbytes // (1 << 20) * 256
+    if sink is None:
+        sink = torch.empty(max(n, 1), dtype=torch.int32, device=buf.device)
+    _check(lib.pkc_read_stream_probe(_ptr(buf), nbytes, _ptr(sink), sink.numel(), _stream(buf.device)))
+    return sink
 
 
 def read_plan_arrays(info: PlanInfo, host_buf: torch.Tensor):

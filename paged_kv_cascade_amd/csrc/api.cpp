@@ -566,6 +566,20 @@ pkc_status pkc_debug_cta_trace(const pkc_plan_info* plan, int32_t stage, const v
   PKC_TRY_END("pkc_debug_cta_trace")
 }
 
+pkc_status pkc_read_stream_probe(const void* src, int64_t bytes, uint32_t* sink, int64_t sink_len,
+                                 void* stream) {
+  PKC_TRY_BEGIN
+  constexpr int64_t kMiB = 1 << 20;
+  if (!src || !sink || bytes <= 0 || bytes % kMiB)
+    return fail(PKC_ERR_INVALID_ARG, "read probe: src and sink must be set, bytes a positive multiple of 1 MiB");
+  if (reinterpret_cast<uintptr_t>(src) & 15) return fail(PKC_ERR_INVALID_ARG, "read probe: src must be 16-byte aligned");
+  if (sink_len < bytes / kMiB * 256) return fail(PKC_ERR_WORKSPACE_TOO_SMALL, "read probe: sink too small");
+  hipError_t e = pkc::launch_read_stream(src, bytes / kMiB, sink, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "read probe launch");
+  return PKC_OK;
+  PKC_TRY_END("pkc_read_stream_probe")
+}
+
 pkc_status pkc_timing_enable(int32_t enable) {
   g_timing = enable != 0;
   return PKC_OK;

@@ -93,6 +93,9 @@ hipError_t launch_merge_inplace(pkc_dtype dt, int head_dim, void* o_a, float* ls
                                 hipStream_t s);
 // Copies `bytes` (a multiple of 16, 16-byte aligned) from pinned host memory to the device.
 hipError_t launch_plan_upload(const void* host_src, void* dev_dst, int64_t bytes, hipStream_t s);
+// Reads `mib` MiB of src (16-byte aligned) once as a nontemporal stream; sink gets mib * 256
+// uint32 values.
+hipError_t launch_read_stream(const void* src, int64_t mib, uint32_t* sink, hipStream_t s);
 hipError_t launch_debug_gather(const int32_t* block_table, int32_t max_blocks,
                                const int32_t* seqlens, const int32_t* kv_start, int32_t batch,
                                int32_t page_shift, int64_t num_pages, int32_t* rows_out,

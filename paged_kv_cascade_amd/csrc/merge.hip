@@ -158,6 +158,35 @@ hipError_t launch_plan_upload(const void* host_src, void* dev_dst, int64_t bytes
   return hipGetLastError();
 }
 
+// Read-stream probe (measurement only): workgroup g reads bytes [g MiB, (g+1) MiB) of src,
+// wave w its w-th quarter, each lane 16 bytes per load with 16 loads in flight and the
+// nontemporal hint of the KV streams; one XOR per thread goes to sink so nothing is elided.
+__global__ __launch_bounds__(256) void read_stream_kernel(const uint4* __restrict__ src,
+                                                          uint32_t* __restrict__ sink) {
+  typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+  constexpr int kWaveBytes = 256 * 1024;
+  constexpr int kLoads = kWaveBytes / 1024;     // 1 KB per wave load instruction
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const u4v* p = reinterpret_cast<const u4v*>(src) + ((int64_t)blockIdx.x * 4 + wv) * (kWaveBytes / 16) + lane;
+  uint32_t acc = 0;
+  for (int i = 0; i < kLoads; i += 16) {
+    u4v v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = __builtin_nontemporal_load(p + (i + u) * 64);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  sink[(int64_t)blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
+hipError_t launch_read_stream(const void* src, int64_t mib, uint32_t* sink, hipStream_t s) {
+  if (mib <= 0) return hipSuccess;
+  hipLaunchKernelGGL(read_stream_kernel, dim3((unsigned)mib), dim3(256), 0, s,
+                     static_cast<const uint4*>(src), sink);
+  return hipGetLastError();
+}
+
 template <typename TO>
 static hipError_t merge_plan_d(int head_dim, const MergePlanParams& p, hipStream_t s) {
   if (p.batch <= 0) return hipSuccess;
