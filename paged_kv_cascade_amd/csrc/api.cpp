@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <cstdlib>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -191,8 +192,19 @@ pkc_status run_level(const pkc_plan_info* plan, int level, const void* q, const 
   p.indptr = at<int32_t>(ws, plan->off_lvl_indptr[level]);
   p.items = at<int32_t>(ws, plan->off_lvl_items[level]);
   const int g = plan->num_qo_heads / plan->num_kv_heads;
+  // A level whose workgroups fit one per compute unit runs them with 8 waves (two tile streams
+  // merged at the end of each item), so every SIMD still holds two waves; otherwise 4-wave
+  // workgroups, two per compute unit.  PKC_PREFIX_STREAMS (1 or 2) overrides, for measurements.
+  int32_t cus = 0;
+  pkc_status st = device_cus(&cus);
+  if (st != PKC_OK) return st;
+  int streams = (int64_t)plan->level_ctas * plan->num_kv_heads <= cus ? 2 : 1;
+  if (const char* e = std::getenv("PKC_PREFIX_STREAMS")) {
+    const int v = std::atoi(e);
+    if (v == 1 || v == 2) streams = v;
+  }
   return timed(1, s, "prefix kernel launch", [&] {
-    return pkc::launch_prefix(dtype, plan->head_dim, g, plan->lvl_tile_q[level], p,
+    return pkc::launch_prefix(dtype, plan->head_dim, g, plan->lvl_tile_q[level], streams, p,
                               plan->level_ctas, s);
   });
 }

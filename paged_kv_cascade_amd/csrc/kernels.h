@@ -82,8 +82,10 @@ struct MergeGenericParams {
 
 hipError_t launch_decode(pkc_dtype dt, int head_dim, int group, int waves, const DecodeParams& p,
                          int grid_x, hipStream_t s);
-hipError_t launch_prefix(pkc_dtype dt, int head_dim, int group, int tile_q, const PrefixParams& p,
-                         int grid_x, hipStream_t s);
+// streams: 1 = 4-wave workgroups (two per compute unit), 2 = 8-wave workgroups whose two
+// 4-wave halves take alternate tiles of an item and merge at its end (one per compute unit).
+hipError_t launch_prefix(pkc_dtype dt, int head_dim, int group, int tile_q, int streams,
+                         const PrefixParams& p, int grid_x, hipStream_t s);
 hipError_t launch_merge_plan(pkc_dtype out_dt, int head_dim, const MergePlanParams& p,
                              hipStream_t s);
 hipError_t launch_merge_generic(pkc_dtype in_dt, pkc_dtype out_dt, int head_dim,

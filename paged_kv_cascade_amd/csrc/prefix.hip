@@ -39,7 +39,7 @@ namespace pkc {
 namespace {
 
 constexpr int kTK = 32;        // KV tokens per tile
-constexpr int kThreads = 256;  // 4 waves
+constexpr int kWavesPerStream = 4;  // 4 waves x 32 query rows = one 128-row tile
 constexpr int kRowsPerWave = 32;
 constexpr float kSlack = 8.f;  // lazy-rescale margin of the running maximum, log2 units
 
@@ -102,11 +102,33 @@ __device__ __forceinline__ uint2 lds_read_tr(const char* p) {
   return __builtin_bit_cast(uint2, r);
 }
 
-// Buffer load of 16 bytes per lane into LDS (nontemporal): lane l writes lds + 16 * l.
-__device__ __forceinline__ void load_lds16(rsrc_t r, char* lds, int32_t voff, int32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0,
-                                           kCachePolicyStream);
+// Buffer resource words for the LDS-writing loads below (raw addressing, no swizzle, the
+// same word 3 as make_rsrc): `bytes` bytes at `base`; an offset at or past `bytes` reads zeros.
+typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u4_t dma_rsrc(const void* base, int32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return u4_t{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, (uint32_t)bytes, (uint32_t)kBufferWord3};
 }
+
+// Nontemporal buffer load of 16 bytes per lane straight into LDS: lane l writes lds + 16 * l
+// (M0 holds the LDS address).  Written as an asm statement, so the compiler neither moves
+// memory accesses across it nor adds waits of its own for it: the ring below orders these
+// loads against the LDS reads with explicit vector-memory waits and barriers.
+__device__ __forceinline__ void load_lds16(u4_t r, char* lds, int32_t voff, int32_t soff) {
+  const uint32_t m0 = (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)lds);
+  __asm__ volatile("buffer_load_dwordx4 %0, %1, %2 offen nt lds" ::"v"(voff), "s"(r), "s"(soff), "{m0}"(m0)
+                   : "memory");
+}
+
+// 16-byte global load whose completion the caller orders with an explicit vector-memory wait
+// (the compiler does not count the asm loads above, so it must not place that wait itself).
+// The value must pass through ready() after the wait and before its first use.
+__device__ __forceinline__ u4_t load16_async(const void* p) {
+  u4_t x;
+  __asm__ volatile("global_load_dwordx4 %0, %1, off" : "=v"(x) : "v"(p) : "memory");
+  return x;
+}
+__device__ __forceinline__ void ready(u4_t& x) { __asm__ volatile("" : "+v"(x)); }
 
 // s_waitcnt on the vector-memory count only (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt in
 // 6:4, lgkmcnt in 11:8; the others at their maxima).
@@ -132,27 +154,29 @@ __device__ __forceinline__ int swz(int r) {
 
 }  // namespace
 
-template <typename T, int D, int G>
-__global__ __launch_bounds__(kThreads, 2) void prefix_kernel(const PrefixParams p) {
+template <typename T, int D, int G, int NS>
+__global__ __launch_bounds__(64 * kWavesPerStream * NS, NS == 1 ? 2 : 1) void prefix_kernel(const PrefixParams p) {
   constexpr int ES = 2;
   constexpr int RB = D * ES;                 // bytes per K / V row
   constexpr int CPR = RB / 16;               // 16-byte chunks per row
   constexpr int NDMA = 4;                    // load instructions per wave per tile (K and V)
-  constexpr int STB = kTK * RB;              // bytes of K (or V) per stage
+  constexpr int STB = kTK * RB;              // bytes of K (or V) of one tile
+  constexpr int SLOT = 2 * STB;              // one tile in LDS: K rows, then V rows
+  constexpr int STAGES = 4;
   constexpr int KS = D / 32;                 // contraction steps of S^T
   constexpr int DM = D / 16;                 // 16-row tiles of O^T
-  static_assert(kTK == 32 && kThreads == 256 && (D == 64 || D == 128), "tile layout");
+  static_assert(kTK == 32 && (D == 64 || D == 128) && (NS == 1 || NS == 2), "tile layout");
 
-  // One array per stage and operand: the compiler tracks LDS-writing loads per array, so a
-  // read of one stage waits only for that stage's loads.
-  __shared__ __attribute__((aligned(16))) char sk0[STB], sk1[STB], sk2[STB], sk3[STB];
-  __shared__ __attribute__((aligned(16))) char sv0[STB], sv1[STB], sv2[STB], sv3[STB];
-  // Valid-row bits of the tile in each stage: byte w is written by wave w for its 8 rows.
-  __shared__ uint32_t sflag[4];
+  // The ring: stage s of stream g is ring + (g * STAGES + s) * SLOT; the valid-row bits of that
+  // tile are word g * STAGES + s of sflag (byte w written by the stream's wave w).
+  __shared__ __attribute__((aligned(16))) char ring[STAGES * NS * SLOT];
+  __shared__ uint32_t sflag[STAGES * NS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int stream = wv / kWavesPerStream;   // tiles stream, stream + NS, stream + 2 NS, ...
+  const int wq = wv % kWavesPerStream;       // query rows 32 wq .., tile rows 8 wq ..
   const int l16 = lane & 15;
   const int lg = lane >> 4;              // lane group 0..3
   const int hk = blockIdx.y;
@@ -167,10 +191,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefix_kernel(const PrefixParams 
   const int tr_row = (lane & 15) >> 2;
   const int tr_piece = lane & 3;
 
-  // Loader role.  Wave wv loads tile rows 8wv .. 8wv+7 of K and of V as two 4-row groups
-  // (rows 8wv + 4g .., one page each since pages hold a multiple of 4 slots).  D = 128: one
-  // 1 KB instruction per group, lane l -> row 8wv + 4g + l/16, LDS chunk l%16.  D = 64: one
-  // 1 KB instruction covers both groups as two exec-masked halves, lane l -> row 8wv + l/8,
+  // Loader role.  Wave wq of a stream loads tile rows 8wq .. 8wq+7 of K and of V as two 4-row
+  // groups (rows 8wq + 4g .., one page each since pages hold a multiple of 4 slots).  D = 128:
+  // one 1 KB instruction per group, lane l -> row 8wq + 4g + l/16, LDS chunk l%16.  D = 64: one
+  // 1 KB instruction covers both groups as two exec-masked halves, lane l -> row 8wq + l/8,
   // LDS chunk l%8.  Each lane fetches logical chunk (LDS chunk) ^ swz(row); voff is its byte
   // offset from its group's first row in the page.
   constexpr int NI = D == 128 ? 2 : 1;   // instructions per operand per tile
@@ -178,9 +202,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefix_kernel(const PrefixParams 
   int lrow[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    lrow[i] = 8 * wv + (D == 128 ? 4 * i + lane / 16 : lane / 8);
+    lrow[i] = 8 * wq + (D == 128 ? 4 * i + lane / 16 : lane / 8);
     const int cg = (lane % CPR) ^ swz<D>(lrow[i]);
-    voff[i] = ((lrow[i] - 8 * wv) & 3) * row_stride + hk * RB + cg * 16;
+    voff[i] = ((lrow[i] - 8 * wq) & 3) * row_stride + hk * RB + cg * 16;
   }
 
   const int it_begin = scalar_load(p.indptr + blockIdx.x);
@@ -197,28 +221,29 @@ __global__ __launch_bounds__(kThreads, 2) void prefix_kernel(const PrefixParams 
     const int t0 = (kb / kTK) * kTK;
     // A group without pages holds no tokens (its kv_len is then a caller error).
     const int ntiles = (ke > kb && npages_grp > 0) ? (ke - t0 + kTK - 1) / kTK : 0;
+    const int nsteps = (ntiles + NS - 1) / NS;   // tiles per stream, rounded up
     const int last_page = max(npages_grp - 1, 0);
-    const bool wave_active = wv * kRowsPerWave < nrows;
+    const bool wave_active = wq * kRowsPerWave < nrows;
 
     // Page-list entries of this wave's two row groups in tile tt (scalar loads, clamped into
     // the list; a group past the list is rejected when the tile is issued).  They are fetched
     // one step before use, so their latency hides behind a tile's arithmetic.
     struct Pg { int e0, e1; };
     auto fetch = [&](int tt) -> Pg {
-      const int rb = t0 + tt * kTK + 8 * wv;
+      const int rb = t0 + tt * kTK + 8 * wq;
       Pg r;
       r.e0 = scalar_load(pages + min(rb >> shift, last_page));
       r.e1 = scalar_load(pages + min((rb + 4) >> shift, last_page));
       return r;
     };
 
-    // Loads of tile tt into stage (sk, sv) and the stage's valid-row byte of this wave; a tile
-    // past the end reads nothing (zeros) and marks no row valid.
-    auto issue = [&](int tt, const Pg& pg, char* sk, char* sv, uint32_t* flag) {
-      const int rb = t0 + tt * kTK + 8 * wv;      // token of the wave's first row
+    // Loads of tile tt into slot `dst` and the slot's valid-row byte of this wave; a tile past
+    // the end reads nothing (zeros) and marks no row valid.
+    auto issue = [&](int tt, const Pg& pg, char* dst, uint32_t* flag) {
+      const int rb = t0 + tt * kTK + 8 * wq;      // token of the wave's first row
       const bool in_tiles = tt < ntiles;
       const int e[2] = {pg.e0, pg.e1};
-      rsrc_t rk[2], rw[2];
+      u4_t rk[2], rw[2];
       int32_t soff[2];
       bool ok[2];
 #pragma unroll
@@ -226,16 +251,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefix_kernel(const PrefixParams 
         const int tg = rb + 4 * g;
         ok[g] = in_tiles & ((tg >> shift) < npages_grp) & (e[g] >= 0) & (e[g] < npool);
         const int64_t pofs = ok[g] ? (int64_t)e[g] * page_bytes : 0;
-        rk[g] = make_rsrc(kg + pofs, ok[g] ? page_bytes : 0);
-        rw[g] = make_rsrc(vg + pofs, ok[g] ? page_bytes : 0);
+        rk[g] = dma_rsrc(kg + pofs, ok[g] ? page_bytes : 0);
+        rw[g] = dma_rsrc(vg + pofs, ok[g] ? page_bytes : 0);
         soff[g] = (tg & (P - 1)) * row_stride;
       }
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const int t = t0 + tt * kTK + lrow[i];
-        const int32_t off = (t >= kb) & (t < ke) ? voff[i] : kOffsetNone;
-        char* dk = sk + (8 * wv + 4 * i) * RB;
-        char* dv = sv + (8 * wv + 4 * i) * RB;
+        const int32_t off = ((t >= kb) & (t < ke)) ? voff[i] : kOffsetNone;
+        char* dk = dst + (8 * wq + 4 * i) * RB;
+        char* dv = dk + STB;
         if constexpr (D == 128) {
           load_lds16(rk[i], dk, off, soff[i]);
           load_lds16(rw[i], dv, off, soff[i]);
@@ -255,10 +280,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefix_kernel(const PrefixParams 
       const int lo = min(max(kb - rb, 0), 8), hi = min(max(ke - rb, 0), 8);
       uint32_t bits = hi > lo ? (((1u << hi) - 1u) & ~((1u << lo) - 1u)) : 0u;
       bits &= (ok[0] ? 0x0Fu : 0u) | (ok[1] ? 0xF0u : 0u);
-      reinterpret_cast<uint8_t*>(flag)[wv] = (uint8_t)bits;
+      reinterpret_cast<uint8_t*>(flag)[wq] = (uint8_t)bits;
     };
 
-    V16 qb[2][KS];   // Q^T operands: query row wv*32 + nt*16 + l16, head_dim ks*32 + 8*lg .. +8
+    V16 qb[2][KS];   // Q^T operands: query row wq*32 + nt*16 + l16, head_dim ks*32 + 8*lg .. +8
     f4_t oacc[DM][2];
 #pragma unroll
     for (int dm = 0; dm < DM; ++dm)
@@ -358,64 +383,123 @@ __global__ __launch_bounds__(kThreads, 2) void prefix_kernel(const PrefixParams 
     };
 
     if (ntiles > 0) {
-      // Q^T operands first, so that the ring's waits below also cover them.  Rows past the
-      // tile read the tile's first row: their columns are computed but never stored.
+      // Q^T operands first (rows past the tile read the tile's first row: their columns are
+      // computed but never stored).
+      u4_t qr[2][KS];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        const int r = wv * kRowsPerWave + nt * 16 + l16;
+        const int r = wq * kRowsPerWave + nt * 16 + l16;
         const int rr = r < nrows ? r : 0;
         const int64_t qoff = ((int64_t)(q0 + rr / G) * p.hq + hk * G + rr % G) * D;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-          qb[nt][ks] = load16(static_cast<const char*>(p.q) + (qoff + ks * 32 + 8 * lg) * ES);
+          qr[nt][ks] = load16_async(static_cast<const char*>(p.q) + (qoff + ks * 32 + 8 * lg) * ES);
       }
-      // Ring prologue: tiles 0..2 in flight; page entries of tile 3 requested.
-      Pg pg = fetch(0);
-      issue(0, pg, sk0, sv0, &sflag[0]);
-      pg = fetch(1);
-      issue(1, pg, sk1, sv1, &sflag[1]);
-      pg = fetch(2);
-      issue(2, pg, sk2, sv2, &sflag[2]);
-      pg = fetch(3);
+      // The stream's j-th tile (tile stream + j NS) lives in stage j % 4.  Prologue: its first
+      // three tiles in flight, page entries of the fourth requested.
+      char* const sring = ring + stream * STAGES * SLOT;
+      uint32_t* const sfl = sflag + stream * STAGES;
+      Pg pg = fetch(stream);
+#pragma unroll
+      for (int j = 0; j < STAGES - 1; ++j) {
+        issue(stream + j * NS, pg, sring + j * SLOT, sfl + j);
+        pg = fetch(stream + (j + 1) * NS);
+      }
+      // The Q loads precede the prologue's 3 * NDMA loads.
+      PKC_WAIT_VMCNT(3 * NDMA);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          ready(qr[nt][ks]);
+          qb[nt][ks] = V16{{qr[nt][ks][0], qr[nt][ks][1], qr[nt][ks][2], qr[nt][ks][3]}};
+        }
 
-      // Step for tile tt in stage S: wait for this wave's loads of tile tt (tiles tt+1 and
-      // tt+2 stay in flight), barrier (every wave's loads of tt have landed and every wave is
-      // done reading stage S-1), refill stage S-1 with tile tt+3, request tile tt+4's page
-      // entries, compute tile tt.  No LDS wait is needed before the barrier: a wave's LDS
-      // operations complete in order, and the compiler waits for the last operand read of a
-      // tile before its final products, so by the end of a step the wave's valid-row byte is
-      // written and its reads of the stage are done.
-      auto step = [&](auto stage, int tt) {
-        constexpr int S = decltype(stage)::value;
-        constexpr int N = (S + 3) & 3;
-        char* const sk = S == 0 ? sk0 : S == 1 ? sk1 : S == 2 ? sk2 : sk3;
-        char* const sv = S == 0 ? sv0 : S == 1 ? sv1 : S == 2 ? sv2 : sv3;
-        char* const nk = N == 0 ? sk0 : N == 1 ? sk1 : N == 2 ? sk2 : sk3;
-        char* const nv = N == 0 ? sv0 : N == 1 ? sv1 : N == 2 ? sv2 : sv3;
+      // Step j in stage S = j % 4: wait for this wave's loads of the stream's j-th tile (its
+      // next two tiles stay in flight), barrier (every wave's loads and valid-row byte of the
+      // step's tiles have landed and every wave is done with step j-1), refill stage S-1 with
+      // the stream's tile j+3, request the page entries of its tile j+4, compute tile j.  No
+      // LDS wait is needed before the barrier: a wave's LDS operations complete in order, and
+      // the compiler waits for the last operand read of a tile before its final products, so
+      // by the end of a step the wave's valid-row byte is written and its reads of the stage
+      // are done.  Every stream runs the same number of steps (and barriers).  Stage numbers
+      // are compile-time constants (four steps per loop trip), so LDS addresses are immediate
+      // offsets.
+      auto step = [&](auto stage_c, int j) {
+        constexpr int S = decltype(stage_c)::value;
+        constexpr int N = (S + STAGES - 1) % STAGES;
+        const int tt = stream + j * NS;
         PKC_WAIT_VMCNT(2 * NDMA);
         ring_barrier();
-        const uint32_t mask = sflag[S];   // the same on every lane; first needed after S^T
-        issue(tt + 3, pg, nk, nv, &sflag[N]);
-        pg = fetch(tt + 4);
-        compute(sk, sv, mask);
+        const uint32_t mask = sfl[S];   // the same on every lane; first needed after S^T
+        issue(tt + (STAGES - 1) * NS, pg, sring + N * SLOT, sfl + N);
+        pg = fetch(tt + STAGES * NS);
+        if (tt < ntiles) compute(sring + S * SLOT, sring + S * SLOT + STB, mask);
       };
-      for (int tt = 0; tt < ntiles; tt += 4) {
-        step(std::integral_constant<int, 0>(), tt);
-        if (tt + 1 >= ntiles) break;
-        step(std::integral_constant<int, 1>(), tt + 1);
-        if (tt + 2 >= ntiles) break;
-        step(std::integral_constant<int, 2>(), tt + 2);
-        if (tt + 3 >= ntiles) break;
-        step(std::integral_constant<int, 3>(), tt + 3);
+      for (int j = 0; j < nsteps; j += 4) {
+        step(std::integral_constant<int, 0>(), j);
+        if (j + 1 >= nsteps) break;
+        step(std::integral_constant<int, 1>(), j + 1);
+        if (j + 2 >= nsteps) break;
+        step(std::integral_constant<int, 2>(), j + 2);
+        if (j + 3 >= nsteps) break;
+        step(std::integral_constant<int, 3>(), j + 3);
       }
     }
 
-    // Finish: total sum over the 4 lane groups, normalise, write the fp32 state.
-    if (wave_active) {
+    // Every load of the ring (including the empty ones past the last tile, which still write
+    // zeros to their slot) has landed and every wave is done with the ring.
+    __builtin_amdgcn_s_waitcnt(0);
+    ring_barrier();
+
+    if constexpr (NS == 2) {
+      // Stream 1 hands its state to stream 0 through the idle ring: value f of lane l of wave
+      // wq goes to float f * 256 + 64 wq + l.  Waves wq of the two streams hold the same rows
+      // in the same lanes, so the merge is lane to lane.
+      constexpr int NV = DM * 2 * 4 + 4;          // oacc, m_run[2], l_run[2]
+      static_assert(NV * 256 * 4 <= STAGES * NS * SLOT, "merge payload fits the ring");
+      float* xf = reinterpret_cast<float*>(ring) + 64 * wq + lane;
+      if (ntiles > 0) {
+        if (stream == 1) {
+#pragma unroll
+          for (int dm = 0; dm < DM; ++dm)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) xf[((dm * 2 + nt) * 4 + i) * 256] = oacc[dm][nt][i];
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) {
+            xf[(DM * 8 + nt) * 256] = m_run[nt];
+            xf[(DM * 8 + 2 + nt) * 256] = l_run[nt];
+          }
+        }
+        ring_barrier();
+        if (stream == 0) {
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) {
+            const float m2 = xf[(DM * 8 + nt) * 256];
+            const float l2 = xf[(DM * 8 + 2 + nt) * 256];
+            const float mn = fmaxf(m_run[nt], m2);
+            const float mu = (mn == kNegInf) ? 0.f : mn;
+            const float a1 = fast_exp2(m_run[nt] - mu), a2 = fast_exp2(m2 - mu);
+            m_run[nt] = mn;
+            l_run[nt] = l_run[nt] * a1 + l2 * a2;
+#pragma unroll
+            for (int dm = 0; dm < DM; ++dm)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                oacc[dm][nt][i] = oacc[dm][nt][i] * a1 + xf[((dm * 2 + nt) * 4 + i) * 256] * a2;
+          }
+        }
+      }
+    }
+
+    // Finish (stream 0): total sum over the 4 lane groups, normalise, write the fp32 state.
+    if (stream == 0 && wave_active) {
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         const float lt = lane_groups_sum(l_run[nt]);
-        const int r = wv * kRowsPerWave + nt * 16 + l16;
+        const int r = wq * kRowsPerWave + nt * 16 + l16;
         if (r < nrows) {
           const float inv = lt > 0.f ? 1.f / lt : 0.f;
           const int64_t srow_q = (int64_t)srow + r / G;
@@ -431,47 +515,51 @@ __global__ __launch_bounds__(kThreads, 2) void prefix_kernel(const PrefixParams 
         }
       }
     }
-    // Every load (including the empty ones past the last tile) and store of this item is done
-    // and every wave has left the ring before the next item refills it.
+    // The merge reads of the ring and this item's stores are done and every wave has left the
+    // ring before the next item refills it.
     __builtin_amdgcn_s_waitcnt(0);
     ring_barrier();
   }
 }
 
 template <typename T, int D, int G>
-static hipError_t launch_prefix_t(const PrefixParams& p, int grid_x, hipStream_t s) {
-  dim3 grid(grid_x, p.hkv), block(kThreads);
-  hipLaunchKernelGGL((prefix_kernel<T, D, G>), grid, block, 0, s, p);
+static hipError_t launch_prefix_t(int streams, const PrefixParams& p, int grid_x, hipStream_t s) {
+  const dim3 grid(grid_x, p.hkv);
+  if (streams == 2)
+    hipLaunchKernelGGL((prefix_kernel<T, D, G, 2>), grid, dim3(128 * kWavesPerStream), 0, s, p);
+  else
+    hipLaunchKernelGGL((prefix_kernel<T, D, G, 1>), grid, dim3(64 * kWavesPerStream), 0, s, p);
   return hipGetLastError();
 }
 
 template <typename T, int D>
-static hipError_t launch_prefix_g(int group, const PrefixParams& p, int grid_x, hipStream_t s) {
+static hipError_t launch_prefix_g(int group, int streams, const PrefixParams& p, int grid_x,
+                                  hipStream_t s) {
   switch (group) {
-    case 1: return launch_prefix_t<T, D, 1>(p, grid_x, s);
-    case 2: return launch_prefix_t<T, D, 2>(p, grid_x, s);
-    case 4: return launch_prefix_t<T, D, 4>(p, grid_x, s);
-    case 8: return launch_prefix_t<T, D, 8>(p, grid_x, s);
+    case 1: return launch_prefix_t<T, D, 1>(streams, p, grid_x, s);
+    case 2: return launch_prefix_t<T, D, 2>(streams, p, grid_x, s);
+    case 4: return launch_prefix_t<T, D, 4>(streams, p, grid_x, s);
+    case 8: return launch_prefix_t<T, D, 8>(streams, p, grid_x, s);
   }
   return hipErrorInvalidValue;
 }
 
 template <typename T>
-static hipError_t launch_prefix_d(int head_dim, int group, const PrefixParams& p, int grid_x,
-                                  hipStream_t s) {
-  if (head_dim == 64) return launch_prefix_g<T, 64>(group, p, grid_x, s);
-  if (head_dim == 128) return launch_prefix_g<T, 128>(group, p, grid_x, s);
+static hipError_t launch_prefix_d(int head_dim, int group, int streams, const PrefixParams& p,
+                                  int grid_x, hipStream_t s) {
+  if (head_dim == 64) return launch_prefix_g<T, 64>(group, streams, p, grid_x, s);
+  if (head_dim == 128) return launch_prefix_g<T, 128>(group, streams, p, grid_x, s);
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_prefix(pkc_dtype dt, int head_dim, int group, int tile_q, const PrefixParams& p,
-                         int grid_x, hipStream_t s) {
+hipError_t launch_prefix(pkc_dtype dt, int head_dim, int group, int tile_q, int streams,
+                         const PrefixParams& p, int grid_x, hipStream_t s) {
   if (grid_x <= 0) return hipSuccess;
-  if (tile_q * group > 4 * kRowsPerWave) return hipErrorInvalidValue;
-  if (p.page_size < 4) return hipErrorInvalidValue;
+  if (tile_q * group > kWavesPerStream * kRowsPerWave) return hipErrorInvalidValue;
+  if (p.page_size < 4 || (streams != 1 && streams != 2)) return hipErrorInvalidValue;
   switch (dt) {
-    case PKC_F16: return launch_prefix_d<F16>(head_dim, group, p, grid_x, s);
-    case PKC_BF16: return launch_prefix_d<BF16>(head_dim, group, p, grid_x, s);
+    case PKC_F16: return launch_prefix_d<F16>(head_dim, group, streams, p, grid_x, s);
+    case PKC_BF16: return launch_prefix_d<BF16>(head_dim, group, streams, p, grid_x, s);
     default: break;
   }
   return hipErrorInvalidValue;
