@@ -303,6 +303,26 @@ pkc_status pkc_cascade_decode(const pkc_plan_info* plan, const void* q, const vo
                               size_t dev_bytes, void* stream);
 
 /*
+ * In-place KV append ("Paged attention" page, decode path: the cache is updated in place, and
+ * its worked example places each sequence's next token at logical block cache_seqlens[b] / P,
+ * slot cache_seqlens[b] % P of the sequence's block-table row).  For every request b, the new
+ * token's rows k_new[b] and v_new[b] ([B, Hkv, D] each, the dtype of the pools) are copied to
+ * row (block_table[b][cache_seqlens[b] / P], cache_seqlens[b] % P) of k_pool and v_pool
+ * ([num_pages, P, Hkv, D]), and new_seqlens[b] = cache_seqlens[b] + 1 (new_seqlens may be
+ * NULL, or alias cache_seqlens for an in-place update).  Decoding over new_seqlens then
+ * attends over the appended token as well.
+ * A target block outside the table row, unallocated (-1) or naming a page outside
+ * [0, num_pages) is a caller error: nothing is written for that request and new_seqlens[b]
+ * keeps the old length.  All pointers are device pointers owned by the caller; the work is
+ * enqueued on `stream`.  Returns PKC_ERR_INVALID_ARG / PKC_ERR_UNSUPPORTED on bad sizes.
+ */
+pkc_status pkc_append_kv(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                         int64_t num_pages, const int32_t* block_table, int32_t max_blocks,
+                         const int32_t* cache_seqlens, int32_t* new_seqlens, int32_t batch,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                         pkc_dtype dtype, void* stream);
+
+/*
  * Host-side check of block-table contents (host arrays): every block holding one of the
  * tokens [kv_start[b], cache_seqlens[b]) must name a page in [0, num_pages).  Returns
  * PKC_ERR_INVALID_ARG naming the first bad (request, block) otherwise.  Not on the hot path.

@@ -88,3 +88,31 @@ def referenced_pages(block_table, cache_seqlens, page_size, kv_start=None):
         pages, _ = token_pages(row, start, int(cache_seqlens[b]), page_size)
         used.update(int(p) for p in pages)
     return used
+
+
+def append_targets(block_table, cache_seqlens, page_size):
+    """Physical (page, slot) where each sequence's next token is written, or None when the
+    logical block cache_seqlens[b] // P is outside the row or not allocated ("Paged attention"
+    page, decode path: the cache is updated in place; the worked example's next-token
+    bullets)."""
+    out = []
+    for b, row in enumerate(block_table):
+        j, page, slot = next_token_slot(row, int(cache_seqlens[b]), page_size)
+        out.append((page, slot) if page >= 0 else None)
+    return out
+
+
+def append_kv(k_pool, v_pool, k_new, v_new, block_table, cache_seqlens, page_size):
+    """Copies of the pools ([pages, P, Hkv, D]) with request b's new rows k_new[b], v_new[b]
+    ([B, Hkv, D]) written at its next-token slot, and the new lengths (cache_seqlens[b] + 1,
+    or unchanged when the target block is not allocated: nothing is written then)."""
+    k = np.array(k_pool, copy=True)
+    v = np.array(v_pool, copy=True)
+    lens = [int(x) for x in cache_seqlens]
+    for b, tgt in enumerate(append_targets(block_table, cache_seqlens, page_size)):
+        if tgt is None or tgt[0] >= k.shape[0]:
+            continue
+        k[tgt[0], tgt[1]] = k_new[b]
+        v[tgt[0], tgt[1]] = v_new[b]
+        lens[b] += 1
+    return k, v, lens

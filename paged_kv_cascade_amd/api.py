@@ -117,6 +117,7 @@ SIGNATURES = {
     "pkc_timing_reset": (_I32, []),
     "pkc_timing_read": (_I32, [_I32, ctypes.POINTER(_I64), ctypes.POINTER(ctypes.c_double)]),
     "pkc_read_stream_probe": (_I32, [_P, _I64, _P, _I64, _P]),
+    "pkc_append_kv": (_I32, [_P, _P, _P, _P, _I64, _P, _I32, _P, _P, _I32, _I32, _I32, _I32, _I32, _P]),
 }
 
 
@@ -285,6 +286,27 @@ def batch_decode_paged(q, k_pool, v_pool, block_table, cache_seqlens, kv_start=N
                                       B, Hq, Hkv, D, P, dtype_code(q.dtype), scale, _ptr(out),
                                       _ptr(lse), ws, wsn, _stream(dev)))
     return out, lse
+
+
+def append_kv(k_new, v_new, k_pool, v_pool, block_table, cache_seqlens, new_seqlens=None):
+    """pkc_append_kv: write each request's new token rows (k_new / v_new [B, Hkv, D]) at
+    position cache_seqlens[b] of its block-table row, in place.  Returns the new lengths
+    (new_seqlens, allocated when None; pass cache_seqlens itself to update it in place)."""
+    B, Hkv, D = k_new.shape
+    N, P, Hkv2, D2 = k_pool.shape
+    dev = k_pool.device
+    if (Hkv, D) != (Hkv2, D2) or tuple(v_new.shape) != tuple(k_new.shape) or tuple(v_pool.shape) != tuple(k_pool.shape):
+        raise PkcError(1, "append_kv: shape mismatch")
+    for t, n in ((k_new, "k_new"), (v_new, "v_new"), (k_pool, "k_pool"), (v_pool, "v_pool")):
+        _need(t, n, k_pool.dtype, dev)
+    _need(block_table, "block_table", torch.int32, dev)
+    _need(cache_seqlens, "cache_seqlens", torch.int32, dev)
+    if new_seqlens is None:
+        new_seqlens = torch.empty_like(cache_seqlens)
+    _check(lib.pkc_append_kv(_ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), N, _ptr(block_table),
+                             block_table.shape[1], _ptr(cache_seqlens), _ptr(new_seqlens), B, Hkv, D, P,
+                             dtype_code(k_pool.dtype), _stream(dev)))
+    return new_seqlens
 
 
 def level_dev(level: dict, device="cuda"):

@@ -80,6 +80,22 @@ struct MergeGenericParams {
   float* lse_out;
 };
 
+// In-place KV append: request b's new K and V rows (row_bytes = Hkv * D * esize each, at
+// k_new + b * row_bytes) go to slot seqlens[b] % P of page block_table[b][seqlens[b] / P].
+struct AppendParams {
+  const void* k_new;
+  const void* v_new;
+  void* k_pool;
+  void* v_pool;
+  int64_t num_pages;
+  const int32_t* block_table;
+  int32_t max_blocks;
+  int32_t page_shift;
+  const int32_t* seqlens;
+  int32_t* seqlens_out;      // nullable; may alias seqlens
+  int64_t row_bytes;         // multiple of 16
+};
+
 hipError_t launch_decode(pkc_dtype dt, int head_dim, int group, int waves, const DecodeParams& p,
                          int grid_x, hipStream_t s);
 // streams: 1 = 4-wave workgroups (two per compute unit), 2 = 8-wave workgroups whose two
@@ -95,6 +111,7 @@ hipError_t launch_merge_inplace(pkc_dtype dt, int head_dim, void* o_a, float* ls
                                 hipStream_t s);
 // Copies `bytes` (a multiple of 16, 16-byte aligned) from pinned host memory to the device.
 hipError_t launch_plan_upload(const void* host_src, void* dev_dst, int64_t bytes, hipStream_t s);
+hipError_t launch_append_kv(const AppendParams& p, int32_t batch, hipStream_t s);
 // Reads `mib` MiB of src (16-byte aligned) once as a nontemporal stream; sink gets mib * 256
 // uint32 values.
 hipError_t launch_read_stream(const void* src, int64_t mib, uint32_t* sink, hipStream_t s);

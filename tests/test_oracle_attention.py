@@ -284,6 +284,44 @@ def test_block_table_example_next_token():
         assert (page >= 0) == exp["fits_in_allocated"]
 
 
+def test_append_writes_the_example_next_token_slots():
+    """In-place append on the worked example: each sequence's new row lands at the printed
+    next-token (page, slot), nothing else changes, lengths grow by one; afterwards the token
+    is read (q = 0 and V = row id: O is the mean row id of the first length+1 tokens)."""
+    g = _golden("hf_paged_decode_example.json")
+    P = g["page_size"]
+    k_pool = np.random.default_rng(2).normal(size=(8, P, 1, 4))
+    v_pool = np.arange(8 * P, dtype=np.float64).reshape(8, P, 1, 1).repeat(4, axis=3)
+    k_new = np.full((3, 1, 4), 7.0)
+    v_new = np.full((3, 1, 4), -1000.0) - np.arange(3).reshape(3, 1, 1)
+    tg = indexing.append_targets(g["block_table"], g["cache_seqlens"], P)
+    assert tg == [(e["page"], e["slot"]) for e in g["next_token"]]
+    k2, v2, lens = indexing.append_kv(k_pool, v_pool, k_new, v_new, g["block_table"], g["cache_seqlens"], P)
+    assert lens == [n + 1 for n in g["cache_seqlens"]]
+    changed = np.argwhere(np.any(v2 != v_pool, axis=(2, 3)))
+    assert sorted(map(tuple, changed.tolist())) == sorted((e["page"], e["slot"]) for e in g["next_token"])
+    assert np.array_equal(np.delete(k2.reshape(8 * P, -1), [e["page"] * P + e["slot"] for e in g["next_token"]], 0),
+                          np.delete(k_pool.reshape(8 * P, -1), [e["page"] * P + e["slot"] for e in g["next_token"]], 0))
+    q = np.zeros((3, 1, 4))
+    O, L = attention.batch_decode(q, k2, v2, g["block_table"], lens, P, 1.0)
+    for b in range(3):
+        pages, slots = indexing.token_pages(g["block_table"][b], 0, lens[b], P)
+        ids = (pages * P + slots).astype(np.float64)
+        ids[-1] = -1000.0 - b            # the appended row's value
+        assert abs(L[b, 0] - math.log(lens[b])) < 1e-12
+        assert np.allclose(O[b, 0], ids.mean(), rtol=0, atol=1e-9)
+
+
+def test_append_to_unallocated_block_writes_nothing():
+    P = 4
+    bt = [[3, -1], [1, 2]]
+    k = np.zeros((4, P, 1, 2))
+    k2, v2, lens = indexing.append_kv(k, k, np.ones((2, 1, 2)), np.ones((2, 1, 2)), bt, [4, 8], P)
+    # request 0's next token needs block 1 (-1); request 1's needs block 2 (outside its row)
+    assert lens == [4, 8] and not k2.any()
+    assert indexing.append_targets(bt, [4, 8], P) == [None, None]
+
+
 def test_unallocated_block_inside_length_raises():
     g = _golden("hf_paged_decode_example.json")
     with pytest.raises(ValueError):
