@@ -115,6 +115,11 @@ typedef struct pkc_plan_params {
   int32_t enable_split; /* 0 -> L_kv = longest KV length (one chunk per tile, no split-KV) */
   int64_t alpha;        /* cost per query row (>= 0) */
   int64_t beta;         /* cost per KV token (>= 0) */
+  int32_t decode_waves; /* waves per decode workgroup: 0 -> chosen from the plan's average item
+                           length (4 from 256 tokens, 2 from 64, else 1); 1, 2 or 4 fix it.  A
+                           run captured in a HIP graph replays the launches it was captured
+                           with, so plans replayed under one graph need a fixed value (and no
+                           merge launch: enable_split = 0 in a cascade) */
 } pkc_plan_params;
 
 /* Host description of one cascade level: groups of consecutive requests sharing a KV run.

@@ -42,7 +42,7 @@ class PlanParams(ctypes.Structure):
                 ("page_size", ctypes.c_int32), ("num_ctas", ctypes.c_int32),
                 ("level_ctas", ctypes.c_int32), ("level_tile_q", ctypes.c_int32),
                 ("chunk_align", ctypes.c_int32), ("enable_split", ctypes.c_int32),
-                ("alpha", ctypes.c_int64), ("beta", ctypes.c_int64)]
+                ("alpha", ctypes.c_int64), ("beta", ctypes.c_int64), ("decode_waves", ctypes.c_int32)]
 
 
 class LevelHost(ctypes.Structure):
@@ -185,9 +185,10 @@ def device_info(device: int = 0):
 
 
 def make_params(batch, num_qo_heads, num_kv_heads, head_dim, page_size, num_ctas=0, level_ctas=0,
-                level_tile_q=0, chunk_align=1, enable_split=True, alpha=1, beta=1) -> PlanParams:
+                level_tile_q=0, chunk_align=1, enable_split=True, alpha=1, beta=1,
+                decode_waves=0) -> PlanParams:
     return PlanParams(batch, num_qo_heads, num_kv_heads, head_dim, page_size, num_ctas, level_ctas,
-                      level_tile_q, chunk_align, 1 if enable_split else 0, alpha, beta)
+                      level_tile_q, chunk_align, 1 if enable_split else 0, alpha, beta, decode_waves)
 
 
 class _Levels:

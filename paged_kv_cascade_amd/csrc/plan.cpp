@@ -121,6 +121,8 @@ pkc_status check_params(const pkc_plan_params* params, bool need_ctas, Resolved*
     return fail(PKC_ERR_UNSUPPORTED, "page_size must be a power of two in [1, 1024]");
   if (p.alpha < 0 || p.beta < 0) return fail(PKC_ERR_INVALID_ARG, "alpha and beta must be >= 0");
   if (p.chunk_align < 0) return fail(PKC_ERR_INVALID_ARG, "chunk_align must be >= 0");
+  if (!(p.decode_waves == 0 || p.decode_waves == 1 || p.decode_waves == 2 || p.decode_waves == 4))
+    return fail(PKC_ERR_INVALID_ARG, "decode_waves must be 0, 1, 2 or 4");
   if (p.num_ctas < 0 || p.level_ctas < 0 || p.level_tile_q < 0)
     return fail(PKC_ERR_INVALID_ARG, "num_ctas, level_ctas, level_tile_q must be >= 0");
   if (need_ctas && (p.num_ctas == 0 || p.level_ctas == 0))
@@ -285,7 +287,7 @@ pkc_status build_plan_host(const Resolved& r, const int32_t* kv_lens_h,
     int64_t tokens = 0;
     for (const Item& it : dec.items) tokens += it.ke - it.kb;
     const int64_t avg = dec.items.empty() ? 0 : tokens / (int64_t)dec.items.size();
-    P.dec_waves = avg >= 256 ? 4 : (avg >= 64 ? 2 : 1);
+    P.dec_waves = p.decode_waves ? p.decode_waves : (avg >= 256 ? 4 : (avg >= 64 ? 2 : 1));
   }
   P.dec_slots = slots;
   P.dec_kv_chunk = dec.kv_chunk;
