@@ -308,6 +308,25 @@ pkc_status pkc_cascade_decode(const pkc_plan_info* plan, const void* q, const vo
                               size_t dev_bytes, void* stream);
 
 /*
+ * Paged batch decode over FP8 K/V pools (the FlashInfer paper summary, appendix F: KV in fp8
+ * with fp16 queries and outputs).  The pools hold OCP FP8 E4M3 codes, one byte per element,
+ * same layout [num_pages, P, Hkv, D]; element value = decoded code * k_scale (K) or * v_scale
+ * (V), the scales being per-pool floats (> 0).  q is [B, Hq, D] of q_dtype (PKC_F16 or
+ * PKC_BF16) and o is written in q_dtype; LSE and partial states are fp32 as in
+ * pkc_batch_decode_paged, whose other arguments and rules this call shares (plan == NULL or a
+ * plan without levels).
+ */
+pkc_status pkc_batch_decode_paged_fp8(const pkc_plan_info* plan, const void* q, const void* k_pool,
+                                      const void* v_pool, float k_scale, float v_scale,
+                                      int64_t num_pages, const int32_t* block_table,
+                                      int32_t max_blocks, const int32_t* cache_seqlens,
+                                      const int32_t* kv_start, int32_t batch,
+                                      int32_t num_qo_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t page_size, pkc_dtype q_dtype,
+                                      float sm_scale, void* o, float* lse, void* dev_ws,
+                                      size_t dev_bytes, void* stream);
+
+/*
  * In-place KV append ("Paged attention" page, decode path: the cache is updated in place, and
  * its worked example places each sequence's next token at logical block cache_seqlens[b] / P,
  * slot cache_seqlens[b] % P of the sequence's block-table row).  For every request b, the new

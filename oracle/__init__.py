@@ -33,10 +33,12 @@ Modules:
 * ``merge``     -- the merge operator, used only to check the GPU merge and
   for the algebraic pins.
 * ``plan``      -- the CPU load-balancing plan, step by step.
+* ``fp8``       -- OCP E4M3 decoding of FP8 KV pools and the decode over the
+  dequantised pools (paper summary, appendix F).
 
 Every function here has at least one pin in ``tests/test_oracle_*.py``
 against something other than itself (closed forms, worked examples printed
 on the pages, a textbook routine, brute force).
 """
 
-from . import indexing, attention, merge, plan  # noqa: F401
+from . import indexing, attention, merge, plan, fp8  # noqa: F401

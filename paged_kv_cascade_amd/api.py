@@ -118,6 +118,9 @@ SIGNATURES = {
     "pkc_timing_read": (_I32, [_I32, ctypes.POINTER(_I64), ctypes.POINTER(ctypes.c_double)]),
     "pkc_read_stream_probe": (_I32, [_P, _I64, _P, _I64, _P]),
     "pkc_append_kv": (_I32, [_P, _P, _P, _P, _I64, _P, _I32, _P, _P, _I32, _I32, _I32, _I32, _I32, _P]),
+    "pkc_batch_decode_paged_fp8": (_I32, [ctypes.POINTER(PlanInfo), _P, _P, _P, _F, _F, _I64, _P, _I32,
+                                          _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _F, _P, _P, _P,
+                                          _SZ, _P]),
 }
 
 
@@ -308,6 +311,42 @@ def append_kv(k_new, v_new, k_pool, v_pool, block_table, cache_seqlens, new_seql
                              block_table.shape[1], _ptr(cache_seqlens), _ptr(new_seqlens), B, Hkv, D, P,
                              dtype_code(k_pool.dtype), _stream(dev)))
     return new_seqlens
+
+
+def batch_decode_paged_fp8(q, k_pool, v_pool, block_table, cache_seqlens, k_scale=1.0, v_scale=1.0,
+                           kv_start=None, sm_scale=None, plan_info: Optional[PlanInfo] = None,
+                           out=None, lse=None):
+    """pkc_batch_decode_paged_fp8.  k_pool / v_pool: OCP FP8 E4M3 pools [N, P, Hkv, D]
+    (torch.float8_e4m3fn, or uint8 holding the codes); q fp16 / bf16 [B, Hq, D].  Returns
+    (o in q's dtype, lse fp32)."""
+    B, Hq, D = q.shape
+    N, P, Hkv, D2 = k_pool.shape
+    dev = q.device
+    if q.dtype not in (torch.float16, torch.bfloat16):
+        raise PkcError(1, "q must be fp16 or bf16")
+    for t, n in ((k_pool, "k_pool"), (v_pool, "v_pool")):
+        _need(t, n, None, dev)
+        if t.element_size() != 1:
+            raise PkcError(1, f"{n} must hold one-byte FP8 codes")
+    _need(q, "q", q.dtype, dev)
+    _need(block_table, "block_table", torch.int32, dev)
+    if cache_seqlens is not None:
+        _need(cache_seqlens, "cache_seqlens", torch.int32, dev)
+    if kv_start is not None:
+        _need(kv_start, "kv_start", torch.int32, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+    scale = 1.0 / math.sqrt(D) if sm_scale is None else float(sm_scale)
+    ws, wsn = _ws_of(plan_info)
+    _check(lib.pkc_batch_decode_paged_fp8(ctypes.byref(plan_info) if plan_info is not None else None,
+                                          _ptr(q), _ptr(k_pool), _ptr(v_pool), float(k_scale),
+                                          float(v_scale), N, _ptr(block_table), block_table.shape[1],
+                                          _ptr(cache_seqlens), _ptr(kv_start), B, Hq, Hkv, D, P,
+                                          dtype_code(q.dtype), scale, _ptr(out), _ptr(lse), ws, wsn,
+                                          _stream(dev)))
+    return out, lse
 
 
 def level_dev(level: dict, device="cuda"):

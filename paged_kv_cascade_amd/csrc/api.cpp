@@ -146,6 +146,7 @@ pkc::DecodeParams decode_params(const void* q, const void* k, const void* v, int
   p.page_size = page_size;
   p.page_shift = log2i(page_size);
   p.scale_log2 = sm_scale * 1.4426950408889634f;
+  p.v_scale = 1.0f;
   p.o = o;
   p.lse = lse;
   return p;
@@ -349,7 +350,8 @@ pkc_status pkc_plan(const pkc_plan_params* params, const int32_t* kv_lens_h,
   PKC_TRY_END("pkc_plan")
 }
 
-pkc_status pkc_batch_decode_paged(const pkc_plan_info* plan, const void* q, const void* k_pool,
+static pkc_status decode_impl(bool fp8, float k_scale, float v_scale,
+                              const pkc_plan_info* plan, const void* q, const void* k_pool,
                                   const void* v_pool, int64_t num_pages,
                                   const int32_t* block_table, int32_t max_blocks,
                                   const int32_t* cache_seqlens, const int32_t* kv_start,
@@ -357,9 +359,14 @@ pkc_status pkc_batch_decode_paged(const pkc_plan_info* plan, const void* q, cons
                                   int32_t head_dim, int32_t page_size, pkc_dtype dtype,
                                   float sm_scale, void* o, float* lse, void* dev_ws,
                                   size_t dev_bytes, void* stream) {
-  PKC_TRY_BEGIN
   pkc_status st = check_shapes(batch, num_qo_heads, num_kv_heads, head_dim, page_size, dtype, sm_scale);
   if (st != PKC_OK) return st;
+  if (fp8) {
+    if (dtype != PKC_F16 && dtype != PKC_BF16)
+      return fail(PKC_ERR_UNSUPPORTED, "FP8 pools take fp16 or bf16 queries");
+    if (!(k_scale > 0.f) || !std::isfinite(k_scale) || !(v_scale > 0.f) || !std::isfinite(v_scale))
+      return fail(PKC_ERR_INVALID_ARG, "k_scale and v_scale must be positive and finite");
+  }
   if (batch == 0) return PKC_OK;
   if (!q || !k_pool || !v_pool || !block_table || !o || !lse)
     return fail(PKC_ERR_INVALID_ARG, "NULL tensor pointer");
@@ -372,6 +379,10 @@ pkc_status pkc_batch_decode_paged(const pkc_plan_info* plan, const void* q, cons
   pkc::DecodeParams p = decode_params(q, k_pool, v_pool, num_pages, block_table, max_blocks,
                                       cache_seqlens, kv_start, num_qo_heads, num_kv_heads,
                                       page_size, sm_scale, o, lse);
+  if (fp8) {
+    p.scale_log2 *= k_scale;
+    p.v_scale = v_scale;
+  }
   const int g = num_qo_heads / num_kv_heads;
   int grid_x = batch;
   if (plan) {
@@ -385,7 +396,10 @@ pkc_status pkc_batch_decode_paged(const pkc_plan_info* plan, const void* q, cons
     grid_x = plan->num_ctas;
   }
   const int waves = plan ? plan->dec_waves : 4;
-  if ((st = timed(0, s, "decode kernel launch", [&] { return pkc::launch_decode(dtype, head_dim, g, waves, p, grid_x, s); })) != PKC_OK)
+  if ((st = timed(0, s, "decode kernel launch", [&] {
+         return fp8 ? pkc::launch_decode_fp8(dtype, head_dim, g, waves, p, grid_x, s)
+                    : pkc::launch_decode(dtype, head_dim, g, waves, p, grid_x, s);
+       })) != PKC_OK)
     return st;
   if (plan && plan->num_merge > 0) {
     pkc::MergePlanParams m = merge_params(plan, dev_ws, 0, 1, true, o, lse);
@@ -393,7 +407,39 @@ pkc_status pkc_batch_decode_paged(const pkc_plan_info* plan, const void* q, cons
       return st;
   }
   return PKC_OK;
+}
+
+pkc_status pkc_batch_decode_paged(const pkc_plan_info* plan, const void* q, const void* k_pool,
+                                  const void* v_pool, int64_t num_pages,
+                                  const int32_t* block_table, int32_t max_blocks,
+                                  const int32_t* cache_seqlens, const int32_t* kv_start,
+                                  int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t page_size, pkc_dtype dtype,
+                                  float sm_scale, void* o, float* lse, void* dev_ws,
+                                  size_t dev_bytes, void* stream) {
+  PKC_TRY_BEGIN
+  return decode_impl(false, 1.f, 1.f, plan, q, k_pool, v_pool, num_pages,
+                     block_table, max_blocks, cache_seqlens, kv_start, batch, num_qo_heads,
+                     num_kv_heads, head_dim, page_size, dtype, sm_scale, o, lse, dev_ws, dev_bytes,
+                     stream);
   PKC_TRY_END("pkc_batch_decode_paged")
+}
+
+pkc_status pkc_batch_decode_paged_fp8(const pkc_plan_info* plan, const void* q, const void* k_pool,
+                                      const void* v_pool, float k_scale, float v_scale,
+                                      int64_t num_pages, const int32_t* block_table,
+                                      int32_t max_blocks, const int32_t* cache_seqlens,
+                                      const int32_t* kv_start, int32_t batch,
+                                      int32_t num_qo_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t page_size, pkc_dtype q_dtype,
+                                      float sm_scale, void* o, float* lse, void* dev_ws,
+                                      size_t dev_bytes, void* stream) {
+  PKC_TRY_BEGIN
+  return decode_impl(true, k_scale, v_scale, plan, q, k_pool, v_pool,
+                     num_pages, block_table, max_blocks, cache_seqlens, kv_start, batch,
+                     num_qo_heads, num_kv_heads, head_dim, page_size, q_dtype, sm_scale, o, lse,
+                     dev_ws, dev_bytes, stream);
+  PKC_TRY_END("pkc_batch_decode_paged_fp8")
 }
 
 pkc_status pkc_prefix_attention(const pkc_plan_info* plan, int32_t level, const void* q,

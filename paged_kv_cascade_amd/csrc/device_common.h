@@ -155,6 +155,77 @@ __device__ __forceinline__ void unpack16(T, const V16& a, float* out) {
   }
 }
 
+// OCP FP8 E4M3 KV storage (one byte per element) with queries and outputs of the 16-bit type
+// TQ.  Every E4M3 value is exact in fp16, bf16 and fp32, so the kernels convert codes with the
+// gfx950 conversion instructions (scale 1) and apply the pool scales outside the inner loops:
+// the K scale multiplies sm_scale, the V scale multiplies the output accumulators.
+template <typename TQ> struct KV8 {};
+template <typename TQ> struct Elem<KV8<TQ>> { static constexpr int kBytes = 1; };
+
+template <typename T> struct IsKV8 { static constexpr bool value = false; };
+template <typename TQ> struct IsKV8<KV8<TQ>> { static constexpr bool value = true; };
+template <typename T> struct OutType { typedef T type; };
+template <typename TQ> struct OutType<KV8<TQ>> { typedef TQ type; };
+template <typename T> struct QBytes { static constexpr int kBytes = Elem<T>::kBytes; };
+template <typename TQ> struct QBytes<KV8<TQ>> { static constexpr int kBytes = 2; };
+
+// The q elements matching one lane's 16 bytes of K/V: 16 bytes of q for 16- and 32-bit pools,
+// 32 bytes (16 fp16 / bf16 values) for FP8 pools.
+template <typename T> struct QSlice { V16 v[1]; };
+template <typename TQ> struct QSlice<KV8<TQ>> { V16 v[2]; };
+template <typename T>
+__device__ __forceinline__ QSlice<T> load_qslice(const char* qrow, int col) {
+  QSlice<T> r;
+  if constexpr (IsKV8<T>::value) {
+    r.v[0] = load16(qrow + col * 32);
+    r.v[1] = load16(qrow + col * 32 + 16);
+  } else {
+    r.v[0] = load16(qrow + col * 16);
+  }
+  return r;
+}
+template <typename T>
+__device__ __forceinline__ float dot16(T t, const QSlice<T>& q, const V16& k) {
+  return dot16(t, q.v[0], k);
+}
+// Codes 4i .. 4i+3 sit in word i of the 16-byte slice (bytes in address order); the
+// conversion's word select picks codes (0, 1) or (2, 3) of a word.
+__device__ __forceinline__ float dot16(KV8<F16>, const QSlice<KV8<F16>>& q, const V16& k) {
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const h2_t lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(k.w[i], 1.0f, false);
+    const h2_t hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(k.w[i], 1.0f, true);
+    s = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, q.v[i >> 1].w[2 * (i & 1)]), lo, s, false);
+    s = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, q.v[i >> 1].w[2 * (i & 1) + 1]), hi, s, false);
+  }
+  return s;
+}
+__device__ __forceinline__ float dot16(KV8<BF16>, const QSlice<KV8<BF16>>& q, const V16& k) {
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const b2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(k.w[i], 1.0f, false);
+    const b2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(k.w[i], 1.0f, true);
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2_t, q.v[i >> 1].w[2 * (i & 1)]), lo, s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2_t, q.v[i >> 1].w[2 * (i & 1) + 1]), hi, s, false);
+  }
+  return s;
+}
+template <typename TQ>
+__device__ __forceinline__ void unpack16(KV8<TQ>, const V16& a, float* out) {
+  typedef float f2v __attribute__((ext_vector_type(2)));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f2v lo = __builtin_amdgcn_cvt_pk_f32_fp8(a.w[i], false);
+    const f2v hi = __builtin_amdgcn_cvt_pk_f32_fp8(a.w[i], true);
+    out[4 * i] = lo[0];
+    out[4 * i + 1] = lo[1];
+    out[4 * i + 2] = hi[0];
+    out[4 * i + 3] = hi[1];
+  }
+}
+
 // DPP lane permutations inside 16-lane rows.
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {

@@ -19,7 +19,8 @@ struct DecodeParams {
   const int32_t* seqlens;    // [B] (plan == nullptr only)
   const int32_t* kv_start;   // [B] or nullptr
   int32_t hq, hkv, page_size, page_shift;
-  float scale_log2;          // sm_scale * log2(e)
+  float scale_log2;          // sm_scale * log2(e) (times the K scale for FP8 pools)
+  float v_scale;             // V scale of FP8 pools (1 otherwise)
   void* o;                   // [B, Hq, D] dtype
   float* lse;                // [B, Hq]
   float* st_o;               // partial states [rows, Hq, D] fp32
@@ -98,6 +99,9 @@ struct AppendParams {
 
 hipError_t launch_decode(pkc_dtype dt, int head_dim, int group, int waves, const DecodeParams& p,
                          int grid_x, hipStream_t s);
+// OCP FP8 E4M3 pools; q_dt (fp16 or bf16) is the type of q and o.
+hipError_t launch_decode_fp8(pkc_dtype q_dt, int head_dim, int group, int waves,
+                             const DecodeParams& p, int grid_x, hipStream_t s);
 // streams: 1 = 4-wave workgroups (two per compute unit), 2 = 8-wave workgroups whose two
 // 4-wave halves take alternate tiles of an item and merge at its end (one per compute unit).
 hipError_t launch_prefix(pkc_dtype dt, int head_dim, int group, int tile_q, int streams,

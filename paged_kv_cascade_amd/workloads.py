@@ -293,3 +293,13 @@ def by_number(n, device="cpu", **kw):
     decode, 3 two-level cascade, 4 GQA split decode, 5 multi-level cascade)."""
     return {1: tiny_paged, 2: paged_decode, 3: cascade_two_level, 4: gqa_split,
             5: cascade_multi_level}[n](device=device, **kw)
+
+
+def fp8_e4m3_pool(pool, scale=1.0):
+    """FP8 E4M3 code pool of a float pool: torch's round-to-nearest-even cast of pool / scale
+    to float8_e4m3fn (poisoned NaN rows stay NaN codes).  Inputs only: the pool scale is the
+    number the decode is then given."""
+    x = pool.float()
+    if scale != 1.0:
+        x = x / scale
+    return x.to(torch.float8_e4m3fn)

@@ -82,3 +82,19 @@ def check_state(o, lse, o_ref, lse_ref, dtype, label="", rows=None):
 
 def scale_of(D):
     return 1.0 / math.sqrt(D)
+
+
+class CodeView:
+    """Lets the oracle gather rows of a device FP8 pool as raw bytes: pool[pages, slots, head]
+    returns the uint8 codes of only the requested rows (decoding is the oracle's job)."""
+
+    def __init__(self, t):
+        self.t = t.view(torch.uint8)
+        self.shape = tuple(t.shape)
+
+    def __getitem__(self, idx):
+        pages, slots, head = idx
+        dev = self.t.device
+        p = torch.as_tensor(np.asarray(pages), dtype=torch.long, device=dev)
+        s = torch.as_tensor(np.asarray(slots), dtype=torch.long, device=dev)
+        return self.t[p, s, int(head)].cpu().numpy()
