@@ -12,6 +12,12 @@ HBM before the timed region.  Printed: one JSON line with the achieved algorithm
 each launch on the launch stream), HBM traffic from rocprofv3 counters when profiles/ holds
 them for the current kernel sources, and the fp64 CPU oracle timed on a bounded sample.
 
+Also reported, outside the timed steps: the distribution of single-run device times (back to
+back, and with the last-level cache evicted before each run); the same step without the
+cascade (every request reads the shared prefix through its own full page list) with the
+largest output difference between the two; the in-place append of one token per request; and
+the LLaMA2-7B decode shape (64 x 4096 tokens) over fp16 pools and over FP8 E4M3 pools.
+
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 """
 
@@ -29,7 +35,8 @@ sys.path.insert(0, ROOT)
 METRIC = "KV bytes/s from HBM (% of peak) + decode steps/s, cascade 32K prefix, batch 128"
 PEAK_HBM_GBPS = 8000.0
 KERNEL_SOURCES = ["paged_kv_cascade_amd/csrc/prefix.hip", "paged_kv_cascade_amd/csrc/decode.hip",
-                  "paged_kv_cascade_amd/csrc/merge.hip", "paged_kv_cascade_amd/csrc/device_common.h"]
+                  "paged_kv_cascade_amd/csrc/decode_kernel.h", "paged_kv_cascade_amd/csrc/merge.hip",
+                  "paged_kv_cascade_amd/csrc/device_common.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "cascade32k_b128_hbm_traffic.json")
 
 
@@ -172,6 +179,125 @@ def run_cpu_baseline_child(n_req):
     return json.loads(r.stdout.strip().splitlines()[-1])
 
 
+def percentiles(xs):
+    import numpy as np
+    a = np.asarray(xs, dtype=np.float64)
+    return {"p10": round(float(np.percentile(a, 10)), 2), "p50": round(float(np.percentile(a, 50)), 2),
+            "p90": round(float(np.percentile(a, 90)), 2), "n": int(a.size)}
+
+
+def step_time_distribution(step, info, n, evict=None):
+    """Device time of n single cascade runs, each between its own pair of events on the launch
+    stream; with `evict`, a 512 MiB buffer is rewritten before each run, outside the pair, so
+    the run starts with none of its KV in the last-level cache."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in evs:
+        if evict is not None:
+            evict.add_(1)
+        a.record()
+        step.run(info)
+        b.record()
+    torch.cuda.synchronize()
+    return percentiles([1e3 * a.elapsed_time(b) for a, b in evs])
+
+
+def noncascade_comparison(api, w, step, info, runs=5):
+    """The same step without the cascade: every request attends over its own full page list
+    (the 2048 prefix pages then its 16 suffix pages, 33,024 tokens) through the batch decode
+    kernel, so each request reads the shared prefix itself.  Returns its time, its algorithmic
+    KV bytes, the cascade's speedup over it and the largest output difference between the two."""
+    import torch
+    pre = torch.tensor(w.levels[0]["kv_page_indices"], dtype=torch.int32, device="cuda")
+    bt = torch.cat([pre.unsqueeze(0).expand(w.batch, -1), w.block_table], dim=1).contiguous()
+    lens = (w.cache_seqlens + w.levels[0]["kv_lens"][0]).to(torch.int32)
+    out = torch.empty_like(w.q)
+    lse = torch.empty(w.batch, w.num_qo_heads, dtype=torch.float32, device="cuda")
+    api.batch_decode_paged(w.q, w.k_pool, w.v_pool, bt, lens, sm_scale=w.sm_scale, out=out, lse=lse)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(runs):
+        api.batch_decode_paged(w.q, w.k_pool, w.v_pool, bt, lens, sm_scale=w.sm_scale, out=out, lse=lse)
+    b.record()
+    step.run(info)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / runs
+    nbytes = int(lens.sum()) * w.num_kv_heads * w.head_dim * 2 * w.esize
+    d_o = float((out.float() - step.out.float()).abs().max())
+    d_l = float((lse - step.lse).abs().max())
+    return {"ms_per_step": round(ms, 4), "alg_kv_bytes_per_step": nbytes,
+            "alg_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1), "runs": runs,
+            "max_abs_diff_vs_cascade": {"o": d_o, "lse": d_l}}
+
+
+def fp8_decode_comparison(api, workloads, runs=10):
+    """Batch decode of the LLaMA2-7B decode shape (64 requests x 4096 tokens, 32 heads x 128,
+    page 16, fp16 queries) over fp16 pools and over the same pools quantised to FP8 E4M3:
+    KV kernel time and algorithmic KV bytes/s of each (HIP events around each launch)."""
+    import torch
+    w = workloads.paged_decode(batch=64, kv_len=4096, page_size=16, dtype=torch.float16, device="cuda")
+    k8 = workloads.fp8_e4m3_pool(w.k_pool, 0.25)
+    v8 = workloads.fp8_e4m3_pool(w.v_pool, 0.25)
+    out = torch.empty_like(w.q)
+    lse = torch.empty(w.batch, w.num_qo_heads, dtype=torch.float32, device="cuda")
+    tokens = int(w.cache_seqlens.sum())
+    res = {"workload": w.name}
+    for name, fn, es in (
+            ("fp16", lambda: api.batch_decode_paged(w.q, w.k_pool, w.v_pool, w.block_table, w.cache_seqlens,
+                                                    sm_scale=w.sm_scale, out=out, lse=lse), 2),
+            ("fp8_e4m3", lambda: api.batch_decode_paged_fp8(w.q, k8, v8, w.block_table, w.cache_seqlens,
+                                                            k_scale=0.25, v_scale=0.25, sm_scale=w.sm_scale,
+                                                            out=out, lse=lse), 1)):
+        fn()
+        torch.cuda.synchronize()
+        api.timing_reset()
+        api.timing_enable(True)
+        for _ in range(runs):
+            fn()
+        torch.cuda.synchronize()
+        n, ms = api.timing_read(api.KIND_DECODE)
+        api.timing_enable(False)
+        us = 1e3 * ms / max(1, n)
+        nbytes = tokens * w.num_kv_heads * w.head_dim * 2 * es
+        res[name] = {"avg_us": round(us, 1), "alg_bytes": nbytes, "achieved_GBps": round(nbytes / us / 1e3, 1),
+                     "frac_of_peak": round(nbytes / us / 1e3 / PEAK_HBM_GBPS, 4)}
+    res["speedup_fp8_over_fp16"] = round(res["fp16"]["avg_us"] / res["fp8_e4m3"]["avg_us"], 3)
+    del w, k8, v8
+    torch.cuda.empty_cache()
+    return res
+
+
+def append_timing(api, w, runs=50):
+    """Appending one new K/V token per request (the step before decode) for the cascade
+    workload's batch and head shape: 128 requests with 256 cached suffix tokens each and a
+    17th page already allocated, in pools of their own.  Device time per call."""
+    import torch
+    P, B = w.page_size, w.batch
+    npg = w.block_table.shape[1] + 1
+    shape = (B * npg, P, w.num_kv_heads, w.head_dim)
+    kp = torch.zeros(shape, dtype=w.dtype, device="cuda")
+    vp = torch.zeros_like(kp)
+    bt = torch.arange(B * npg, dtype=torch.int32, device="cuda").view(B, npg)
+    lens = w.cache_seqlens.clone()
+    new_lens = torch.empty_like(lens)
+    k_new = torch.ones(B, w.num_kv_heads, w.head_dim, dtype=w.dtype, device="cuda")
+    v_new = torch.ones_like(k_new)
+    api.append_kv(k_new, v_new, kp, vp, bt, lens, new_seqlens=new_lens)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(runs):
+        api.append_kv(k_new, v_new, kp, vp, bt, lens, new_seqlens=new_lens)
+    b.record()
+    torch.cuda.synchronize()
+    written = int((kp[:, 0] != 0).any(dim=-1).any(dim=-1).sum())
+    res = {"avg_us": round(1e3 * a.elapsed_time(b) / runs, 2), "tokens_per_call": B,
+           "bytes_written_per_call": 2 * B * w.num_kv_heads * w.head_dim * w.esize,
+           "pages_written": written}
+    del kp, vp
+    torch.cuda.empty_cache()
+    return res
+
+
 def load_traffic(src_hash):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or None when it is
     missing or was taken on other kernel sources."""
@@ -269,6 +395,16 @@ def main():
             "traffic": (traffic or {}).get(dom, {}).get("hbm_bytes_per_launch") if traffic else None,
             "alg_bytes_per_launch": kern[dom]["alg_bytes"], "avg_launch_us": kern[dom]["avg_us"]}
 
+    # Per-run device time distribution, back to back and with the last-level cache evicted.
+    dist_warm = step_time_distribution(step, info, args.steps)
+    evict = torch.zeros(512 << 20, dtype=torch.uint8, device="cuda")
+    dist_cold = step_time_distribution(step, info, min(args.steps, 50), evict)
+    del evict
+    nonc = noncascade_comparison(api, w, step, info)
+    nonc["cascade_speedup"] = round(nonc["ms_per_step"] / (dist_warm["p50"] * 1e-3), 2)
+    app = append_timing(api, w)
+    fp8 = fp8_decode_comparison(api, workloads)
+
     # The device's achievable read rate: one nontemporal 16-byte-load stream over 2 GiB.
     buf = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
     buf.fill_(1)
@@ -309,8 +445,12 @@ def main():
         "pct_of_read_stream_peak": round(100 * value / stream_gbps, 2),
         "ms_per_step_device_only": round(ms_dev, 4),
         "ms_plan_cpu": round(ms_plan, 4),
+        "device_us_per_run": {"back_to_back": dist_warm, "llc_evicted": dist_cold},
         "kernels": kern,
         "roofline": roof,
+        "noncascade_same_step": nonc,
+        "append_kv": app,
+        "fp8_kv_decode": fp8,
         "kernel_source_hash": src_hash,
     }
     line["cpu_baseline"] = cpu
