@@ -16,7 +16,8 @@ Also reported, outside the timed steps: the distribution of single-run device ti
 back, and with the last-level cache evicted before each run); the same step without the
 cascade (every request reads the shared prefix through its own full page list) with the
 largest output difference between the two; the in-place append of one token per request; and
-the LLaMA2-7B decode shape (64 x 4096 tokens) over fp16 pools and over FP8 E4M3 pools.
+the LLaMA2-7B decode shape (64 x 4096 tokens) over fp16 pools and over FP8 E4M3 pools; and
+the same cascade step over FP8 E4M3 pools.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 """
@@ -34,7 +35,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "KV bytes/s from HBM (% of peak) + decode steps/s, cascade 32K prefix, batch 128"
 PEAK_HBM_GBPS = 8000.0
-KERNEL_SOURCES = ["paged_kv_cascade_amd/csrc/prefix.hip", "paged_kv_cascade_amd/csrc/decode.hip",
+KERNEL_SOURCES = ["paged_kv_cascade_amd/csrc/prefix_kernel.h", "paged_kv_cascade_amd/csrc/decode.hip",
                   "paged_kv_cascade_amd/csrc/decode_kernel.h", "paged_kv_cascade_amd/csrc/merge.hip",
                   "paged_kv_cascade_amd/csrc/device_common.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "cascade32k_b128_hbm_traffic.json")
@@ -267,6 +268,47 @@ def fp8_decode_comparison(api, workloads, runs=10):
     return res
 
 
+def fp8_cascade_timing(api, workloads, w, step, info, runs=50):
+    """The same cascade step over the workload's pools quantised to FP8 E4M3 (k_scale = v_scale =
+    0.25, fp16 queries): device time per run with the step's plan, per-kernel times, and its
+    algorithmic KV bytes/s (one byte per element) -- against the fp16 run of the same plan."""
+    import torch
+    k8 = workloads.fp8_e4m3_pool(w.k_pool, 0.25)
+    v8 = workloads.fp8_e4m3_pool(w.v_pool, 0.25)
+    out = torch.empty_like(w.q)
+    lse = torch.empty(w.batch, w.num_qo_heads, dtype=torch.float32, device="cuda")
+
+    def run():
+        api.cascade_decode_fp8(info, w.q, k8, v8, step.devs, w.block_table, w.cache_seqlens, k_scale=0.25,
+                               v_scale=0.25, sm_scale=w.sm_scale, out=out, lse=lse)
+
+    for _ in range(10):
+        run()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(runs):
+        run()
+    b.record()
+    torch.cuda.synchronize()
+    us = 1e3 * a.elapsed_time(b) / runs
+    api.timing_reset()
+    api.timing_enable(True)
+    for _ in range(runs):
+        run()
+    torch.cuda.synchronize()
+    kern = {}
+    for kind, name in ((api.KIND_PREFIX, "prefix_mfma"), (api.KIND_DECODE, "suffix_decode")):
+        n, ms = api.timing_read(kind)
+        kern[name] = round(1e3 * ms / max(1, n), 2)
+    api.timing_enable(False)
+    nbytes = w.algorithmic_kv_bytes() // w.esize
+    del k8, v8
+    torch.cuda.empty_cache()
+    return {"us_per_run": round(us, 1), "alg_kv_bytes_per_step": nbytes,
+            "alg_GBps": round(nbytes / us / 1e3, 1), "kernel_avg_us": kern, "runs": runs}
+
+
 def append_timing(api, w, runs=50):
     """Appending one new K/V token per request (the step before decode) for the cascade
     workload's batch and head shape: 128 requests with 256 cached suffix tokens each and a
@@ -403,6 +445,7 @@ def main():
     nonc = noncascade_comparison(api, w, step, info)
     nonc["cascade_speedup"] = round(nonc["ms_per_step"] / (dist_warm["p50"] * 1e-3), 2)
     app = append_timing(api, w)
+    fp8c = fp8_cascade_timing(api, workloads, w, step, info)
     fp8 = fp8_decode_comparison(api, workloads)
 
     # The device's achievable read rate: one nontemporal 16-byte-load stream over 2 GiB.
@@ -451,6 +494,7 @@ def main():
         "noncascade_same_step": nonc,
         "append_kv": app,
         "fp8_kv_decode": fp8,
+        "fp8_kv_cascade": fp8c,
         "kernel_source_hash": src_hash,
     }
     line["cpu_baseline"] = cpu

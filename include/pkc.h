@@ -327,6 +327,39 @@ pkc_status pkc_batch_decode_paged_fp8(const pkc_plan_info* plan, const void* q, 
                                       size_t dev_bytes, void* stream);
 
 /*
+ * pkc_prefix_attention over FP8 K/V pools (paper summary, appendix F): the same call and rules
+ * with OCP FP8 E4M3 pools (one byte per element, [num_pages, P, Hkv, D]) whose element values
+ * are decoded code * k_scale (K) and * v_scale (V), per-pool floats > 0.  q_dtype (PKC_F16 or
+ * PKC_BF16) is the type of q and of the matrix-core operands (every E4M3 value is exact in
+ * both); o_state / lse_state are written as in pkc_prefix_attention.
+ */
+pkc_status pkc_prefix_attention_fp8(const pkc_plan_info* plan, int32_t level, const void* q,
+                                    const void* k_pool, const void* v_pool, float k_scale,
+                                    float v_scale, int64_t num_pages,
+                                    const pkc_level_dev* level_dev, int32_t batch,
+                                    int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t page_size, pkc_dtype q_dtype, float sm_scale,
+                                    void* o_state, pkc_dtype o_dtype, float* lse_state,
+                                    void* dev_ws, size_t dev_bytes, void* stream);
+
+/*
+ * pkc_cascade_decode over FP8 K/V pools (paper summary, appendix F, with the "Cascade
+ * Inference" blog's algorithm): every level and every request's own KV are read from OCP FP8
+ * E4M3 pools with per-pool scales k_scale and v_scale (> 0); q and o are q_dtype (PKC_F16 or
+ * PKC_BF16), LSE and partial states fp32.  Arguments and rules are those of
+ * pkc_cascade_decode.
+ */
+pkc_status pkc_cascade_decode_fp8(const pkc_plan_info* plan, const void* q, const void* k_pool,
+                                  const void* v_pool, float k_scale, float v_scale,
+                                  int64_t num_pages, const pkc_level_dev* levels,
+                                  int32_t num_levels, const int32_t* block_table,
+                                  int32_t max_blocks, const int32_t* suffix_seqlens,
+                                  int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t page_size, pkc_dtype q_dtype,
+                                  float sm_scale, void* o, float* lse, void* dev_ws,
+                                  size_t dev_bytes, void* stream);
+
+/*
  * In-place KV append ("Paged attention" page, decode path: the cache is updated in place, and
  * its worked example places each sequence's next token at logical block cache_seqlens[b] / P,
  * slot cache_seqlens[b] % P of the sequence's block-table row).  For every request b, the new

@@ -26,7 +26,7 @@ import math
 
 import numpy as np
 
-from .attention import batch_decode
+from .attention import batch_decode, cascade_decode, level_prefix_states
 
 BIAS = 7
 
@@ -75,3 +75,19 @@ def batch_decode_fp8(q, k_codes, v_codes, k_scale, v_scale, block_table, cache_s
     return batch_decode(q, DequantizedPool(k_codes, k_scale), DequantizedPool(v_codes, v_scale),
                         block_table, cache_seqlens, page_size, sm_scale, kv_start=kv_start,
                         requests=requests, heads=heads)
+
+
+def cascade_decode_fp8(q, k_codes, v_codes, k_scale, v_scale, page_size, sm_scale, levels,
+                       suffix_block_table, suffix_seqlens, requests=None, heads=None):
+    """Cascade decode over FP8 E4M3 pools: ``attention.cascade_decode`` (one softmax over each
+    request's level token sets and suffix) over the dequantised pools."""
+    return cascade_decode(q, DequantizedPool(k_codes, k_scale), DequantizedPool(v_codes, v_scale),
+                          page_size, sm_scale, levels, suffix_block_table, suffix_seqlens,
+                          requests=requests, heads=heads)
+
+
+def level_prefix_states_fp8(q, k_codes, v_codes, k_scale, v_scale, page_size, sm_scale, level,
+                            num_requests):
+    """``attention.level_prefix_states`` over the dequantised FP8 E4M3 pools."""
+    return level_prefix_states(q, DequantizedPool(k_codes, k_scale), DequantizedPool(v_codes, v_scale),
+                               page_size, sm_scale, level, num_requests)

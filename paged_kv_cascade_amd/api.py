@@ -121,6 +121,12 @@ SIGNATURES = {
     "pkc_batch_decode_paged_fp8": (_I32, [ctypes.POINTER(PlanInfo), _P, _P, _P, _F, _F, _I64, _P, _I32,
                                           _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _F, _P, _P, _P,
                                           _SZ, _P]),
+    "pkc_prefix_attention_fp8": (_I32, [ctypes.POINTER(PlanInfo), _I32, _P, _P, _P, _F, _F, _I64,
+                                        ctypes.POINTER(LevelDev), _I32, _I32, _I32, _I32, _I32, _I32,
+                                        _F, _P, _I32, _P, _P, _SZ, _P]),
+    "pkc_cascade_decode_fp8": (_I32, [ctypes.POINTER(PlanInfo), _P, _P, _P, _F, _F, _I64,
+                                      ctypes.POINTER(LevelDev), _I32, _P, _I32, _P, _I32, _I32, _I32,
+                                      _I32, _I32, _I32, _F, _P, _P, _P, _SZ, _P]),
 }
 
 
@@ -322,12 +328,7 @@ def batch_decode_paged_fp8(q, k_pool, v_pool, block_table, cache_seqlens, k_scal
     B, Hq, D = q.shape
     N, P, Hkv, D2 = k_pool.shape
     dev = q.device
-    if q.dtype not in (torch.float16, torch.bfloat16):
-        raise PkcError(1, "q must be fp16 or bf16")
-    for t, n in ((k_pool, "k_pool"), (v_pool, "v_pool")):
-        _need(t, n, None, dev)
-        if t.element_size() != 1:
-            raise PkcError(1, f"{n} must hold one-byte FP8 codes")
+    _check_fp8_pools(q, k_pool, v_pool)
     _need(q, "q", q.dtype, dev)
     _need(block_table, "block_table", torch.int32, dev)
     if cache_seqlens is not None:
@@ -426,6 +427,59 @@ def cascade_decode(plan_info: PlanInfo, q, k_pool, v_pool, lvl_devs: Sequence[Le
                                   arr, len(lvl_devs), _ptr(block_table), block_table.shape[1],
                                   _ptr(suffix_seqlens), B, Hq, Hkv, D, P, dtype_code(q.dtype), scale,
                                   _ptr(out), _ptr(lse), ws, wsn, _stream(dev)))
+    return out, lse
+
+
+def _check_fp8_pools(q, k_pool, v_pool):
+    if q.dtype not in (torch.float16, torch.bfloat16):
+        raise PkcError(1, "q must be fp16 or bf16")
+    for t, n in ((k_pool, "k_pool"), (v_pool, "v_pool")):
+        _need(t, n, None, q.device)
+        if t.element_size() != 1:
+            raise PkcError(1, f"{n} must hold one-byte FP8 codes")
+
+
+def prefix_attention_fp8(plan_info: PlanInfo, level: int, q, k_pool, v_pool, lvl_dev: LevelDev,
+                         k_scale=1.0, v_scale=1.0, sm_scale=None, o_dtype=torch.float32, out=None,
+                         lse=None):
+    """pkc_prefix_attention_fp8: prefix_attention over OCP FP8 E4M3 pools (float8_e4m3fn or
+    uint8 codes) with per-pool scales; q fp16 / bf16."""
+    B, Hq, D = q.shape
+    N, P, Hkv, _ = k_pool.shape
+    dev = q.device
+    _check_fp8_pools(q, k_pool, v_pool)
+    if out is None:
+        out = torch.empty(B, Hq, D, dtype=o_dtype, device=dev)
+    if lse is None:
+        lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+    scale = 1.0 / math.sqrt(D) if sm_scale is None else float(sm_scale)
+    ws, wsn = _ws_of(plan_info)
+    _check(lib.pkc_prefix_attention_fp8(ctypes.byref(plan_info), level, _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                        float(k_scale), float(v_scale), N, ctypes.byref(lvl_dev), B, Hq, Hkv,
+                                        D, P, dtype_code(q.dtype), scale, _ptr(out), dtype_code(out.dtype),
+                                        _ptr(lse), ws, wsn, _stream(dev)))
+    return out, lse
+
+
+def cascade_decode_fp8(plan_info: PlanInfo, q, k_pool, v_pool, lvl_devs: Sequence[LevelDev], block_table,
+                       suffix_seqlens, k_scale=1.0, v_scale=1.0, sm_scale=None, out=None, lse=None):
+    """pkc_cascade_decode_fp8: cascade_decode over OCP FP8 E4M3 pools with per-pool scales;
+    q and o fp16 / bf16."""
+    B, Hq, D = q.shape
+    N, P, Hkv, _ = k_pool.shape
+    dev = q.device
+    _check_fp8_pools(q, k_pool, v_pool)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+    scale = 1.0 / math.sqrt(D) if sm_scale is None else float(sm_scale)
+    arr = (LevelDev * max(1, len(lvl_devs)))(*lvl_devs)
+    ws, wsn = _ws_of(plan_info)
+    _check(lib.pkc_cascade_decode_fp8(ctypes.byref(plan_info), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                      float(k_scale), float(v_scale), N, arr, len(lvl_devs), _ptr(block_table),
+                                      block_table.shape[1], _ptr(suffix_seqlens), B, Hq, Hkv, D, P,
+                                      dtype_code(q.dtype), scale, _ptr(out), _ptr(lse), ws, wsn, _stream(dev)))
     return out, lse
 
 

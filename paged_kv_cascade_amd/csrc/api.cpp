@@ -170,9 +170,11 @@ pkc::MergePlanParams merge_params(const pkc_plan_info* plan, void* ws, int l0, i
   return m;
 }
 
+// FP8 pools (fp8 = true): k_scale folds into the softmax scale, v_scale into the state.
 pkc_status run_level(const pkc_plan_info* plan, int level, const void* q, const void* k, const void* v,
                      int64_t num_pages, const pkc_level_dev* lv, pkc_dtype dtype, float sm_scale,
-                     void* ws, hipStream_t s) {
+                     void* ws, hipStream_t s, bool fp8 = false, float k_scale = 1.f,
+                     float v_scale = 1.f) {
   if (plan->lvl_groups[level] > 0 && (!lv->kv_page_indptr || !lv->kv_page_indices))
     return fail(PKC_ERR_INVALID_ARG, "level " + std::to_string(level) + ": NULL page arrays");
   pkc::PrefixParams p{};
@@ -187,7 +189,8 @@ pkc_status run_level(const pkc_plan_info* plan, int level, const void* q, const 
   p.hkv = plan->num_kv_heads;
   p.page_size = plan->page_size;
   p.page_shift = log2i(plan->page_size);
-  p.scale_log2 = sm_scale * 1.4426950408889634f;
+  p.scale_log2 = sm_scale * 1.4426950408889634f * (fp8 ? k_scale : 1.f);
+  p.v_scale = fp8 ? v_scale : 1.f;
   p.st_o = at<float>(ws, plan->off_state_o);
   p.st_lse = at<float>(ws, plan->off_state_lse);
   p.indptr = at<int32_t>(ws, plan->off_lvl_indptr[level]);
@@ -205,8 +208,10 @@ pkc_status run_level(const pkc_plan_info* plan, int level, const void* q, const 
     if (v == 1 || v == 2) streams = v;
   }
   return timed(1, s, "prefix kernel launch", [&] {
-    return pkc::launch_prefix(dtype, plan->head_dim, g, plan->lvl_tile_q[level], streams, p,
-                              plan->level_ctas, s);
+    return fp8 ? pkc::launch_prefix_fp8(dtype, plan->head_dim, g, plan->lvl_tile_q[level], streams, p,
+                                        plan->level_ctas, s)
+               : pkc::launch_prefix(dtype, plan->head_dim, g, plan->lvl_tile_q[level], streams, p,
+                                    plan->level_ctas, s);
   });
 }
 
@@ -249,8 +254,16 @@ pkc_status resolve_params(const pkc_plan_params* params, pkc::Resolved* r) {
 
 pkc_status check_prefix_supported(pkc_dtype dtype, int32_t page_size) {
   if (dtype != PKC_F16 && dtype != PKC_BF16)
-    return fail(PKC_ERR_UNSUPPORTED, "the multi-query prefix kernel needs f16 or bf16");
+    return fail(PKC_ERR_UNSUPPORTED, "the multi-query prefix kernel needs f16 or bf16 queries");
   if (page_size < 4) return fail(PKC_ERR_UNSUPPORTED, "the multi-query prefix kernel needs page_size >= 4");
+  return PKC_OK;
+}
+
+pkc_status check_fp8(pkc_dtype q_dtype, float k_scale, float v_scale) {
+  if (q_dtype != PKC_F16 && q_dtype != PKC_BF16)
+    return fail(PKC_ERR_UNSUPPORTED, "FP8 pools take fp16 or bf16 queries");
+  if (!(k_scale > 0.f) || !std::isfinite(k_scale) || !(v_scale > 0.f) || !std::isfinite(v_scale))
+    return fail(PKC_ERR_INVALID_ARG, "k_scale and v_scale must be positive and finite");
   return PKC_OK;
 }
 
@@ -361,12 +374,7 @@ static pkc_status decode_impl(bool fp8, float k_scale, float v_scale,
                                   size_t dev_bytes, void* stream) {
   pkc_status st = check_shapes(batch, num_qo_heads, num_kv_heads, head_dim, page_size, dtype, sm_scale);
   if (st != PKC_OK) return st;
-  if (fp8) {
-    if (dtype != PKC_F16 && dtype != PKC_BF16)
-      return fail(PKC_ERR_UNSUPPORTED, "FP8 pools take fp16 or bf16 queries");
-    if (!(k_scale > 0.f) || !std::isfinite(k_scale) || !(v_scale > 0.f) || !std::isfinite(v_scale))
-      return fail(PKC_ERR_INVALID_ARG, "k_scale and v_scale must be positive and finite");
-  }
+  if (fp8 && (st = check_fp8(dtype, k_scale, v_scale)) != PKC_OK) return st;
   if (batch == 0) return PKC_OK;
   if (!q || !k_pool || !v_pool || !block_table || !o || !lse)
     return fail(PKC_ERR_INVALID_ARG, "NULL tensor pointer");
@@ -442,17 +450,17 @@ pkc_status pkc_batch_decode_paged_fp8(const pkc_plan_info* plan, const void* q, 
   PKC_TRY_END("pkc_batch_decode_paged_fp8")
 }
 
-pkc_status pkc_prefix_attention(const pkc_plan_info* plan, int32_t level, const void* q,
-                                const void* k_pool, const void* v_pool, int64_t num_pages,
-                                const pkc_level_dev* level_dev, int32_t batch,
-                                int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
-                                int32_t page_size, pkc_dtype dtype, float sm_scale,
-                                void* o_state, pkc_dtype o_dtype, float* lse_state,
-                                void* dev_ws, size_t dev_bytes, void* stream) {
-  PKC_TRY_BEGIN
+static pkc_status prefix_impl(bool fp8, float k_scale, float v_scale, const pkc_plan_info* plan,
+                              int32_t level, const void* q, const void* k_pool, const void* v_pool,
+                              int64_t num_pages, const pkc_level_dev* level_dev, int32_t batch,
+                              int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t page_size, pkc_dtype dtype, float sm_scale, void* o_state,
+                              pkc_dtype o_dtype, float* lse_state, void* dev_ws, size_t dev_bytes,
+                              void* stream) {
   pkc_status st = check_shapes(batch, num_qo_heads, num_kv_heads, head_dim, page_size, dtype, sm_scale);
   if (st != PKC_OK) return st;
   if ((st = check_prefix_supported(dtype, page_size)) != PKC_OK) return st;
+  if (fp8 && (st = check_fp8(dtype, k_scale, v_scale)) != PKC_OK) return st;
   if (!dtype_ok(o_dtype)) return fail(PKC_ERR_UNSUPPORTED, "unknown o_dtype");
   if (!plan || !level_dev) return fail(PKC_ERR_INVALID_ARG, "plan and level_dev are required");
   if ((st = check_plan(plan, batch, num_qo_heads, num_kv_heads, head_dim, page_size, dev_ws, dev_bytes)) != PKC_OK)
@@ -462,11 +470,40 @@ pkc_status pkc_prefix_attention(const pkc_plan_info* plan, int32_t level, const 
   if (!q || !k_pool || !v_pool || !o_state || !lse_state) return fail(PKC_ERR_INVALID_ARG, "NULL tensor pointer");
   if (num_pages < 1) return fail(PKC_ERR_INVALID_ARG, "num_pages must be >= 1 (masked lanes read row 0 of page 0)");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if ((st = run_level(plan, level, q, k_pool, v_pool, num_pages, level_dev, dtype, sm_scale, dev_ws, s)) != PKC_OK)
+  if ((st = run_level(plan, level, q, k_pool, v_pool, num_pages, level_dev, dtype, sm_scale, dev_ws, s,
+                      fp8, k_scale, v_scale)) != PKC_OK)
     return st;
   pkc::MergePlanParams m = merge_params(plan, dev_ws, level, level + 1, false, o_state, lse_state);
   return timed(2, s, "merge kernel launch", [&] { return pkc::launch_merge_plan(o_dtype, head_dim, m, s); });
+}
+
+pkc_status pkc_prefix_attention(const pkc_plan_info* plan, int32_t level, const void* q,
+                                const void* k_pool, const void* v_pool, int64_t num_pages,
+                                const pkc_level_dev* level_dev, int32_t batch,
+                                int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t page_size, pkc_dtype dtype, float sm_scale,
+                                void* o_state, pkc_dtype o_dtype, float* lse_state,
+                                void* dev_ws, size_t dev_bytes, void* stream) {
+  PKC_TRY_BEGIN
+  return prefix_impl(false, 1.f, 1.f, plan, level, q, k_pool, v_pool, num_pages, level_dev, batch,
+                     num_qo_heads, num_kv_heads, head_dim, page_size, dtype, sm_scale, o_state,
+                     o_dtype, lse_state, dev_ws, dev_bytes, stream);
   PKC_TRY_END("pkc_prefix_attention")
+}
+
+pkc_status pkc_prefix_attention_fp8(const pkc_plan_info* plan, int32_t level, const void* q,
+                                    const void* k_pool, const void* v_pool, float k_scale,
+                                    float v_scale, int64_t num_pages,
+                                    const pkc_level_dev* level_dev, int32_t batch,
+                                    int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t page_size, pkc_dtype q_dtype, float sm_scale,
+                                    void* o_state, pkc_dtype o_dtype, float* lse_state,
+                                    void* dev_ws, size_t dev_bytes, void* stream) {
+  PKC_TRY_BEGIN
+  return prefix_impl(true, k_scale, v_scale, plan, level, q, k_pool, v_pool, num_pages, level_dev,
+                     batch, num_qo_heads, num_kv_heads, head_dim, page_size, q_dtype, sm_scale,
+                     o_state, o_dtype, lse_state, dev_ws, dev_bytes, stream);
+  PKC_TRY_END("pkc_prefix_attention_fp8")
 }
 
 pkc_status pkc_merge_states(const void* o_states, pkc_dtype in_dtype, const float* lse_states,
@@ -519,17 +556,17 @@ pkc_status pkc_merge_state_inplace(void* o_a, float* lse_a, const void* o_b, con
   PKC_TRY_END("pkc_merge_state_inplace")
 }
 
-pkc_status pkc_cascade_decode(const pkc_plan_info* plan, const void* q, const void* k_pool,
-                              const void* v_pool, int64_t num_pages,
-                              const pkc_level_dev* levels, int32_t num_levels,
-                              const int32_t* block_table, int32_t max_blocks,
-                              const int32_t* suffix_seqlens, int32_t batch, int32_t num_qo_heads,
-                              int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
-                              pkc_dtype dtype, float sm_scale, void* o, float* lse, void* dev_ws,
-                              size_t dev_bytes, void* stream) {
-  PKC_TRY_BEGIN
+static pkc_status cascade_impl(bool fp8, float k_scale, float v_scale, const pkc_plan_info* plan,
+                               const void* q, const void* k_pool, const void* v_pool,
+                               int64_t num_pages, const pkc_level_dev* levels, int32_t num_levels,
+                               const int32_t* block_table, int32_t max_blocks,
+                               const int32_t* suffix_seqlens, int32_t batch, int32_t num_qo_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                               pkc_dtype dtype, float sm_scale, void* o, float* lse, void* dev_ws,
+                               size_t dev_bytes, void* stream) {
   pkc_status st = check_shapes(batch, num_qo_heads, num_kv_heads, head_dim, page_size, dtype, sm_scale);
   if (st != PKC_OK) return st;
+  if (fp8 && (st = check_fp8(dtype, k_scale, v_scale)) != PKC_OK) return st;
   if (!plan) return fail(PKC_ERR_INVALID_ARG, "cascade decode needs a plan");
   if ((st = check_plan(plan, batch, num_qo_heads, num_kv_heads, head_dim, page_size, dev_ws, dev_bytes)) != PKC_OK)
     return st;
@@ -547,11 +584,16 @@ pkc_status pkc_cascade_decode(const pkc_plan_info* plan, const void* q, const vo
     return fail(PKC_ERR_INVALID_ARG, "max_blocks * page_size exceeds int32");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   for (int32_t l = 0; l < num_levels; ++l)
-    if ((st = run_level(plan, l, q, k_pool, v_pool, num_pages, &levels[l], dtype, sm_scale, dev_ws, s)) != PKC_OK)
+    if ((st = run_level(plan, l, q, k_pool, v_pool, num_pages, &levels[l], dtype, sm_scale, dev_ws, s,
+                        fp8, k_scale, v_scale)) != PKC_OK)
       return st;
   pkc::DecodeParams p = decode_params(q, k_pool, v_pool, num_pages, block_table, max_blocks,
                                       suffix_seqlens, nullptr, num_qo_heads, num_kv_heads,
                                       page_size, sm_scale, o, lse);
+  if (fp8) {
+    p.scale_log2 *= k_scale;
+    p.v_scale = v_scale;
+  }
   p.st_o = at<float>(dev_ws, plan->off_state_o);
   p.st_lse = at<float>(dev_ws, plan->off_state_lse);
   p.indptr = at<int32_t>(dev_ws, plan->off_dec_indptr);
@@ -571,7 +613,10 @@ pkc_status pkc_cascade_decode(const pkc_plan_info* plan, const void* q, const vo
     }
   }
   const int g = num_qo_heads / num_kv_heads;
-  if ((st = timed(0, s, "decode kernel launch", [&] { return pkc::launch_decode(dtype, head_dim, g, plan->dec_waves, p, plan->num_ctas, s); })) != PKC_OK)
+  if ((st = timed(0, s, "decode kernel launch", [&] {
+         return fp8 ? pkc::launch_decode_fp8(dtype, head_dim, g, plan->dec_waves, p, plan->num_ctas, s)
+                    : pkc::launch_decode(dtype, head_dim, g, plan->dec_waves, p, plan->num_ctas, s);
+       })) != PKC_OK)
     return st;
   if (plan->num_merge > 0) {
     pkc::MergePlanParams m = merge_params(plan, dev_ws, 0, num_levels + 1, true, o, lse);
@@ -579,7 +624,37 @@ pkc_status pkc_cascade_decode(const pkc_plan_info* plan, const void* q, const vo
       return st;
   }
   return PKC_OK;
+}
+
+pkc_status pkc_cascade_decode(const pkc_plan_info* plan, const void* q, const void* k_pool,
+                              const void* v_pool, int64_t num_pages,
+                              const pkc_level_dev* levels, int32_t num_levels,
+                              const int32_t* block_table, int32_t max_blocks,
+                              const int32_t* suffix_seqlens, int32_t batch, int32_t num_qo_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                              pkc_dtype dtype, float sm_scale, void* o, float* lse, void* dev_ws,
+                              size_t dev_bytes, void* stream) {
+  PKC_TRY_BEGIN
+  return cascade_impl(false, 1.f, 1.f, plan, q, k_pool, v_pool, num_pages, levels, num_levels,
+                      block_table, max_blocks, suffix_seqlens, batch, num_qo_heads, num_kv_heads,
+                      head_dim, page_size, dtype, sm_scale, o, lse, dev_ws, dev_bytes, stream);
   PKC_TRY_END("pkc_cascade_decode")
+}
+
+pkc_status pkc_cascade_decode_fp8(const pkc_plan_info* plan, const void* q, const void* k_pool,
+                                  const void* v_pool, float k_scale, float v_scale,
+                                  int64_t num_pages, const pkc_level_dev* levels,
+                                  int32_t num_levels, const int32_t* block_table,
+                                  int32_t max_blocks, const int32_t* suffix_seqlens,
+                                  int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t page_size, pkc_dtype q_dtype,
+                                  float sm_scale, void* o, float* lse, void* dev_ws,
+                                  size_t dev_bytes, void* stream) {
+  PKC_TRY_BEGIN
+  return cascade_impl(true, k_scale, v_scale, plan, q, k_pool, v_pool, num_pages, levels, num_levels,
+                      block_table, max_blocks, suffix_seqlens, batch, num_qo_heads, num_kv_heads,
+                      head_dim, page_size, q_dtype, sm_scale, o, lse, dev_ws, dev_bytes, stream);
+  PKC_TRY_END("pkc_cascade_decode_fp8")
 }
 
 pkc_status pkc_debug_gather_rows(const int32_t* block_table, int32_t max_blocks,

@@ -431,8 +431,8 @@ inline int env_waves() {
 template <typename T, int D, int G, int NW, int PM>
 inline hipError_t launch_decode_t(const DecodeParams& p, int grid_x, hipStream_t s) {
   dim3 grid(grid_x, p.hkv), block(64 * NW);
-  if constexpr (std::is_same<T, F32>::value || IsKV8<T>::value) {
-    // Cascades need the matrix-core prefix kernel, which takes 16-bit pools only.
+  if constexpr (std::is_same<T, F32>::value) {
+    // Cascades need the matrix-core prefix kernel, which takes 16-bit and FP8 pools only.
     if (p.merge_ptr) return hipErrorInvalidValue;
     hipLaunchKernelGGL((decode_kernel<T, D, G, NW, PM, false>), grid, block, 0, s, p);
   } else {

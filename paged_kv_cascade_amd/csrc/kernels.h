@@ -50,7 +50,8 @@ struct PrefixParams {
   const int32_t* page_indices;  // [nnz]
   int32_t num_page_indices;
   int32_t hq, hkv, page_size, page_shift;
-  float scale_log2;
+  float scale_log2;             // sm_scale * log2(e) (times the K scale for FP8 pools)
+  float v_scale;                // FP8 pools: V scale applied to the state (unused otherwise)
   float* st_o;
   float* st_lse;
   const int32_t* indptr;        // [#CTA + 1]
@@ -106,6 +107,9 @@ hipError_t launch_decode_fp8(pkc_dtype q_dt, int head_dim, int group, int waves,
 // 4-wave halves take alternate tiles of an item and merge at its end (one per compute unit).
 hipError_t launch_prefix(pkc_dtype dt, int head_dim, int group, int tile_q, int streams,
                          const PrefixParams& p, int grid_x, hipStream_t s);
+// The same over OCP FP8 E4M3 pools; q_dt (fp16 or bf16) is the query and operand type.
+hipError_t launch_prefix_fp8(pkc_dtype q_dt, int head_dim, int group, int tile_q, int streams,
+                             const PrefixParams& p, int grid_x, hipStream_t s);
 hipError_t launch_merge_plan(pkc_dtype out_dt, int head_dim, const MergePlanParams& p,
                              hipStream_t s);
 hipError_t launch_merge_generic(pkc_dtype in_dt, pkc_dtype out_dt, int head_dim,

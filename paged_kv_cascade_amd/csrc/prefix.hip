@@ -1,565 +1,13 @@
-// Multi-query attention over a shared KV run (one cascade level) for gfx950, on MFMA.
-//
-// "Cascade Inference" blog, algorithm step 1 and Fig. 3: the queries of all requests that
-// share a prefix attend to it together, so the prefix KV is staged once on chip and reused by
-// every query instead of being fetched once per request.  The FlashInfer paper summary
-// (section A3, composable formats) describes the same thing as a dense block of the KV
-// block-sparse matrix processed with a large row tile.  Many queries against one KV set is a
-// real dense contraction, so both products run on matrix cores.
-//
-// Workgroup = 4 waves = 128 query rows (a row is one (query, head) pair of the KV head's
-// group; heads of one query are adjacent rows); two workgroups per compute unit.
-//
-// KV streaming: 32-token tiles go straight from HBM into a 4-stage LDS ring with buffer loads
-// that write LDS (no register staging), so three tiles (48 KB per workgroup) are in flight
-// while one is computed.  Each load instruction moves 1 KB: whole 16-byte chunks of a few
-// head_dim-contiguous K (or V) rows of one page, through a buffer resource over that page.
-// Rows outside the item's token range and pages outside [0, num_pages) are out of the
-// resource's range, so the hardware writes zeros to LDS and reads nothing.  Chunk positions
-// inside a row are XOR-swizzled by the row so that the matrix-core operand reads below hit
-// distinct LDS banks; the swizzle is applied on the global side (each lane fetches the chunk
-// that belongs at its LDS position).
-//
-// Per tile and wave (32 query rows):
-//   * S^T = K Q^T on v_mfma_f32_16x16x32_{f16,bf16} (tokens are the M dimension, so each lane
-//     owns one query column and the softmax reductions are mostly in-lane);
-//   * online softmax in base 2 (running max / sum per query), masked by the tile's valid-token
-//     bits (range and page validity, computed on the scalar unit);
-//   * O^T += V^T P^T on the same MFMA: P^T comes straight from the S^T accumulators, and V^T's
-//     operand is read with the gfx950 LDS transpose read (ds_read_b64_tr_b16), which hands
-//     each lane one head_dim column of four consecutive token rows.
-// Output: one fp32 state (O normalised, natural-log LSE) per (query, head, item).
-#include <type_traits>
-
-#include "device_common.h"
-#include "kernels.h"
+// Instantiations of the multi-query level kernel (prefix_kernel.h) for fp16 / bf16 pools.
+#include "prefix_kernel.h"
 
 namespace pkc {
 
-namespace {
-
-constexpr int kTK = 32;        // KV tokens per tile
-constexpr int kWavesPerStream = 4;  // 4 waves x 32 query rows = one 128-row tile
-constexpr int kRowsPerWave = 32;
-constexpr float kSlack = 8.f;  // lazy-rescale margin of the running maximum, log2 units
-
-typedef short s4_t __attribute__((ext_vector_type(4)));
-typedef float f2_t __attribute__((ext_vector_type(2)));
-
-// Round-to-nearest-even packing of two floats into the operand type is one gfx950
-// instruction (v_cvt_pk_f16_f32 / v_cvt_pk_bf16_f32).
-template <typename T> struct Mfma;
-template <> struct Mfma<F16> {
-  __device__ static f4_t run(const V16& a, const V16& b, f4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, a), __builtin_bit_cast(h8_t, b), c, 0, 0, 0);
-  }
-  __device__ static uint32_t pack(float lo, float hi) {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_t{lo, hi}, h2_t));
-  }
-};
-template <> struct Mfma<BF16> {
-  __device__ static f4_t run(const V16& a, const V16& b, f4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8_t, a), __builtin_bit_cast(b8_t, b), c, 0, 0, 0);
-  }
-  __device__ static uint32_t pack(float lo, float hi) {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_t{lo, hi}, b2_t));
-  }
-};
-
-// True on every lane when `pred` holds on some active lane of the wave.
-__device__ __forceinline__ bool wave_any(bool pred) {
-  return __builtin_amdgcn_ballot_w64(pred) != 0;
-}
-
-// Reductions over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the lane groups that hold one
-// query column of an S^T tile), with the gfx950 lane-swap instructions: permlane32_swap of a
-// value with itself leaves lanes l and l ^ 32 in the two results, permlane16_swap likewise
-// for l ^ 16.
-__device__ __forceinline__ float lane_groups_max(float x) {
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float lane_groups_sum(float x) {
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
-__device__ __forceinline__ V16 lds_load16(const char* p) {
-  const uint4 x = *reinterpret_cast<const uint4*>(p);
-  V16 r;
-  r.w[0] = x.x; r.w[1] = x.y; r.w[2] = x.z; r.w[3] = x.w;
-  return r;
-}
-
-// Transpose read: within each 16-lane group, lanes 4i .. 4i+3 name the four 8-byte pieces of
-// row i (16 consecutive 16-bit values); lane j of the group receives element j of rows 0..3.
-__device__ __forceinline__ uint2 lds_read_tr(const char* p) {
-  const s4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4_t*)(p));
-  return __builtin_bit_cast(uint2, r);
-}
-
-// Buffer resource words for the LDS-writing loads below (raw addressing, no swizzle, the
-// same word 3 as make_rsrc): `bytes` bytes at `base`; an offset at or past `bytes` reads zeros.
-typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ u4_t dma_rsrc(const void* base, int32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  return u4_t{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, (uint32_t)bytes, (uint32_t)kBufferWord3};
-}
-
-// Nontemporal buffer load of 16 bytes per lane straight into LDS: lane l writes lds + 16 * l
-// (M0 holds the LDS address).  Written as an asm statement, so the compiler neither moves
-// memory accesses across it nor adds waits of its own for it: the ring below orders these
-// loads against the LDS reads with explicit vector-memory waits and barriers.
-__device__ __forceinline__ void load_lds16(u4_t r, char* lds, int32_t voff, int32_t soff) {
-  const uint32_t m0 = (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)lds);
-  __asm__ volatile("buffer_load_dwordx4 %0, %1, %2 offen nt lds" ::"v"(voff), "s"(r), "s"(soff), "{m0}"(m0)
-                   : "memory");
-}
-
-// 16-byte global load whose completion the caller orders with an explicit vector-memory wait
-// (the compiler does not count the asm loads above, so it must not place that wait itself).
-// The value must pass through ready() after the wait and before its first use.
-__device__ __forceinline__ u4_t load16_async(const void* p) {
-  u4_t x;
-  __asm__ volatile("global_load_dwordx4 %0, %1, off" : "=v"(x) : "v"(p) : "memory");
-  return x;
-}
-__device__ __forceinline__ void ready(u4_t& x) { __asm__ volatile("" : "+v"(x)); }
-
-// s_waitcnt on the vector-memory count only (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt in
-// 6:4, lgkmcnt in 11:8; the others at their maxima).
-#define PKC_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x70 | 0xF00)
-
-// Workgroup barrier that the compiler may not move memory accesses across (the builtin alone
-// is not a memory operation); the ring's waits are explicit.
-__device__ __forceinline__ void ring_barrier() {
-  __asm__ volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  __asm__ volatile("" ::: "memory");
-}
-
-// Physical 16-byte chunk of logical chunk c in LDS row r: c ^ swz(r).  D = 128 (16 chunks per
-// 256-byte row): the 16 rows read by one K operand load and the 8 rows x 2 chunks of one
-// transpose read land on distinct banks.  D = 64 (8 chunks per 128-byte row, two rows per bank
-// sweep): the same property with the row parity selecting the bank half.
-template <int D>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (D == 128) return 2 * (r & 7) + ((r >> 3) & 1);
-  else return 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
-}
-
-}  // namespace
-
-template <typename T, int D, int G, int NS>
-__global__ __launch_bounds__(64 * kWavesPerStream * NS, NS == 1 ? 2 : 1) void prefix_kernel(const PrefixParams p) {
-  constexpr int ES = 2;
-  constexpr int RB = D * ES;                 // bytes per K / V row
-  constexpr int CPR = RB / 16;               // 16-byte chunks per row
-  constexpr int NDMA = 4;                    // load instructions per wave per tile (K and V)
-  constexpr int STB = kTK * RB;              // bytes of K (or V) of one tile
-  constexpr int SLOT = 2 * STB;              // one tile in LDS: K rows, then V rows
-  constexpr int STAGES = 4;
-  constexpr int KS = D / 32;                 // contraction steps of S^T
-  constexpr int DM = D / 16;                 // 16-row tiles of O^T
-  static_assert(kTK == 32 && (D == 64 || D == 128) && (NS == 1 || NS == 2), "tile layout");
-
-  // The ring: stage s of stream g is ring + (g * STAGES + s) * SLOT; the valid-row bits of that
-  // tile are word g * STAGES + s of sflag (byte w written by the stream's wave w).
-  __shared__ __attribute__((aligned(16))) char ring[STAGES * NS * SLOT];
-  __shared__ uint32_t sflag[STAGES * NS];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int stream = wv / kWavesPerStream;   // tiles stream, stream + NS, stream + 2 NS, ...
-  const int wq = wv % kWavesPerStream;       // query rows 32 wq .., tile rows 8 wq ..
-  const int l16 = lane & 15;
-  const int lg = lane >> 4;              // lane group 0..3
-  const int hk = blockIdx.y;
-  const int shift = p.page_shift;
-  const int P = p.page_size;
-  const char* kg = static_cast<const char*>(p.k);
-  const char* vg = static_cast<const char*>(p.v);
-  const int32_t row_stride = p.hkv * RB;        // bytes between consecutive slots of a page
-  const int32_t page_bytes = P * row_stride;    // < 2 GiB (checked on the host)
-  const int32_t npool = (int32_t)min<int64_t>(p.num_pages, INT32_MAX);
-  // Transpose-read role inside the lane group: row (4 tokens apart) and 8-byte column piece.
-  const int tr_row = (lane & 15) >> 2;
-  const int tr_piece = lane & 3;
-
-  // Loader role.  Wave wq of a stream loads tile rows 8wq .. 8wq+7 of K and of V as two 4-row
-  // groups (rows 8wq + 4g .., one page each since pages hold a multiple of 4 slots).  D = 128:
-  // one 1 KB instruction per group, lane l -> row 8wq + 4g + l/16, LDS chunk l%16.  D = 64: one
-  // 1 KB instruction covers both groups as two exec-masked halves, lane l -> row 8wq + l/8,
-  // LDS chunk l%8.  Each lane fetches logical chunk (LDS chunk) ^ swz(row); voff is its byte
-  // offset from its group's first row in the page.
-  constexpr int NI = D == 128 ? 2 : 1;   // instructions per operand per tile
-  int32_t voff[NI];
-  int lrow[NI];
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    lrow[i] = 8 * wq + (D == 128 ? 4 * i + lane / 16 : lane / 8);
-    const int cg = (lane % CPR) ^ swz<D>(lrow[i]);
-    voff[i] = ((lrow[i] - 8 * wq) & 3) * row_stride + hk * RB + cg * 16;
-  }
-
-  const int it_begin = scalar_load(p.indptr + blockIdx.x);
-  const int it_end = scalar_load(p.indptr + blockIdx.x + 1);
-  for (int it = it_begin; it < it_end; ++it) {
-    const int32_t* rec = p.items + 8 * (int64_t)it;
-    const int grp = scalar_load(rec);
-    const int q0 = scalar_load(rec + 1), nq = scalar_load(rec + 2);
-    const int kb = scalar_load(rec + 3), ke = scalar_load(rec + 4), srow = scalar_load(rec + 5);
-    const int nrows = nq * G;
-    const int pbeg = scalar_load(p.page_indptr + grp);
-    const int npages_grp = scalar_load(p.page_indptr + grp + 1) - pbeg;
-    const int32_t* pages = p.page_indices + pbeg;
-    const int t0 = (kb / kTK) * kTK;
-    // A group without pages holds no tokens (its kv_len is then a caller error).
-    const int ntiles = (ke > kb && npages_grp > 0) ? (ke - t0 + kTK - 1) / kTK : 0;
-    const int nsteps = (ntiles + NS - 1) / NS;   // tiles per stream, rounded up
-    const int last_page = max(npages_grp - 1, 0);
-    const bool wave_active = wq * kRowsPerWave < nrows;
-
-    // Page-list entries of this wave's two row groups in tile tt (scalar loads, clamped into
-    // the list; a group past the list is rejected when the tile is issued).  They are fetched
-    // one step before use, so their latency hides behind a tile's arithmetic.
-    struct Pg { int e0, e1; };
-    auto fetch = [&](int tt) -> Pg {
-      const int rb = t0 + tt * kTK + 8 * wq;
-      Pg r;
-      r.e0 = scalar_load(pages + min(rb >> shift, last_page));
-      r.e1 = scalar_load(pages + min((rb + 4) >> shift, last_page));
-      return r;
-    };
-
-    // Loads of tile tt into slot `dst` and the slot's valid-row byte of this wave; a tile past
-    // the end reads nothing (zeros) and marks no row valid.
-    auto issue = [&](int tt, const Pg& pg, char* dst, uint32_t* flag) {
-      const int rb = t0 + tt * kTK + 8 * wq;      // token of the wave's first row
-      const bool in_tiles = tt < ntiles;
-      const int e[2] = {pg.e0, pg.e1};
-      u4_t rk[2], rw[2];
-      int32_t soff[2];
-      bool ok[2];
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        const int tg = rb + 4 * g;
-        ok[g] = in_tiles & ((tg >> shift) < npages_grp) & (e[g] >= 0) & (e[g] < npool);
-        const int64_t pofs = ok[g] ? (int64_t)e[g] * page_bytes : 0;
-        rk[g] = dma_rsrc(kg + pofs, ok[g] ? page_bytes : 0);
-        rw[g] = dma_rsrc(vg + pofs, ok[g] ? page_bytes : 0);
-        soff[g] = (tg & (P - 1)) * row_stride;
-      }
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const int t = t0 + tt * kTK + lrow[i];
-        const int32_t off = ((t >= kb) & (t < ke)) ? voff[i] : kOffsetNone;
-        char* dk = dst + (8 * wq + 4 * i) * RB;
-        char* dv = dk + STB;
-        if constexpr (D == 128) {
-          load_lds16(rk[i], dk, off, soff[i]);
-          load_lds16(rw[i], dv, off, soff[i]);
-        } else {
-          // Two exec-masked halves (their rows may sit in different pages); both write the
-          // block's 1 KB, lane l at 16 * l.
-          if (lane < 32) {
-            load_lds16(rk[0], dk, off, soff[0]);
-            load_lds16(rw[0], dv, off, soff[0]);
-          } else {
-            load_lds16(rk[1], dk, off, soff[1]);
-            load_lds16(rw[1], dv, off, soff[1]);
-          }
-        }
-      }
-      // Valid rows: inside [kb, ke) and in a valid page.
-      const int lo = min(max(kb - rb, 0), 8), hi = min(max(ke - rb, 0), 8);
-      uint32_t bits = hi > lo ? (((1u << hi) - 1u) & ~((1u << lo) - 1u)) : 0u;
-      bits &= (ok[0] ? 0x0Fu : 0u) | (ok[1] ? 0xF0u : 0u);
-      reinterpret_cast<uint8_t*>(flag)[wq] = (uint8_t)bits;
-    };
-
-    V16 qb[2][KS];   // Q^T operands: query row wq*32 + nt*16 + l16, head_dim ks*32 + 8*lg .. +8
-    f4_t oacc[DM][2];
-#pragma unroll
-    for (int dm = 0; dm < DM; ++dm)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) oacc[dm][nt] = f4_t{0.f, 0.f, 0.f, 0.f};
-    float m_run[2] = {kNegInf, kNegInf};
-    float l_run[2] = {0.f, 0.f};
-
-    auto compute = [&](const char* ks_s, const char* vs_s, uint32_t mask) {
-      if (!wave_active) return;
-      // S^T[mt][nt]: tokens mt*16 + 4*lg + i, query column nt*16 + l16.
-      f4_t s[2][2];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        s[mt][0] = f4_t{0.f, 0.f, 0.f, 0.f};
-        s[mt][1] = f4_t{0.f, 0.f, 0.f, 0.f};
-        const int r = mt * 16 + l16;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int c = (ks * 4 + lg) ^ swz<D>(r);
-          const V16 a = lds_load16(ks_s + r * RB + c * 16);
-          s[mt][0] = Mfma<T>::run(a, qb[0][ks], s[mt][0]);
-          s[mt][1] = Mfma<T>::run(a, qb[1][ks], s[mt][1]);
-        }
-      }
-      // Tiles whose 32 tokens are all valid (every tile but the ragged ends) skip masking.
-      if (mask != ~0u) {
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const bool v = (mask >> (mt * 16 + 4 * lg + i)) & 1u;
-            s[mt][0][i] = v ? s[mt][0][i] : kNegInf;
-            s[mt][1][i] = v ? s[mt][1][i] : kNegInf;
-          }
-      }
-      V16 pb[2];   // P^T operands per query tile nt (the tile's 32 tokens are one step)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        float mx = kNegInf;
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[mt][nt][i]);
-        mx = lane_groups_max(mx) * p.scale_log2;
-        // Lazy reference maximum: m_run moves only when a score exceeds it by more than
-        // kSlack (log2 units), so O and l are rescaled only on such tiles (in practice the
-        // first ones).  Weights stay below 2^kSlack, which fp32 and the 16-bit operand types
-        // hold with their usual relative precision, and the final state (O / l, m + log2 l)
-        // does not depend on the reference used.  A fully masked column (mx = -inf) never
-        // raises its reference.
-        const bool raise = mx > m_run[nt] + kSlack;
-        if (wave_any(raise)) {
-          const float alpha = raise ? fast_exp2(m_run[nt] - mx) : 1.f;
-          m_run[nt] = raise ? mx : m_run[nt];
-          l_run[nt] *= alpha;
-#pragma unroll
-          for (int dm = 0; dm < DM; ++dm) oacc[dm][nt] *= alpha;
-        }
-        const float mu = (m_run[nt] == kNegInf) ? 0.f : m_run[nt];
-        float psum = 0.f;
-        float pr[2][4];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            // P enters the PV product rounded to the operand type, but the denominator
-            // (and so the LSE) sums the fp32 weights: with bf16, summing rounded weights
-            // would move LSE by up to 2^-9.
-            pr[mt][i] = fast_exp2(fmaf(s[mt][nt][i], p.scale_log2, -mu));
-            psum += pr[mt][i];
-          }
-        l_run[nt] += psum;
-        pb[nt].w[0] = Mfma<T>::pack(pr[0][0], pr[0][1]);
-        pb[nt].w[1] = Mfma<T>::pack(pr[0][2], pr[0][3]);
-        pb[nt].w[2] = Mfma<T>::pack(pr[1][0], pr[1][1]);
-        pb[nt].w[3] = Mfma<T>::pack(pr[1][2], pr[1][3]);
-      }
-      // O^T[dm][nt] += V^T * P^T over the tile's 32 tokens.  Lane group g supplies contraction
-      // elements 8g .. 8g+7 = tokens 16h + 4g + i (h = 0, 1; i = 0..3), the order of the S^T
-      // accumulators; each half is one transpose read of rows 16h + 4g + tr_row, elements
-      // dm*16 + 4*tr_piece .. +4 (logical chunk 2*dm + tr_piece/2, swizzled by row).
-#pragma unroll
-      for (int dm = 0; dm < DM; ++dm) {
-        V16 a;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int r = 16 * h + 4 * lg + tr_row;
-          const int c = (2 * dm + (tr_piece >> 1)) ^ swz<D>(r);
-          const uint2 x = lds_read_tr(vs_s + r * RB + c * 16 + (tr_piece & 1) * 8);
-          a.w[2 * h] = x.x;
-          a.w[2 * h + 1] = x.y;
-        }
-        oacc[dm][0] = Mfma<T>::run(a, pb[0], oacc[dm][0]);
-        oacc[dm][1] = Mfma<T>::run(a, pb[1], oacc[dm][1]);
-      }
-    };
-
-    if (ntiles > 0) {
-      // Q^T operands first (rows past the tile read the tile's first row: their columns are
-      // computed but never stored).
-      u4_t qr[2][KS];
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const int r = wq * kRowsPerWave + nt * 16 + l16;
-        const int rr = r < nrows ? r : 0;
-        const int64_t qoff = ((int64_t)(q0 + rr / G) * p.hq + hk * G + rr % G) * D;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          qr[nt][ks] = load16_async(static_cast<const char*>(p.q) + (qoff + ks * 32 + 8 * lg) * ES);
-      }
-      // The stream's j-th tile (tile stream + j NS) lives in stage j % 4.  Prologue: its first
-      // three tiles in flight, page entries of the fourth requested.
-      char* const sring = ring + stream * STAGES * SLOT;
-      uint32_t* const sfl = sflag + stream * STAGES;
-      Pg pg = fetch(stream);
-#pragma unroll
-      for (int j = 0; j < STAGES - 1; ++j) {
-        issue(stream + j * NS, pg, sring + j * SLOT, sfl + j);
-        pg = fetch(stream + (j + 1) * NS);
-      }
-      // The Q loads precede the prologue's 3 * NDMA loads.
-      PKC_WAIT_VMCNT(3 * NDMA);
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          ready(qr[nt][ks]);
-          qb[nt][ks] = V16{{qr[nt][ks][0], qr[nt][ks][1], qr[nt][ks][2], qr[nt][ks][3]}};
-        }
-
-      // Step j in stage S = j % 4: wait for this wave's loads of the stream's j-th tile (its
-      // next two tiles stay in flight), barrier (every wave's loads and valid-row byte of the
-      // step's tiles have landed and every wave is done with step j-1), refill stage S-1 with
-      // the stream's tile j+3, request the page entries of its tile j+4, compute tile j.  No
-      // LDS wait is needed before the barrier: a wave's LDS operations complete in order, and
-      // the compiler waits for the last operand read of a tile before its final products, so
-      // by the end of a step the wave's valid-row byte is written and its reads of the stage
-      // are done.  Every stream runs the same number of steps (and barriers).  Stage numbers
-      // are compile-time constants (four steps per loop trip), so LDS addresses are immediate
-      // offsets.
-      auto step = [&](auto stage_c, int j) {
-        constexpr int S = decltype(stage_c)::value;
-        constexpr int N = (S + STAGES - 1) % STAGES;
-        const int tt = stream + j * NS;
-        PKC_WAIT_VMCNT(2 * NDMA);
-        ring_barrier();
-        const uint32_t mask = sfl[S];   // the same on every lane; first needed after S^T
-        issue(tt + (STAGES - 1) * NS, pg, sring + N * SLOT, sfl + N);
-        pg = fetch(tt + STAGES * NS);
-        if (tt < ntiles) compute(sring + S * SLOT, sring + S * SLOT + STB, mask);
-      };
-      for (int j = 0; j < nsteps; j += 4) {
-        step(std::integral_constant<int, 0>(), j);
-        if (j + 1 >= nsteps) break;
-        step(std::integral_constant<int, 1>(), j + 1);
-        if (j + 2 >= nsteps) break;
-        step(std::integral_constant<int, 2>(), j + 2);
-        if (j + 3 >= nsteps) break;
-        step(std::integral_constant<int, 3>(), j + 3);
-      }
-    }
-
-    // Every load of the ring (including the empty ones past the last tile, which still write
-    // zeros to their slot) has landed and every wave is done with the ring.
-    __builtin_amdgcn_s_waitcnt(0);
-    ring_barrier();
-
-    if constexpr (NS == 2) {
-      // Stream 1 hands its state to stream 0 through the idle ring: value f of lane l of wave
-      // wq goes to float f * 256 + 64 wq + l.  Waves wq of the two streams hold the same rows
-      // in the same lanes, so the merge is lane to lane.
-      constexpr int NV = DM * 2 * 4 + 4;          // oacc, m_run[2], l_run[2]
-      static_assert(NV * 256 * 4 <= STAGES * NS * SLOT, "merge payload fits the ring");
-      float* xf = reinterpret_cast<float*>(ring) + 64 * wq + lane;
-      if (ntiles > 0) {
-        if (stream == 1) {
-#pragma unroll
-          for (int dm = 0; dm < DM; ++dm)
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) xf[((dm * 2 + nt) * 4 + i) * 256] = oacc[dm][nt][i];
-#pragma unroll
-          for (int nt = 0; nt < 2; ++nt) {
-            xf[(DM * 8 + nt) * 256] = m_run[nt];
-            xf[(DM * 8 + 2 + nt) * 256] = l_run[nt];
-          }
-        }
-        ring_barrier();
-        if (stream == 0) {
-#pragma unroll
-          for (int nt = 0; nt < 2; ++nt) {
-            const float m2 = xf[(DM * 8 + nt) * 256];
-            const float l2 = xf[(DM * 8 + 2 + nt) * 256];
-            const float mn = fmaxf(m_run[nt], m2);
-            const float mu = (mn == kNegInf) ? 0.f : mn;
-            const float a1 = fast_exp2(m_run[nt] - mu), a2 = fast_exp2(m2 - mu);
-            m_run[nt] = mn;
-            l_run[nt] = l_run[nt] * a1 + l2 * a2;
-#pragma unroll
-            for (int dm = 0; dm < DM; ++dm)
-#pragma unroll
-              for (int i = 0; i < 4; ++i)
-                oacc[dm][nt][i] = oacc[dm][nt][i] * a1 + xf[((dm * 2 + nt) * 4 + i) * 256] * a2;
-          }
-        }
-      }
-    }
-
-    // Finish (stream 0): total sum over the 4 lane groups, normalise, write the fp32 state.
-    if (stream == 0 && wave_active) {
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const float lt = lane_groups_sum(l_run[nt]);
-        const int r = wq * kRowsPerWave + nt * 16 + l16;
-        if (r < nrows) {
-          const float inv = lt > 0.f ? 1.f / lt : 0.f;
-          const int64_t srow_q = (int64_t)srow + r / G;
-          const int h = hk * G + r % G;
-          float* dst = p.st_o + (srow_q * p.hq + h) * D;
-#pragma unroll
-          for (int dm = 0; dm < DM; ++dm) {
-            const f4_t o = oacc[dm][nt] * inv;
-            *reinterpret_cast<float4*>(dst + dm * 16 + 4 * lg) = make_float4(o[0], o[1], o[2], o[3]);
-          }
-          if (lg == 0)
-            p.st_lse[srow_q * p.hq + h] = lt > 0.f ? (m_run[nt] + log2f(lt)) * kLn2 : kNegInf;
-        }
-      }
-    }
-    // The merge reads of the ring and this item's stores are done and every wave has left the
-    // ring before the next item refills it.
-    __builtin_amdgcn_s_waitcnt(0);
-    ring_barrier();
-  }
-}
-
-template <typename T, int D, int G>
-static hipError_t launch_prefix_t(int streams, const PrefixParams& p, int grid_x, hipStream_t s) {
-  const dim3 grid(grid_x, p.hkv);
-  if (streams == 2)
-    hipLaunchKernelGGL((prefix_kernel<T, D, G, 2>), grid, dim3(128 * kWavesPerStream), 0, s, p);
-  else
-    hipLaunchKernelGGL((prefix_kernel<T, D, G, 1>), grid, dim3(64 * kWavesPerStream), 0, s, p);
-  return hipGetLastError();
-}
-
-template <typename T, int D>
-static hipError_t launch_prefix_g(int group, int streams, const PrefixParams& p, int grid_x,
-                                  hipStream_t s) {
-  switch (group) {
-    case 1: return launch_prefix_t<T, D, 1>(streams, p, grid_x, s);
-    case 2: return launch_prefix_t<T, D, 2>(streams, p, grid_x, s);
-    case 4: return launch_prefix_t<T, D, 4>(streams, p, grid_x, s);
-    case 8: return launch_prefix_t<T, D, 8>(streams, p, grid_x, s);
-  }
-  return hipErrorInvalidValue;
-}
-
-template <typename T>
-static hipError_t launch_prefix_d(int head_dim, int group, int streams, const PrefixParams& p,
-                                  int grid_x, hipStream_t s) {
-  if (head_dim == 64) return launch_prefix_g<T, 64>(group, streams, p, grid_x, s);
-  if (head_dim == 128) return launch_prefix_g<T, 128>(group, streams, p, grid_x, s);
-  return hipErrorInvalidValue;
-}
-
 hipError_t launch_prefix(pkc_dtype dt, int head_dim, int group, int tile_q, int streams,
                          const PrefixParams& p, int grid_x, hipStream_t s) {
-  if (grid_x <= 0) return hipSuccess;
-  if (tile_q * group > kWavesPerStream * kRowsPerWave) return hipErrorInvalidValue;
-  if (p.page_size < 4 || (streams != 1 && streams != 2)) return hipErrorInvalidValue;
   switch (dt) {
-    case PKC_F16: return launch_prefix_d<F16>(head_dim, group, streams, p, grid_x, s);
-    case PKC_BF16: return launch_prefix_d<BF16>(head_dim, group, streams, p, grid_x, s);
+    case PKC_F16: return launch_prefix_d<F16, false>(head_dim, group, tile_q, streams, p, grid_x, s);
+    case PKC_BF16: return launch_prefix_d<BF16, false>(head_dim, group, tile_q, streams, p, grid_x, s);
     default: break;
   }
   return hipErrorInvalidValue;

@@ -7,7 +7,10 @@ with the gfx950 conversion instructions.  Covers every byte value through a sing
 decode (bit-exact outputs, which also pins the byte order within a lane's load), a matrix
 of small ragged cases over query dtype, head_dim, group size and page size with NaN codes
 in every row no request reads, the LLaMA2-7B-shaped decode at full size (sampled
-requests) and the plan-driven split path with its merge.
+requests) and the plan-driven split path with its merge.  Cascades over FP8 pools (the
+matrix-core level kernel on converted tiles, then the FP8 suffix decode with its fold): the
+two- and three-level workloads at full size (sampled), small random cascades, and each
+level's states alone with 4- and 8-wave workgroups.
 """
 
 import math
@@ -182,3 +185,105 @@ def test_fp8_argument_errors(api):
     o, lse = api.batch_decode_paged_fp8(q, k8, k8, bt, lens)   # valid: all-zero codes
     torch.cuda.synchronize()
     assert torch.all(o == 0) and torch.allclose(lse, torch.zeros_like(lse))
+
+
+# --- cascades over FP8 pools: MFMA level kernel on converted tiles + FP8 suffix decode ----------
+
+def _fp8_cascade_run(api, w, k8, v8, ksc, vsc, level_ctas=0, num_ctas=0, tile_q=0):
+    params = api.make_params(w.batch, w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size,
+                             num_ctas=num_ctas, level_ctas=level_ctas, level_tile_q=tile_q)
+    host_levels = [{"qo_indptr": lv["qo_indptr"], "kv_lens": lv["kv_lens"]} for lv in w.levels]
+    ws = api.Workspace(params, host_levels)
+    info = api.plan(params, w.cache_seqlens.cpu().tolist(), host_levels, workspace=ws)
+    devs, keep = [], []
+    for lv in w.levels:
+        d, k = api.level_dev(lv)
+        devs.append(d)
+        keep.append(k)
+    o, lse = api.cascade_decode_fp8(info, w.q, k8, v8, devs, w.block_table, w.cache_seqlens,
+                                    k_scale=ksc, v_scale=vsc, sm_scale=w.sm_scale)
+    return o, lse, info, ws, devs, keep
+
+
+def _fp8_cascade_oracle(w, k8, v8, ksc, vsc, requests=None):
+    return ofp8.cascade_decode_fp8(host(w.q), CodeView(k8), CodeView(v8), ksc, vsc, w.page_size,
+                                   w.sm_scale, w.levels, w.block_table.cpu().numpy(),
+                                   w.cache_seqlens.cpu().numpy(), requests=requests)
+
+
+def test_fp8_two_level_cascade_full_size(api):
+    """The cascade workload (32768-token shared prefix + 256 tokens per request, batch 128,
+    32 heads x 128, page 16) with fp16 queries over E4M3 pools (k_scale 0.25, v_scale 0.125)."""
+    say("case: fp8 two-level cascade prefix32768 suffix256 b128 h32 d128 p16, fp16 q (sampled oracle)")
+    w = workloads.cascade_two_level(device="cuda")
+    k8 = workloads.fp8_e4m3_pool(w.k_pool, 0.25)
+    v8 = workloads.fp8_e4m3_pool(w.v_pool, 0.125)
+    o, lse, info, *_ = _fp8_cascade_run(api, w, k8, v8, 0.25, 0.125)
+    o2, lse2, *_ = _fp8_cascade_run(api, w, k8, v8, 0.25, 0.125)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2), "repeat run differs"
+    reqs = [0, 77, 127]
+    O, L = _fp8_cascade_oracle(w, k8, v8, 0.25, 0.125, requests=reqs)
+    check_state(o, lse, O, L, torch.float16, "fp8 cascade 32K prefix", rows=reqs)
+
+
+def test_fp8_multi_level_cascade_full_size(api):
+    """Global prefix 16384 + 4 groups x 4096 + 512 per request, batch 128, bf16 queries over
+    E4M3 pools."""
+    say("case: fp8 three-level cascade 16384 + 4x4096 + 512, b128 h32 d128, bf16 q (sampled oracle)")
+    w = workloads.cascade_multi_level(device="cuda", dtype=torch.bfloat16)
+    k8 = workloads.fp8_e4m3_pool(w.k_pool, 0.5)
+    v8 = workloads.fp8_e4m3_pool(w.v_pool, 0.5)
+    o, lse, *_ = _fp8_cascade_run(api, w, k8, v8, 0.5, 0.5)
+    torch.cuda.synchronize()
+    reqs = [0, 40, 95, 127]
+    O, L = _fp8_cascade_oracle(w, k8, v8, 0.5, 0.5, requests=reqs)
+    check_state(o, lse, O, L, torch.bfloat16, "fp8 cascade 3 levels", rows=reqs)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_fp8_small_cascades(api, seed):
+    from tests.test_gpu_cascade import _small_cascade
+    qdt = [torch.float16, torch.bfloat16][seed % 2]
+    D = [128, 64][(seed // 2) % 2]
+    g = [1, 4, 2, 8][seed % 4]
+    P = [16, 4, 32][seed % 3]
+    w = _small_cascade(500 + seed, qdt, D, g, P)
+    ksc, vsc = [(1.0, 1.0), (0.3, 2.0), (1.7, 0.4)][seed % 3]
+    k8 = workloads.fp8_e4m3_pool(w.k_pool, ksc)
+    v8 = workloads.fp8_e4m3_pool(w.v_pool, vsc)
+    lctas = [1, 3, 8][seed % 3]
+    tile_q = [0, 16 // g, 128 // g][seed % 3]
+    say(f"case: fp8 small cascade seed={seed} q {qdt} D={D} g={g} P={P} B={w.batch} levels={len(w.levels)} "
+        f"level_ctas={lctas} tile_q={tile_q} scales=({ksc}, {vsc})")
+    o, lse, *_ = _fp8_cascade_run(api, w, k8, v8, ksc, vsc, level_ctas=lctas, num_ctas=13, tile_q=tile_q)
+    torch.cuda.synchronize()
+    O, L = _fp8_cascade_oracle(w, k8, v8, ksc, vsc)
+    check_state(o, lse, O, L, qdt, f"fp8 small cascade {seed}")
+
+
+@pytest.mark.parametrize("streams", ["1", "2"])
+def test_fp8_prefix_attention_standalone(api, streams, monkeypatch):
+    """Each level's states alone (the level kernel over converted tiles, then its merge), with
+    4-wave and 8-wave workgroups."""
+    from tests.test_gpu_cascade import _small_cascade
+    say(f"case: fp8 prefix_attention per level vs the oracle's level states, streams={streams}")
+    monkeypatch.setenv("PKC_PREFIX_STREAMS", streams)
+    w = _small_cascade(600, torch.float16, 128, 2, 16)
+    k8 = workloads.fp8_e4m3_pool(w.k_pool, 0.6)
+    v8 = workloads.fp8_e4m3_pool(w.v_pool, 1.5)
+    host_levels = [{"qo_indptr": lv["qo_indptr"], "kv_lens": lv["kv_lens"]} for lv in w.levels]
+    params = api.make_params(w.batch, w.num_qo_heads, w.num_kv_heads, 128, 16, num_ctas=8, level_ctas=5)
+    ws = api.Workspace(params, host_levels)
+    info = api.plan(params, w.cache_seqlens.cpu().tolist(), host_levels, workspace=ws)
+    for l, lv in enumerate(w.levels):
+        d, keep = api.level_dev(lv)
+        o, lse = api.prefix_attention_fp8(info, l, w.q, k8, v8, d, k_scale=0.6, v_scale=1.5,
+                                          sm_scale=w.sm_scale)
+        torch.cuda.synchronize()
+        O, L = ofp8.level_prefix_states_fp8(host(w.q), CodeView(k8), CodeView(v8), 0.6, 1.5, 16,
+                                            w.sm_scale, lv, w.batch)
+        covered = ~np.isnan(L[:, 0])
+        Lf = np.where(covered[:, None], L, -np.inf)
+        Of = np.where(covered[:, None, None], O, 0.0)
+        check_state(o, lse, Of, Lf, torch.float16, f"fp8 level {l}")

@@ -130,3 +130,30 @@ def test_fp8_single_token_returns_the_decoded_value_row():
         krow = kf[page, 0, kh].to(torch.float64).numpy()
         assert np.array_equal(O[b, h], 2.0 * vrow)
         assert math.isclose(L[b, h], 0.25 * 0.5 * float(q[b, h] @ krow), rel_tol=1e-14, abs_tol=1e-15)
+
+
+def test_fp8_cascade_and_level_states_equal_torch_decoded_pools():
+    """The cascade and per-level oracles over code pools equal the same oracles over float
+    pools holding torch's decoding of the codes (two levels, one of them partial)."""
+    gen = torch.Generator().manual_seed(11)
+    P, hkv, g, D, B = 4, 1, 2, 8, 5
+    kf = (torch.randn(12, P, hkv, D, generator=gen) * 0.7).to(torch.float8_e4m3fn)
+    vf = (torch.randn(12, P, hkv, D, generator=gen) * 0.7).to(torch.float8_e4m3fn)
+    q = torch.randn(B, hkv * g, D, generator=gen, dtype=torch.float64).numpy()
+    levels = [{"qo_indptr": [0, 5], "kv_page_indptr": [0, 2], "kv_page_indices": [3, 7], "kv_lens": [6]},
+              {"qo_indptr": [0, 2, 4], "kv_page_indptr": [0, 1, 3], "kv_page_indices": [0, 9, 4],
+               "kv_lens": [3, 8]}]
+    bt = np.array([[1, -1], [2, 5], [6, -1], [8, -1], [10, 11]], dtype=np.int32)
+    lens = np.array([2, 7, 0, 4, 5])
+    kc, vc = kf.view(torch.uint8).numpy(), vf.view(torch.uint8).numpy()
+    kd, vd = kf.to(torch.float64).numpy(), vf.to(torch.float64).numpy()
+    O8, L8 = fp8.cascade_decode_fp8(q, kc, vc, 1.0, 1.0, P, 0.5, levels, bt, lens)
+    O, L = attention.cascade_decode(q, kd, vd, P, 0.5, levels, bt, lens)
+    assert np.array_equal(O8, O) and np.array_equal(L8, L)
+    for lv in levels:
+        O8, L8 = fp8.level_prefix_states_fp8(q, kc, vc, 2.0, 0.5, P, 0.5, lv, B)
+        O, L = attention.level_prefix_states(q, 2.0 * kd, 0.5 * vd, P, 0.5, lv, B)
+        assert np.array_equal(np.isnan(L8), np.isnan(L))
+        m = ~np.isnan(L)
+        assert np.allclose(L8[m], L[m], rtol=1e-14, atol=1e-14)
+        assert np.allclose(O8[m], O[m], rtol=1e-13, atol=1e-15)
