@@ -177,3 +177,44 @@ def level_prefix_states(q, k_pool, v_pool, page_size, sm_scale, level, num_reque
         pages, slots = cascade_token_rows(b, [level], None, None, page_size)
         O[b], L[b] = _state_over_rows(q[b], k_pool, v_pool, pages, slots, sm_scale, range(Hq))
     return O, L
+
+
+def prefill_limit(lq, lkv, i, causal):
+    """Number of KV tokens query i of a request with lq queries and lkv KV tokens sees: the
+    queries are the request's last lq tokens, so query i sits at position lkv - lq + i and,
+    with the causal mask, sees tokens 0 .. lkv - lq + i (none when that is negative); without
+    it, all lkv tokens."""
+    if not causal:
+        return lkv
+    return max(0, min(lkv, lkv - lq + i + 1))
+
+
+def batch_prefill(q, qo_indptr, k_pool, v_pool, block_table, kv_lens, page_size, sm_scale,
+                  causal, rows=None, heads=None):
+    """Ragged multi-token queries over a paged KV cache.
+
+    q: [total_q, Hq, D], packed without padding: request b's queries are rows
+    qo_indptr[b] .. qo_indptr[b+1]-1 (the cu_seq_lens_q indexing of the "Paged attention"
+    page's varlen path; the paper summary's ragged query tensors, section A3).  Request b's
+    KV is its block-table row over kv_lens[b] tokens (decode-path indexing), already holding
+    the new tokens.  Query i of request b attends over the first prefill_limit(...) tokens.
+    ``rows`` restricts the work to some query rows (sampled parity); other rows are NaN.
+    Returns (O [total_q, Hq, D], LSE [total_q, Hq])."""
+    q = np.asarray(q, dtype=np.float64)
+    T, Hq, D = q.shape
+    O = np.full((T, Hq, D), np.nan)
+    L = np.full((T, Hq), np.nan)
+    want = None if rows is None else set(int(r) for r in rows)
+    hs = list(range(Hq)) if heads is None else list(heads)
+    B = len(qo_indptr) - 1
+    for b in range(B):
+        q0, q1 = int(qo_indptr[b]), int(qo_indptr[b + 1])
+        lq, lkv = q1 - q0, int(kv_lens[b])
+        for i in range(lq):
+            r = q0 + i
+            if want is not None and r not in want:
+                continue
+            n = prefill_limit(lq, lkv, i, causal)
+            pages, slots = token_pages(block_table[b], 0, n, page_size)
+            O[r], L[r] = _state_over_rows(q[r], k_pool, v_pool, pages, slots, sm_scale, hs)
+    return O, L
