@@ -360,6 +360,36 @@ pkc_status pkc_cascade_decode_fp8(const pkc_plan_info* plan, const void* q, cons
                                   size_t dev_bytes, void* stream);
 
 /*
+ * Ragged multi-token queries over the paged KV cache (prefill / append attention): the
+ * "Paged attention" page's varlen indexing (cu_seq_lens_q packing of queries without padding)
+ * over the decode path's block tables, as the FlashInfer paper summary's ragged query tensors
+ * over a block-sparse KV cache (section A3).  Request b (0 <= b < num_requests) owns query
+ * rows qo_indptr[b] .. qo_indptr[b+1]-1 of q ([total_q, Hq, D], dtype PKC_F16 or PKC_BF16)
+ * and attends over tokens [0, kv_lens[b]) of its block-table row (block_table [num_requests,
+ * max_blocks], -1 = unallocated; the new tokens already appended).  Its l_q(b) queries are
+ * the sequence's last tokens: with causal != 0, query i sees tokens t <= kv_lens[b] - l_q(b)
+ * + i (none when negative); with causal == 0 it sees all kv_lens[b] tokens.  Writes o
+ * ([total_q, Hq, D], q's dtype) and lse ([total_q, Hq], fp32, natural log, -inf for a query
+ * that sees no token).
+ * The plan must be built by pkc_plan with batch = total_q (each query row is one plan
+ * request), kv_lens_h all zero, and one level whose num_groups = num_requests, qo_indptr =
+ * the same qo_indptr (host copy) and kv_lens = the same kv_lens (host copy); the run is the
+ * level's multi-query kernel (query tiles of T_q rows, KV chunks by the plan) followed by the
+ * merge of every query row's chunk states.  qo_indptr and kv_lens here are device arrays.
+ * Errors: PKC_ERR_PLAN_MISMATCH when the plan does not have that shape; PKC_ERR_UNSUPPORTED
+ * for fp32 queries or page_size < 4.  Pointers are caller-owned; the work is enqueued on
+ * `stream`.
+ */
+pkc_status pkc_batch_prefill_paged(const pkc_plan_info* plan, const void* q, const void* k_pool,
+                                   const void* v_pool, int64_t num_pages,
+                                   const int32_t* block_table, int32_t max_blocks,
+                                   const int32_t* qo_indptr, const int32_t* kv_lens,
+                                   int32_t num_requests, int32_t total_q, int32_t num_qo_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                                   pkc_dtype dtype, float sm_scale, int32_t causal, void* o,
+                                   float* lse, void* dev_ws, size_t dev_bytes, void* stream);
+
+/*
  * In-place KV append ("Paged attention" page, decode path: the cache is updated in place, and
  * its worked example places each sequence's next token at logical block cache_seqlens[b] / P,
  * slot cache_seqlens[b] % P of the sequence's block-table row).  For every request b, the new

@@ -124,6 +124,8 @@ SIGNATURES = {
     "pkc_prefix_attention_fp8": (_I32, [ctypes.POINTER(PlanInfo), _I32, _P, _P, _P, _F, _F, _I64,
                                         ctypes.POINTER(LevelDev), _I32, _I32, _I32, _I32, _I32, _I32,
                                         _F, _P, _I32, _P, _P, _SZ, _P]),
+    "pkc_batch_prefill_paged": (_I32, [ctypes.POINTER(PlanInfo), _P, _P, _P, _I64, _P, _I32, _P, _P, _I32,
+                                       _I32, _I32, _I32, _I32, _I32, _I32, _F, _I32, _P, _P, _P, _SZ, _P]),
     "pkc_cascade_decode_fp8": (_I32, [ctypes.POINTER(PlanInfo), _P, _P, _P, _F, _F, _I64,
                                       ctypes.POINTER(LevelDev), _I32, _P, _I32, _P, _I32, _I32, _I32,
                                       _I32, _I32, _I32, _F, _P, _P, _P, _SZ, _P]),
@@ -480,6 +482,50 @@ def cascade_decode_fp8(plan_info: PlanInfo, q, k_pool, v_pool, lvl_devs: Sequenc
                                       float(k_scale), float(v_scale), N, arr, len(lvl_devs), _ptr(block_table),
                                       block_table.shape[1], _ptr(suffix_seqlens), B, Hq, Hkv, D, P,
                                       dtype_code(q.dtype), scale, _ptr(out), _ptr(lse), ws, wsn, _stream(dev)))
+    return out, lse
+
+
+def prefill_plan(qo_lens, kv_lens, num_qo_heads, num_kv_heads, head_dim, page_size, level_ctas=0,
+                 level_tile_q=0, enable_split=True, alpha=1, beta=1, workspace: Workspace = None):
+    """Plan of a batch prefill: every query row is one plan request (batch = total_q, no own
+    KV) and one level whose groups are the requests (qo_indptr = cumulative query lengths,
+    kv_lens).  Returns (plan_info, workspace, qo_indptr list)."""
+    qo_lens = [int(x) for x in qo_lens]
+    qo_indptr = [0]
+    for n in qo_lens:
+        qo_indptr.append(qo_indptr[-1] + n)
+    total_q = qo_indptr[-1]
+    params = make_params(total_q, num_qo_heads, num_kv_heads, head_dim, page_size, num_ctas=1,
+                         level_ctas=level_ctas, level_tile_q=level_tile_q, enable_split=enable_split,
+                         alpha=alpha, beta=beta)
+    levels = [{"qo_indptr": qo_indptr, "kv_lens": [int(x) for x in kv_lens]}]
+    if workspace is None:
+        workspace = Workspace(params, levels)
+    info = plan(params, [0] * total_q, levels, workspace=workspace)
+    return info, workspace, qo_indptr
+
+
+def batch_prefill_paged(plan_info: PlanInfo, q, k_pool, v_pool, block_table, qo_indptr, kv_lens, causal=True,
+                        sm_scale=None, out=None, lse=None):
+    """pkc_batch_prefill_paged: ragged queries q [total_q, Hq, D] (rows qo_indptr[b] ..
+    qo_indptr[b+1]-1 belong to request b) over the requests' block-table rows of kv_lens[b]
+    tokens; qo_indptr / kv_lens are int32 device tensors.  Returns (o, lse)."""
+    T, Hq, D = q.shape
+    N, P, Hkv, _ = k_pool.shape
+    dev = q.device
+    B = block_table.shape[0]
+    for t, n in ((block_table, "block_table"), (qo_indptr, "qo_indptr"), (kv_lens, "kv_lens")):
+        _need(t, n, torch.int32, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(T, Hq, dtype=torch.float32, device=dev)
+    scale = 1.0 / math.sqrt(D) if sm_scale is None else float(sm_scale)
+    ws, wsn = _ws_of(plan_info)
+    _check(lib.pkc_batch_prefill_paged(ctypes.byref(plan_info), _ptr(q), _ptr(k_pool), _ptr(v_pool), N,
+                                       _ptr(block_table), block_table.shape[1], _ptr(qo_indptr), _ptr(kv_lens),
+                                       B, T, Hq, Hkv, D, P, dtype_code(q.dtype), scale, 1 if causal else 0,
+                                       _ptr(out), _ptr(lse), ws, wsn, _stream(dev)))
     return out, lse
 
 

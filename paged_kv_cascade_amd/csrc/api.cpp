@@ -170,21 +170,41 @@ pkc::MergePlanParams merge_params(const pkc_plan_info* plan, void* ws, int l0, i
   return m;
 }
 
+// Ragged multi-token queries run as a level whose groups are the requests: their pages come
+// from a dense block table, and the causal mask needs each group's query range and length.
+struct PrefillLevel {
+  const int32_t* block_table;
+  int32_t max_blocks;
+  const int32_t* qo_indptr;
+  const int32_t* kv_lens;
+  int32_t causal;
+};
+
 // FP8 pools (fp8 = true): k_scale folds into the softmax scale, v_scale into the state.
+// With pf, lv is unused and the groups' pages are the rows of pf->block_table.
 pkc_status run_level(const pkc_plan_info* plan, int level, const void* q, const void* k, const void* v,
                      int64_t num_pages, const pkc_level_dev* lv, pkc_dtype dtype, float sm_scale,
                      void* ws, hipStream_t s, bool fp8 = false, float k_scale = 1.f,
-                     float v_scale = 1.f) {
-  if (plan->lvl_groups[level] > 0 && (!lv->kv_page_indptr || !lv->kv_page_indices))
+                     float v_scale = 1.f, const PrefillLevel* pf = nullptr) {
+  if (!pf && plan->lvl_groups[level] > 0 && (!lv->kv_page_indptr || !lv->kv_page_indices))
     return fail(PKC_ERR_INVALID_ARG, "level " + std::to_string(level) + ": NULL page arrays");
   pkc::PrefixParams p{};
   p.q = q;
   p.k = k;
   p.v = v;
   p.num_pages = num_pages;
-  p.page_indptr = lv->kv_page_indptr;
-  p.page_indices = lv->kv_page_indices;
-  p.num_page_indices = lv->num_page_indices;
+  if (pf) {
+    p.page_indptr = nullptr;
+    p.page_indices = pf->block_table;
+    p.table_stride = pf->max_blocks;
+    p.grp_qo_indptr = pf->qo_indptr;
+    p.grp_kv_lens = pf->kv_lens;
+    p.causal = pf->causal;
+  } else {
+    p.page_indptr = lv->kv_page_indptr;
+    p.page_indices = lv->kv_page_indices;
+    p.num_page_indices = lv->num_page_indices;
+  }
   p.hq = plan->num_qo_heads;
   p.hkv = plan->num_kv_heads;
   p.page_size = plan->page_size;
@@ -207,6 +227,11 @@ pkc_status run_level(const pkc_plan_info* plan, int level, const void* q, const 
     const int v = std::atoi(e);
     if (v == 1 || v == 2) streams = v;
   }
+  if (pf && pf->causal)
+    return timed(1, s, "prefix kernel launch", [&] {
+      return pkc::launch_prefill_causal(dtype, plan->head_dim, g, plan->lvl_tile_q[level], streams, p,
+                                        plan->level_ctas, s);
+    });
   return timed(1, s, "prefix kernel launch", [&] {
     return fp8 ? pkc::launch_prefix_fp8(dtype, plan->head_dim, g, plan->lvl_tile_q[level], streams, p,
                                         plan->level_ctas, s)
@@ -504,6 +529,43 @@ pkc_status pkc_prefix_attention_fp8(const pkc_plan_info* plan, int32_t level, co
                      batch, num_qo_heads, num_kv_heads, head_dim, page_size, q_dtype, sm_scale,
                      o_state, o_dtype, lse_state, dev_ws, dev_bytes, stream);
   PKC_TRY_END("pkc_prefix_attention_fp8")
+}
+
+pkc_status pkc_batch_prefill_paged(const pkc_plan_info* plan, const void* q, const void* k_pool,
+                                   const void* v_pool, int64_t num_pages,
+                                   const int32_t* block_table, int32_t max_blocks,
+                                   const int32_t* qo_indptr, const int32_t* kv_lens,
+                                   int32_t num_requests, int32_t total_q, int32_t num_qo_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                                   pkc_dtype dtype, float sm_scale, int32_t causal, void* o,
+                                   float* lse, void* dev_ws, size_t dev_bytes, void* stream) {
+  PKC_TRY_BEGIN
+  pkc_status st = check_shapes(total_q, num_qo_heads, num_kv_heads, head_dim, page_size, dtype, sm_scale);
+  if (st != PKC_OK) return st;
+  if ((st = check_prefix_supported(dtype, page_size)) != PKC_OK) return st;
+  if (!plan) return fail(PKC_ERR_INVALID_ARG, "batch prefill needs a plan");
+  if (num_requests < 0) return fail(PKC_ERR_INVALID_ARG, "num_requests < 0");
+  if ((st = check_plan(plan, total_q, num_qo_heads, num_kv_heads, head_dim, page_size, dev_ws, dev_bytes)) != PKC_OK)
+    return st;
+  if (plan->num_levels != 1 || plan->lvl_groups[0] != num_requests || plan->dec_items != 0)
+    return fail(PKC_ERR_PLAN_MISMATCH,
+                "batch prefill needs a plan with batch = total_q, one level whose groups are the "
+                "requests and no decode items");
+  if (total_q == 0) return PKC_OK;
+  if (!q || !k_pool || !v_pool || !o || !lse || !block_table || !qo_indptr || !kv_lens)
+    return fail(PKC_ERR_INVALID_ARG, "NULL pointer");
+  if (num_pages < 1 || max_blocks < 1)
+    return fail(PKC_ERR_INVALID_ARG, "num_pages and max_blocks must be >= 1");
+  if ((int64_t)max_blocks * page_size > INT32_MAX || (int64_t)max_blocks * num_requests > INT32_MAX)
+    return fail(PKC_ERR_INVALID_ARG, "block table too large for int32 offsets");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const PrefillLevel pf{block_table, max_blocks, qo_indptr, kv_lens, causal ? 1 : 0};
+  if ((st = run_level(plan, 0, q, k_pool, v_pool, num_pages, nullptr, dtype, sm_scale, dev_ws, s, false,
+                      1.f, 1.f, &pf)) != PKC_OK)
+    return st;
+  pkc::MergePlanParams m = merge_params(plan, dev_ws, 0, 1, false, o, lse);
+  return timed(2, s, "merge kernel launch", [&] { return pkc::launch_merge_plan(dtype, head_dim, m, s); });
+  PKC_TRY_END("pkc_batch_prefill_paged")
 }
 
 pkc_status pkc_merge_states(const void* o_states, pkc_dtype in_dtype, const float* lse_states,

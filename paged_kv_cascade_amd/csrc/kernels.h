@@ -56,6 +56,14 @@ struct PrefixParams {
   float* st_lse;
   const int32_t* indptr;        // [#CTA + 1]
   const int32_t* items;
+  // Ragged multi-token queries: page_indptr == nullptr selects a dense block table (group g's
+  // pages are page_indices[g * table_stride ..]); the causal kernel masks query i of group g
+  // (its queries are rows grp_qo_indptr[g] ..) to tokens t <= grp_kv_lens[g] - l_q(g) + i
+  // (causal records which kernel the host launched).
+  const int32_t* grp_qo_indptr;
+  const int32_t* grp_kv_lens;
+  int32_t table_stride;
+  int32_t causal;
 };
 
 // Plan-driven merge: request b merges merge_rows[merge_ptr[b*NL2 + l0] .. merge_ptr[b*NL2 + l1]).
@@ -107,6 +115,9 @@ hipError_t launch_decode_fp8(pkc_dtype q_dt, int head_dim, int group, int waves,
 // 4-wave halves take alternate tiles of an item and merge at its end (one per compute unit).
 hipError_t launch_prefix(pkc_dtype dt, int head_dim, int group, int tile_q, int streams,
                          const PrefixParams& p, int grid_x, hipStream_t s);
+// The level kernel with the causal mask (ragged multi-token queries, fp16 / bf16 pools).
+hipError_t launch_prefill_causal(pkc_dtype dt, int head_dim, int group, int tile_q, int streams,
+                                 const PrefixParams& p, int grid_x, hipStream_t s);
 // The same over OCP FP8 E4M3 pools; q_dt (fp16 or bf16) is the query and operand type.
 hipError_t launch_prefix_fp8(pkc_dtype q_dt, int head_dim, int group, int tile_q, int streams,
                              const PrefixParams& p, int grid_x, hipStream_t s);

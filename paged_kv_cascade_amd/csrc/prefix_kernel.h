@@ -127,9 +127,17 @@ __device__ __forceinline__ u4_t dma_rsrc(const void* base, int32_t bytes) {
 // (M0 holds the LDS address).  Written as an asm statement, so the compiler neither moves
 // memory accesses across it nor adds waits of its own for it: the ring below orders these
 // loads against the LDS reads with explicit vector-memory waits and barriers.
-__device__ __forceinline__ void load_lds16(u4_t r, char* lds, int32_t voff, int32_t soff) {
-  const uint32_t m0 = (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)lds);
-  __asm__ volatile("buffer_load_dwordx4 %0, %1, %2 offen nt lds" ::"v"(voff), "s"(r), "s"(soff), "{m0}"(m0)
+// m0 is the LDS byte address.  The descriptor and the scalar offset are wave-uniform by
+// construction; readfirstlane states that to the compiler (a no-op on scalar registers).
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)p);
+}
+__device__ __forceinline__ void load_lds16(u4_t r, uint32_t m0, int32_t voff, int32_t soff) {
+  u4_t rs;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) rs[i] = (uint32_t)__builtin_amdgcn_readfirstlane((int)r[i]);
+  const int32_t ss = __builtin_amdgcn_readfirstlane(soff);
+  __asm__ volatile("buffer_load_dwordx4 %0, %1, %2 offen nt lds" ::"v"(voff), "s"(rs), "s"(ss), "{m0}"(m0)
                    : "memory");
 }
 
@@ -206,8 +214,9 @@ __device__ __forceinline__ bool unrolled_steps(F& f, int j, int n) {
 
 }  // namespace prefix_detail
 
-// F8: the K / V pools hold OCP E4M3 codes (T is the query and operand type).
-template <typename T, int D, int G, int NS, bool F8>
+// F8: the K / V pools hold OCP E4M3 codes (T is the query and operand type).  CAUSAL: ragged
+// multi-token queries with the causal mask (each group's queries are its last tokens).
+template <typename T, int D, int G, int NS, bool F8, bool CAUSAL = false>
 __global__ __launch_bounds__(64 * prefix_detail::kWavesPerStream * NS, NS == 1 ? 2 : 1) void prefix_kernel(const PrefixParams p) {
   using namespace prefix_detail;
   constexpr int ES = 2;
@@ -286,11 +295,21 @@ __global__ __launch_bounds__(64 * prefix_detail::kWavesPerStream * NS, NS == 1 ?
     const int32_t* rec = p.items + 8 * (int64_t)it;
     const int grp = scalar_load(rec);
     const int q0 = scalar_load(rec + 1), nq = scalar_load(rec + 2);
-    const int kb = scalar_load(rec + 3), ke = scalar_load(rec + 4), srow = scalar_load(rec + 5);
+    const int kb = scalar_load(rec + 3), srow = scalar_load(rec + 5);
+    int ke = scalar_load(rec + 4);
     const int nrows = nq * G;
-    const int pbeg = scalar_load(p.page_indptr + grp);
-    const int npages_grp = scalar_load(p.page_indptr + grp + 1) - pbeg;
+    const int pbeg = p.page_indptr ? scalar_load(p.page_indptr + grp) : grp * p.table_stride;
+    const int npages_grp = p.page_indptr ? scalar_load(p.page_indptr + grp + 1) - pbeg : p.table_stride;
     const int32_t* pages = p.page_indices + pbeg;
+    // Causal mask: query i of the item (rows i * G ..) sees tokens t <= lim0 + i, where lim0
+    // is the limit of the item's first query (its queries are the group's last l_q tokens).
+    // Tokens past the last query's limit are not visited at all.
+    int lim0 = 0;
+    if constexpr (CAUSAL) {
+      const int gq0 = scalar_load(p.grp_qo_indptr + grp), gq1 = scalar_load(p.grp_qo_indptr + grp + 1);
+      lim0 = scalar_load(p.grp_kv_lens + grp) - (gq1 - gq0) + (q0 - gq0);
+      ke = min(ke, lim0 + nq);
+    }
     const int t0 = (kb / kTK) * kTK;
     // A group without pages holds no tokens (its kv_len is then a caller error).
     const int ntiles = (ke > kb && npages_grp > 0) ? (ke - t0 + kTK - 1) / kTK : 0;
@@ -302,7 +321,10 @@ __global__ __launch_bounds__(64 * prefix_detail::kWavesPerStream * NS, NS == 1 ?
     // the list; a group past the list is rejected when the tile is issued).  They are fetched
     // one step before use, so their latency hides behind a tile's arithmetic.
     struct Pg { int e0, e1; };
-    auto fetch = [&](int tt) -> Pg {
+    // Every lambda here is forced inline: one left out of line takes the kernel parameters by
+    // reference, which moves them to scratch memory and every address computation with them to
+    // the vector unit.
+    auto fetch = [&](int tt) __attribute__((always_inline)) -> Pg {
       const int rb = t0 + tt * kTK + 8 * wq;
       Pg r;
       r.e0 = scalar_load(pages + min(rb >> shift, last_page));
@@ -312,7 +334,8 @@ __global__ __launch_bounds__(64 * prefix_detail::kWavesPerStream * NS, NS == 1 ?
 
     // Loads of tile tt into slot `dst` and the slot's valid-row byte of this wave; a tile past
     // the end reads nothing (zeros) and marks no row valid.
-    auto issue = [&](int tt, const Pg& pg, char* dst, uint32_t* flag) {
+    // dst is the LDS byte address of the slot.
+    auto issue = [&](int tt, const Pg& pg, uint32_t dst, uint32_t* flag) __attribute__((always_inline)) {
       const int rb = t0 + tt * kTK + 8 * wq;      // token of the wave's first row
       const bool in_tiles = tt < ntiles;
       const int e[2] = {pg.e0, pg.e1};
@@ -332,8 +355,8 @@ __global__ __launch_bounds__(64 * prefix_detail::kWavesPerStream * NS, NS == 1 ?
       for (int i = 0; i < NI; ++i) {
         const int t = t0 + tt * kTK + lrow[i];
         const int32_t off = ((t >= kb) & (t < ke)) ? voff[i] : kOffsetNone;
-        char* dk = dst + (8 * wq + 4 * i) * RBG;
-        char* dv = dk + STBG;
+        const uint32_t dk = dst + (8 * wq + 4 * i) * RBG;
+        const uint32_t dv = dk + STBG;
         if constexpr (RBG == 256) {
           load_lds16(rk[i], dk, off, soff[i]);
           load_lds16(rw[i], dv, off, soff[i]);
@@ -366,7 +389,20 @@ __global__ __launch_bounds__(64 * prefix_detail::kWavesPerStream * NS, NS == 1 ?
     float m_run[2] = {kNegInf, kNegInf};
     float l_run[2] = {0.f, 0.f};
 
-    auto compute = [&](const char* ks_s, const char* vs_s, uint32_t mask) {
+    // Per lane and query tile nt: the causal limit of the lane's query column minus the offset
+    // 4 * lg of its first S^T row, so that element (mt, i) of a tile starting at token tok0 is
+    // masked when tok0 + 16 mt + i > cbase[nt].  (A compile-time switch rather than a runtime
+    // flag: the kernel's scalar registers are nearly all taken, and the extra live values of a
+    // runtime branch push the loads' buffer descriptors out of them.)
+    int cbase[2] = {0, 0};
+    int vtok0 = 0;   // first token of the stream's first tile, in a vector register
+    if constexpr (CAUSAL) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) cbase[nt] = lim0 + (wq * kRowsPerWave + nt * 16 + l16) / G - 4 * lg;
+      vtok0 = t0 + stream * kTK;
+      __asm__ volatile("" : "+v"(vtok0));
+    }
+    auto compute = [&](const char* ks_s, const char* vs_s, uint32_t mask, int tok0) __attribute__((always_inline)) {
       if (!wave_active) return;
       // S^T[mt][nt]: tokens mt*16 + 4*lg + i, query column nt*16 + l16.
       f4_t s[2][2];
@@ -394,7 +430,27 @@ __global__ __launch_bounds__(64 * prefix_detail::kWavesPerStream * NS, NS == 1 ?
             s[mt][1][i] = v ? s[mt][1][i] : kNegInf;
           }
       }
+      // Causal mask, on tiles reaching past the smallest limit of the wave's queries.
+      if constexpr (CAUSAL) {
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+            {
+              // Branch-free select on the vector unit (all-ones sign mask, bitfield insert), so
+              // the comparison needs no lane-mask registers.
+              const uint32_t neg = (uint32_t)((cbase[nt] - (tok0 + mt * 16 + i)) >> 31);
+              s[mt][nt][i] = __uint_as_float((neg & __float_as_uint(kNegInf)) | (~neg & __float_as_uint(s[mt][nt][i])));
+            }
+      }
       V16 pb[2];   // P^T operands per query tile nt (the tile's 32 tokens are one step)
+      // bf16 weights go to the matrix cores as two bf16 terms (rounded weight and residual):
+      // a single bf16 weight carries a relative error up to 2^-9, which over a few tokens with
+      // values of opposite sign exceeds the output tolerance.  fp16 weights (2^-12) need not.
+      constexpr bool kSplitP = std::is_same<T, BF16>::value;
+      V16 pl[2];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         float mx = kNegInf;
@@ -435,6 +491,16 @@ __global__ __launch_bounds__(64 * prefix_detail::kWavesPerStream * NS, NS == 1 ?
         pb[nt].w[1] = Mfma<T>::pack(pr[0][2], pr[0][3]);
         pb[nt].w[2] = Mfma<T>::pack(pr[1][0], pr[1][1]);
         pb[nt].w[3] = Mfma<T>::pack(pr[1][2], pr[1][3]);
+        if constexpr (kSplitP) {
+          // bf16 keeps 8 bits of each weight; the residual weight - bf16(weight), rounded to
+          // bf16 again, makes the product exact to about 2^-17 relative.
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const uint32_t w = pb[nt].w[k];
+            const float* src = pr[k >> 1] + 2 * (k & 1);
+            pl[nt].w[k] = Mfma<T>::pack(src[0] - __uint_as_float(w << 16), src[1] - __uint_as_float(w & 0xffff0000u));
+          }
+        }
       }
       // O^T[dm][nt] += V^T * P^T over the tile's 32 tokens.  Lane group g supplies contraction
       // elements 8g .. 8g+7 = tokens 16h + 4g + i (h = 0, 1; i = 0..3), the order of the S^T
@@ -453,6 +519,10 @@ __global__ __launch_bounds__(64 * prefix_detail::kWavesPerStream * NS, NS == 1 ?
         }
         oacc[dm][0] = Mfma<T>::run(a, pb[0], oacc[dm][0]);
         oacc[dm][1] = Mfma<T>::run(a, pb[1], oacc[dm][1]);
+        if constexpr (kSplitP) {
+          oacc[dm][0] = Mfma<T>::run(a, pl[0], oacc[dm][0]);
+          oacc[dm][1] = Mfma<T>::run(a, pl[1], oacc[dm][1]);
+        }
       }
     };
 
@@ -476,7 +546,7 @@ __global__ __launch_bounds__(64 * prefix_detail::kWavesPerStream * NS, NS == 1 ?
       Pg pg = fetch(stream);
 #pragma unroll
       for (int j = 0; j < AHEAD; ++j) {
-        issue(stream + j * NS, pg, sring + j * SLOT, sfl + j);
+        issue(stream + j * NS, pg, lds_addr(sring) + j * SLOT, sfl + j);
         pg = fetch(stream + (j + 1) * NS);
       }
       // The Q loads precede the prologue's AHEAD * NDMA loads.
@@ -508,7 +578,7 @@ __global__ __launch_bounds__(64 * prefix_detail::kWavesPerStream * NS, NS == 1 ?
       // wave reads stage S any more: the stream's tile j + AHEAD refills it.  The valid-row
       // word of stage S is read before the barrier (its bytes were written at step j - AHEAD,
       // before the barrier of step j-1), since the refill rewrites it.
-      auto step = [&](auto stage_c, int j) {
+      auto step = [&](auto stage_c, int j) __attribute__((always_inline)) {
         constexpr int S = decltype(stage_c)::value;
         constexpr int N = (S + AHEAD) % STAGES;
         const int tt = stream + j * NS;
@@ -535,11 +605,20 @@ __global__ __launch_bounds__(64 * prefix_detail::kWavesPerStream * NS, NS == 1 ?
         }
         ring_barrier();
         if constexpr (!F8) mask = sfl[S];   // the same on every lane; first needed after S^T
-        issue(tt + AHEAD * NS, pg, sring + N * SLOT, sfl + N);
+        issue(tt + AHEAD * NS, pg, lds_addr(sring) + N * SLOT, sfl + N);
         pg = fetch(tt + (AHEAD + 1) * NS);
         if (tt < ntiles) {
-          if constexpr (F8) compute(cb, cb + STB, mask);
-          else compute(sring + S * SLOT, sring + S * SLOT + STB, mask);
+          // The tile's first token, for the causal mask, is formed on the vector unit from
+          // opaque copies: shared with the scalar address arithmetic of the loads, the compiler
+          // would otherwise move that arithmetic to the vector unit as well.
+          int tok0 = 0;
+          if constexpr (CAUSAL) {
+            int jv = j;
+            __asm__ volatile("" : "+v"(jv));
+            tok0 = vtok0 + jv * (NS * kTK);
+          }
+          if constexpr (F8) compute(cb, cb + STB, mask, tok0);
+          else compute(sring + S * SLOT, sring + S * SLOT + STB, mask, tok0);
         }
       };
       for (int j = 0; j < nsteps; j += STAGES)
@@ -622,39 +701,40 @@ __global__ __launch_bounds__(64 * prefix_detail::kWavesPerStream * NS, NS == 1 ?
   }
 }
 
-template <typename T, int D, int G, bool F8>
+template <typename T, int D, int G, bool F8, bool CAUSAL>
 inline hipError_t launch_prefix_t(int streams, const PrefixParams& p, int grid_x, hipStream_t s) {
   const dim3 grid(grid_x, p.hkv);
   constexpr int W = prefix_detail::kWavesPerStream;
   if (streams == 2)
-    hipLaunchKernelGGL((prefix_kernel<T, D, G, 2, F8>), grid, dim3(128 * W), 0, s, p);
+    hipLaunchKernelGGL((prefix_kernel<T, D, G, 2, F8, CAUSAL>), grid, dim3(128 * W), 0, s, p);
   else
-    hipLaunchKernelGGL((prefix_kernel<T, D, G, 1, F8>), grid, dim3(64 * W), 0, s, p);
+    hipLaunchKernelGGL((prefix_kernel<T, D, G, 1, F8, CAUSAL>), grid, dim3(64 * W), 0, s, p);
   return hipGetLastError();
 }
 
-template <typename T, int D, bool F8>
+template <typename T, int D, bool F8, bool CAUSAL>
 inline hipError_t launch_prefix_g(int group, int streams, const PrefixParams& p, int grid_x,
                                   hipStream_t s) {
   switch (group) {
-    case 1: return launch_prefix_t<T, D, 1, F8>(streams, p, grid_x, s);
-    case 2: return launch_prefix_t<T, D, 2, F8>(streams, p, grid_x, s);
-    case 4: return launch_prefix_t<T, D, 4, F8>(streams, p, grid_x, s);
-    case 8: return launch_prefix_t<T, D, 8, F8>(streams, p, grid_x, s);
+    case 1: return launch_prefix_t<T, D, 1, F8, CAUSAL>(streams, p, grid_x, s);
+    case 2: return launch_prefix_t<T, D, 2, F8, CAUSAL>(streams, p, grid_x, s);
+    case 4: return launch_prefix_t<T, D, 4, F8, CAUSAL>(streams, p, grid_x, s);
+    case 8: return launch_prefix_t<T, D, 8, F8, CAUSAL>(streams, p, grid_x, s);
   }
   return hipErrorInvalidValue;
 }
 
-// Launches the level kernel for 16-bit operand type T over 16-bit (F8 = false) or E4M3 pools.
-template <typename T, bool F8>
+// Launches the level kernel for 16-bit operand type T over 16-bit (F8 = false) or E4M3 pools,
+// with the causal mask of ragged multi-token queries when CAUSAL.
+template <typename T, bool F8, bool CAUSAL = false>
 inline hipError_t launch_prefix_d(int head_dim, int group, int tile_q, int streams,
                                   const PrefixParams& p, int grid_x, hipStream_t s) {
   using namespace prefix_detail;
   if (grid_x <= 0) return hipSuccess;
   if (tile_q * group > kWavesPerStream * kRowsPerWave) return hipErrorInvalidValue;
   if (p.page_size < 4 || (streams != 1 && streams != 2)) return hipErrorInvalidValue;
-  if (head_dim == 64) return launch_prefix_g<T, 64, F8>(group, streams, p, grid_x, s);
-  if (head_dim == 128) return launch_prefix_g<T, 128, F8>(group, streams, p, grid_x, s);
+  if (head_dim == 64) return launch_prefix_g<T, 64, F8, CAUSAL>(group, streams, p, grid_x, s);
+  if (head_dim == 128) return launch_prefix_g<T, 128, F8, CAUSAL>(group, streams, p, grid_x, s);
   return hipErrorInvalidValue;
 }
 
