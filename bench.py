@@ -17,7 +17,8 @@ back, and with the last-level cache evicted before each run); the same step with
 cascade (every request reads the shared prefix through its own full page list) with the
 largest output difference between the two; the in-place append of one token per request; and
 the LLaMA2-7B decode shape (64 x 4096 tokens) over fp16 pools and over FP8 E4M3 pools; and
-the same cascade step over FP8 E4M3 pools.
+the same cascade step over FP8 E4M3 pools; and a causal prefill of ragged multi-token queries
+(matrix-core TFLOP/s).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 """
@@ -309,6 +310,55 @@ def fp8_cascade_timing(api, workloads, w, step, info, runs=50):
             "alg_GBps": round(nbytes / us / 1e3, 1), "kernel_avg_us": kern, "runs": runs}
 
 
+def prefill_timing(api, runs=10):
+    """Ragged multi-token queries at LLaMA2-7B head shape: 8 requests of 2048 new tokens over
+    2048-token sequences (self-attention prefill), causal, fp16, page 16, level #CTA 64.  The
+    level kernel is matrix-core work: reported in TFLOP/s of the visible (query, key) pairs,
+    4 * D * Hq flops each, against the dense fp16 peak."""
+    import torch
+    B, lq, lkv, H, D, P = 8, 2048, 2048, 32, 128, 16
+    npg = lkv // P
+    g = torch.Generator().manual_seed(1006)
+    bt = torch.randperm(B * npg, generator=g).to(torch.int32).view(B, npg).contiguous().cuda()
+    dg = torch.Generator(device="cuda").manual_seed(1007)
+    q = (torch.randn(B * lq, H, D, generator=dg, device="cuda") * 0.5).half()
+    k = (torch.randn(B * npg, P, H, D, generator=dg, device="cuda") * 0.5).half()
+    v = (torch.randn(B * npg, P, H, D, generator=dg, device="cuda") * 0.5).half()
+    qi = torch.arange(0, (B + 1) * lq, lq, dtype=torch.int32, device="cuda")
+    kvl = torch.full((B,), lkv, dtype=torch.int32, device="cuda")
+    info, ws, _ = api.prefill_plan([lq] * B, [lkv] * B, H, H, D, P, level_ctas=64)
+    out = torch.empty_like(q)
+    lse = torch.empty(B * lq, H, dtype=torch.float32, device="cuda")
+
+    def run():
+        api.batch_prefill_paged(info, q, k, v, bt, qi, kvl, causal=True, out=out, lse=lse)
+
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    api.timing_reset()
+    api.timing_enable(True)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(runs):
+        run()
+    b.record()
+    torch.cuda.synchronize()
+    n, ms = api.timing_read(api.KIND_PREFIX)
+    nm, msm = api.timing_read(api.KIND_MERGE_PLAN)
+    api.timing_enable(False)
+    pairs = B * lq * (lq + 1) // 2          # visible (query, key) pairs, causal
+    flops = 4.0 * D * H * pairs
+    kus = 1e3 * ms / max(1, n)
+    res = {"workload": f"prefill_causal_b{B}_q{lq}_kv{lkv}_h{H}_d{D}_p{P}_f16", "us_per_run": round(1e3 * a.elapsed_time(b) / runs, 1),
+           "level_kernel_us": round(kus, 1), "merge_us": round(1e3 * msm / max(1, nm), 1),
+           "flops": flops, "level_kernel_TFLOPs": round(flops / kus / 1e6, 1),
+           "frac_of_fp16_mfma_peak": round(flops / kus / 1e6 / 2500.0, 4)}
+    del q, k, v, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def append_timing(api, w, runs=50):
     """Appending one new K/V token per request (the step before decode) for the cascade
     workload's batch and head shape: 128 requests with 256 cached suffix tokens each and a
@@ -446,6 +496,7 @@ def main():
     nonc["cascade_speedup"] = round(nonc["ms_per_step"] / (dist_warm["p50"] * 1e-3), 2)
     app = append_timing(api, w)
     fp8c = fp8_cascade_timing(api, workloads, w, step, info)
+    pre = prefill_timing(api)
     fp8 = fp8_decode_comparison(api, workloads)
 
     # The device's achievable read rate: one nontemporal 16-byte-load stream over 2 GiB.
@@ -495,6 +546,7 @@ def main():
         "append_kv": app,
         "fp8_kv_decode": fp8,
         "fp8_kv_cascade": fp8c,
+        "prefill": pre,
         "kernel_source_hash": src_hash,
     }
     line["cpu_baseline"] = cpu
