@@ -326,7 +326,7 @@ def prefill_timing(api, runs=10):
     v = (torch.randn(B * npg, P, H, D, generator=dg, device="cuda") * 0.5).half()
     qi = torch.arange(0, (B + 1) * lq, lq, dtype=torch.int32, device="cuda")
     kvl = torch.full((B,), lkv, dtype=torch.int32, device="cuda")
-    info, ws, _ = api.prefill_plan([lq] * B, [lkv] * B, H, H, D, P, level_ctas=64)
+    info, ws, _ = api.prefill_plan([lq] * B, [lkv] * B, H, H, D, P, level_ctas=64, causal=True)
     out = torch.empty_like(q)
     lse = torch.empty(B * lq, H, dtype=torch.float32, device="cuda")
 

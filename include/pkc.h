@@ -124,11 +124,16 @@ typedef struct pkc_plan_params {
 
 /* Host description of one cascade level: groups of consecutive requests sharing a KV run.
  * Group g holds requests qo_indptr[g] <= b < qo_indptr[g+1] (0 <= qo_indptr[0],
- * non-decreasing, qo_indptr[G] <= B) and attends over kv_lens[g] tokens. */
+ * non-decreasing, qo_indptr[G] <= B) and attends over kv_lens[g] tokens.  causal != 0 (ragged
+ * multi-token queries, pkc_batch_prefill_paged with causal): group g's requests are the last
+ * l = qo_indptr[g+1] - qo_indptr[g] tokens of its sequence, so a query tile whose last query is
+ * the i-th of the group (0-based) needs only tokens [0, kv_lens[g] - l + i + 1); the plan
+ * chunks and weighs that extent instead of kv_lens[g]. */
 typedef struct pkc_level_host {
   int32_t num_groups;
   const int32_t* qo_indptr; /* [G+1] host */
   const int32_t* kv_lens;   /* [G] host, tokens */
+  int32_t causal;
 } pkc_level_host;
 
 /* Device description of one cascade level (block-sparse row view of the KV cache, paper
@@ -179,6 +184,7 @@ typedef struct pkc_plan_info {
   int64_t off_state_lse;   /* fp32 [state_rows, Hq] */
   int64_t dev_bytes;       /* device workspace bytes this plan uses */
   uint64_t dev_ws;         /* address of the workspace the plan was copied to (0: host-only) */
+  int32_t lvl_causal[PKC_MAX_LEVELS]; /* 1: the level was planned with causal tile extents */
 } pkc_plan_info;
 
 /*

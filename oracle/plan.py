@@ -70,9 +70,19 @@ def ceil_div(a: int, b: int) -> int:
     return -(-a // b)
 
 
+def tile_extent(lqo, lkv, tile_q, j, causal):
+    """KV tokens query tile j of a request needs: all l_kv, or with the causal mask (the
+    request's l_qo queries are its last tokens) the tokens its last query sees, reading R28:
+    l_kv - l_qo + min((j + 1) T_q, l_qo), clamped to [0, l_kv]."""
+    if not causal:
+        return lkv
+    return min(lkv, max(0, lkv - lqo + min((j + 1) * tile_q, lqo)))
+
+
 def lpt_plan(qo_lens, kv_lens, tile_q, num_ctas, alpha=1, beta=1,
-             chunk_align=1, enable_split=True) -> StagePlan:
-    """Steps 1-7 of the scheduler for one stage."""
+             chunk_align=1, enable_split=True, causal=False) -> StagePlan:
+    """Steps 1-7 of the scheduler for one stage.  With ``causal`` every query tile's KV is
+    its causal extent (``tile_extent``) in steps 3 and 4."""
     if tile_q < 1 or num_ctas < 1 or chunk_align < 1:
         raise ValueError("tile_q, num_ctas and chunk_align must be >= 1")
     if alpha < 0 or beta < 0:
@@ -84,7 +94,8 @@ def lpt_plan(qo_lens, kv_lens, tile_q, num_ctas, alpha=1, beta=1,
 
     # Step 3: maximum chunk length.
     if enable_split:
-        total = sum(ceil_div(lqo, tile_q) * lkv for lqo, lkv in zip(qo_lens, kv_lens))
+        total = sum(tile_extent(lqo, lkv, tile_q, j, causal)
+                    for lqo, lkv in zip(qo_lens, kv_lens) for j in range(ceil_div(lqo, tile_q)))
         L = max(1, ceil_div(total, num_ctas))
     else:
         L = max([1] + kv_lens)
@@ -95,8 +106,9 @@ def lpt_plan(qo_lens, kv_lens, tile_q, num_ctas, alpha=1, beta=1,
     for i, (lqo, lkv) in enumerate(zip(qo_lens, kv_lens)):
         for j in range(ceil_div(lqo, tile_q)):
             lq = min(tile_q, lqo - j * tile_q)
-            for c in range(ceil_div(lkv, L)):
-                items.append(WorkItem(len(items), i, j, lq, c * L, min((c + 1) * L, lkv)))
+            ext = tile_extent(lqo, lkv, tile_q, j, causal)
+            for c in range(ceil_div(ext, L)):
+                items.append(WorkItem(len(items), i, j, lq, c * L, min((c + 1) * L, ext)))
 
     # Step 5: longest first (stable).
     order = [it.w for it in sorted(items, key=lambda it: -it.length)]
@@ -169,7 +181,7 @@ def cascade_plan(batch, levels, suffix_kv_lens, num_ctas, level_ctas,
         qi = [int(x) for x in lv["qo_indptr"]]
         qo_lens = [qi[g + 1] - qi[g] for g in range(len(qi) - 1)]
         st = lpt_plan(qo_lens, lv["kv_lens"], level_tile_q[li], level_ctas, alpha,
-                      beta, chunk_align, enable_split)
+                      beta, chunk_align, enable_split, causal=bool(lv.get("causal", False)))
         assign_slots(st, lambda r: False)
         lvl_plans.append(st)
 

@@ -47,7 +47,7 @@ class PlanParams(ctypes.Structure):
 
 class LevelHost(ctypes.Structure):
     _fields_ = [("num_groups", ctypes.c_int32), ("qo_indptr", ctypes.POINTER(ctypes.c_int32)),
-                ("kv_lens", ctypes.POINTER(ctypes.c_int32))]
+                ("kv_lens", ctypes.POINTER(ctypes.c_int32)), ("causal", ctypes.c_int32)]
 
 
 class LevelDev(ctypes.Structure):
@@ -77,7 +77,7 @@ class PlanInfo(ctypes.Structure):
                 ("off_req_flags", ctypes.c_int64), ("off_req_levels", ctypes.c_int64),
                 ("int_bytes", ctypes.c_int64),
                 ("off_state_o", ctypes.c_int64), ("off_state_lse", ctypes.c_int64),
-                ("dev_bytes", ctypes.c_int64), ("dev_ws", ctypes.c_uint64)]
+                ("dev_bytes", ctypes.c_int64), ("dev_ws", ctypes.c_uint64), ("lvl_causal", _L8)]
 
 
 _P = ctypes.c_void_p
@@ -215,6 +215,7 @@ class _Levels:
             self.arr[i].num_groups = len(lv["qo_indptr"]) - 1
             self.arr[i].qo_indptr = ctypes.cast(qi, ctypes.POINTER(ctypes.c_int32))
             self.arr[i].kv_lens = ctypes.cast(kl, ctypes.POINTER(ctypes.c_int32)) if kl is not None else None
+            self.arr[i].causal = 1 if lv.get("causal") else 0
         self.n = len(levels)
 
 
@@ -486,10 +487,12 @@ def cascade_decode_fp8(plan_info: PlanInfo, q, k_pool, v_pool, lvl_devs: Sequenc
 
 
 def prefill_plan(qo_lens, kv_lens, num_qo_heads, num_kv_heads, head_dim, page_size, level_ctas=0,
-                 level_tile_q=0, enable_split=True, alpha=1, beta=1, workspace: Workspace = None):
+                 level_tile_q=0, enable_split=True, alpha=1, beta=1, causal=True,
+                 workspace: Workspace = None):
     """Plan of a batch prefill: every query row is one plan request (batch = total_q, no own
     KV) and one level whose groups are the requests (qo_indptr = cumulative query lengths,
-    kv_lens).  Returns (plan_info, workspace, qo_indptr list)."""
+    kv_lens; causal: tiles weighed by the KV their last query sees).  Returns (plan_info,
+    workspace, qo_indptr list)."""
     qo_lens = [int(x) for x in qo_lens]
     qo_indptr = [0]
     for n in qo_lens:
@@ -498,7 +501,7 @@ def prefill_plan(qo_lens, kv_lens, num_qo_heads, num_kv_heads, head_dim, page_si
     params = make_params(total_q, num_qo_heads, num_kv_heads, head_dim, page_size, num_ctas=1,
                          level_ctas=level_ctas, level_tile_q=level_tile_q, enable_split=enable_split,
                          alpha=alpha, beta=beta)
-    levels = [{"qo_indptr": qo_indptr, "kv_lens": [int(x) for x in kv_lens]}]
+    levels = [{"qo_indptr": qo_indptr, "kv_lens": [int(x) for x in kv_lens], "causal": bool(causal)}]
     if workspace is None:
         workspace = Workspace(params, levels)
     info = plan(params, [0] * total_q, levels, workspace=workspace)

@@ -551,6 +551,10 @@ pkc_status pkc_batch_prefill_paged(const pkc_plan_info* plan, const void* q, con
     return fail(PKC_ERR_PLAN_MISMATCH,
                 "batch prefill needs a plan with batch = total_q, one level whose groups are the "
                 "requests and no decode items");
+  if (plan->lvl_causal[0] != (causal ? 1 : 0))
+    return fail(PKC_ERR_PLAN_MISMATCH,
+                "the plan's level was built with a different causal flag (a causal plan covers "
+                "only the tokens each tile's queries see)");
   if (total_q == 0) return PKC_OK;
   if (!q || !k_pool || !v_pool || !o || !lse || !block_table || !qo_indptr || !kv_lens)
     return fail(PKC_ERR_INVALID_ARG, "NULL pointer");

@@ -40,16 +40,23 @@ namespace pkc {
 
 pkc_status lpt_plan(const int32_t* qo_lens, const int32_t* kv_lens, int32_t n, int32_t tile_q,
                     int32_t ctas, int64_t alpha, int64_t beta, int32_t chunk_align,
-                    bool enable_split, Stage* out) {
+                    bool enable_split, Stage* out, bool causal) {
   if (tile_q < 1 || ctas < 1 || chunk_align < 1 || n < 0)
     return fail(PKC_ERR_INVALID_ARG, "plan: tile_q, ctas and chunk_align must be >= 1");
   if (alpha < 0 || beta < 0) return fail(PKC_ERR_INVALID_ARG, "plan: alpha, beta must be >= 0");
   if (n > 0 && kv_lens == nullptr) return fail(PKC_ERR_INVALID_ARG, "plan: kv_lens is NULL");
   auto lqo = [&](int32_t i) -> int64_t { return qo_lens ? qo_lens[i] : 1; };
+  // KV extent of query tile j of request i: all of it, or with the causal mask the tokens
+  // its last query sees (the request's queries are its last l_qo tokens).
+  auto extent = [&](int32_t i, int64_t j) -> int64_t {
+    if (!causal) return kv_lens[i];
+    const int64_t last = std::min<int64_t>((j + 1) * tile_q, lqo(i));   // queries before the end
+    return std::min<int64_t>(kv_lens[i], std::max<int64_t>(0, (int64_t)kv_lens[i] - lqo(i) + last));
+  };
   int64_t total = 0, longest = 0;
   for (int32_t i = 0; i < n; ++i) {
     if (lqo(i) < 0 || kv_lens[i] < 0) return fail(PKC_ERR_INVALID_ARG, "plan: negative length");
-    total += ceil_div(lqo(i), tile_q) * (int64_t)kv_lens[i];
+    for (int64_t j = 0; j < ceil_div(lqo(i), tile_q); ++j) total += extent(i, j);
     longest = std::max<int64_t>(longest, kv_lens[i]);
   }
   // Step 3: maximum KV chunk length.
@@ -67,14 +74,15 @@ pkc_status lpt_plan(const int32_t* qo_lens, const int32_t* kv_lens, int32_t n, i
     const int64_t tiles = ceil_div(lqo(i), tile_q);
     for (int64_t j = 0; j < tiles; ++j) {
       const int32_t lq = (int32_t)std::min<int64_t>(tile_q, lqo(i) - j * tile_q);
-      const int64_t chunks = ceil_div(kv_lens[i], L);
+      const int64_t ext = extent(i, j);
+      const int64_t chunks = ceil_div(ext, L);
       for (int64_t c = 0; c < chunks; ++c) {
         Item it;
         it.req = i;
         it.q0 = (int32_t)(j * tile_q);  // relative to the request / group; fixed up by caller
         it.nq = lq;
         it.kb = (int32_t)(c * L);
-        it.ke = (int32_t)std::min<int64_t>((c + 1) * L, kv_lens[i]);
+        it.ke = (int32_t)std::min<int64_t>((c + 1) * L, ext);
         it.row = -1;
         it.tile = (int32_t)j;
         it.w = (int32_t)st.items.size();
@@ -245,9 +253,10 @@ pkc_status build_plan_host(const Resolved& r, const int32_t* kv_lens_h,
     std::vector<int32_t> qo(h.num_groups);
     for (int32_t g = 0; g < h.num_groups; ++g) qo[g] = h.qo_indptr[g + 1] - h.qo_indptr[g];
     if ((s = lpt_plan(qo.data(), h.kv_lens, h.num_groups, p.level_tile_q, p.level_ctas, p.alpha,
-                      p.beta, r.p.chunk_align, p.enable_split != 0, &lv[l])) != PKC_OK)
+                      p.beta, r.p.chunk_align, p.enable_split != 0, &lv[l], h.causal != 0)) != PKC_OK)
       return s;
     P.lvl_groups[l] = h.num_groups;
+    P.lvl_causal[l] = h.causal != 0 ? 1 : 0;
     P.lvl_tile_q[l] = p.level_tile_q;
     P.lvl_items[l] = (int32_t)lv[l].items.size();
     P.lvl_kv_chunk[l] = lv[l].kv_chunk;

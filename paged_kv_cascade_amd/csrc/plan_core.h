@@ -35,10 +35,11 @@ struct Stage {
   std::vector<int64_t> cta_cost;
 };
 
-// Steps 1-7 of the scheduler for one stage. qo_lens may be nullptr (all 1).
+// Steps 1-7 of the scheduler for one stage. qo_lens may be nullptr (all 1).  causal: a query
+// tile's KV is only the part its last query sees under the causal mask.
 pkc_status lpt_plan(const int32_t* qo_lens, const int32_t* kv_lens, int32_t n, int32_t tile_q,
                     int32_t ctas, int64_t alpha, int64_t beta, int32_t chunk_align,
-                    bool enable_split, Stage* out);
+                    bool enable_split, Stage* out, bool causal = false);
 
 // Offsets of every array of a plan inside the host buffer / device workspace; fixed by the
 // parameters and the level shapes only, so they do not move from one step to the next.

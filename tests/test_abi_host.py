@@ -141,6 +141,29 @@ def test_cascade_plan_matches_oracle(api, seed):
     _compare_plan(api, info, hb, o, levels, tile_q)
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_causal_prefill_plan_matches_oracle(api, seed):
+    """Plans of ragged multi-token queries (one level whose groups are the requests, causal
+    tile extents, one plan request per query row), bit for bit against the oracle."""
+    rng = random.Random(3000 + seed)
+    B = rng.randint(1, 6)
+    qo = [rng.choice([1, 2, 9, 40, 130]) for _ in range(B)]
+    kv = [max(0, q + rng.choice([-5, 0, 3, 200])) for q in qo]
+    qi = [0]
+    for q in qo:
+        qi.append(qi[-1] + q)
+    T = qi[-1]
+    g = rng.choice([1, 2, 4])
+    tile_q = rng.choice([0, 4, 16 // g])
+    lctas = rng.choice([1, 5, 32])
+    levels = [{"qo_indptr": qi, "kv_lens": kv, "causal": seed % 4 != 3}]
+    p = api.make_params(T, 4 * g, 4, 128, 16, num_ctas=1, level_ctas=lctas, level_tile_q=tile_q)
+    info, hb = api.plan_host(p, [0] * T, levels)
+    tq = tile_q or 128 // g
+    o = oplan.cascade_plan(T, levels, [0] * T, num_ctas=1, level_ctas=lctas, level_tile_q=[tq], alpha=1, beta=1)
+    _compare_plan(api, info, hb, o, levels, tq)
+
+
 def test_standard_workload_plans_match_oracle(api):
     """The plans of the GQA split-KV workload (256 requests, log-uniform
     128..32768, #CTA = 512) and of both cascades, bit for bit."""

@@ -57,7 +57,8 @@ def _case(seed, lq, lkv, dtype, D, g, P, hkv=2, scale=1.0):
 def _run(api, q, k, v, bt, lq, lkv, causal, level_ctas=0, tile_q=0):
     T, Hq, D = q.shape
     P, Hkv = k.shape[1], k.shape[2]
-    info, ws, qi = api.prefill_plan(lq, lkv, Hq, Hkv, D, P, level_ctas=level_ctas, level_tile_q=tile_q)
+    info, ws, qi = api.prefill_plan(lq, lkv, Hq, Hkv, D, P, level_ctas=level_ctas, level_tile_q=tile_q,
+                                    causal=causal)
     qi_d = torch.tensor(qi, dtype=torch.int32, device="cuda")
     kv_d = torch.tensor(lkv, dtype=torch.int32, device="cuda")
     o, lse = api.batch_prefill_paged(info, q, k, v, bt.cuda(), qi_d, kv_d, causal=causal,
@@ -140,3 +141,5 @@ def test_prefill_rejects_plan_of_other_shape(api):
         api.batch_prefill_paged(info, q, k, v, torch.cat([bt, bt[:1]]).cuda(), qi_d, kv_d)
     with pytest.raises(api.PkcError):   # fp32 queries
         api.batch_prefill_paged(info, q.float(), k.float(), v.float(), bt.cuda(), qi_d, kv_d)
+    with pytest.raises(api.PkcError):   # a causal plan run without the mask
+        api.batch_prefill_paged(info, q, k, v, bt.cuda(), qi_d, kv_d, causal=False)

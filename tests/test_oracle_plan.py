@@ -167,3 +167,52 @@ def test_cascade_plan_merge_lists():
     assert cp.merge[2] == [(0, 1, 0), ("suffix", 0, 0), ("suffix", 1, 0), ("suffix", 2, 0)]
     assert cp.merge[3] == [(0, 1, 1)]
     assert cp.merge[4] == []
+
+
+# --- causal query tiles (ragged multi-token queries) -----------------------------------------
+
+def test_causal_hand_example():
+    """One request of 5 queries over 7 tokens, T_q = 2, two CTAs, alpha = beta = 1 (worked by
+    hand): tile extents 7-5+2 = 4, 7-5+4 = 6, 7-5+5 = 7, S = 17, L_kv = 9, one chunk each;
+    sorted w2 (7), w1 (6), w0 (4); CTA0 <- w2 (1+7), CTA1 <- w1 (2+6), tie -> CTA0 <- w0 (2+4)."""
+    st = plan.lpt_plan([5], [7], 2, 2, 1, 1, causal=True)
+    assert st.kv_chunk == 9
+    assert [[it.w, it.tile, it.lq, it.kv_begin, it.kv_end] for it in st.items] == \
+        [[0, 0, 2, 0, 4], [1, 1, 2, 0, 6], [2, 2, 1, 0, 7]]
+    assert st.order == [2, 1, 0]
+    assert st.cta_items == [[2, 0], [1]]
+    assert st.cta_cost == [14, 8]
+
+
+def test_causal_tiles_that_see_nothing_get_no_item():
+    """4 queries over 2 tokens, T_q = 2, three CTAs: the first tile's queries see nothing
+    (extent 2-4+2 = 0); the second sees 2 tokens, S = 2, L_kv = 1: two chunks."""
+    st = plan.lpt_plan([4], [2], 2, 3, 1, 1, causal=True)
+    assert [[it.tile, it.kv_begin, it.kv_end] for it in st.items] == [[1, 0, 1], [1, 1, 2]]
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_causal_extent_is_the_last_querys_visible_length(seed):
+    """The chunks of every causal tile cover exactly [0, n) where n is the number of tokens the
+    tile's last query sees by the attention oracle's definition (and nothing for tiles whose
+    queries see none); non-causal tiles cover [0, l_kv)."""
+    from oracle.attention import prefill_limit
+    rng = random.Random(seed)
+    qo = [rng.randint(0, 40) for _ in range(rng.randint(1, 6))]
+    kv = [max(0, q + rng.randint(-10, 60)) for q in qo]
+    tq = rng.choice([1, 3, 8, 16])
+    for causal in (False, True):
+        st = plan.lpt_plan(qo, kv, tq, rng.randint(1, 9), causal=causal, enable_split=rng.random() < 0.7)
+        cover = {}
+        for it in st.items:
+            cover.setdefault((it.req, it.tile), []).append((it.kv_begin, it.kv_end))
+        for i, (lq, lkv) in enumerate(zip(qo, kv)):
+            for j in range(plan.ceil_div(lq, tq)):
+                last = min((j + 1) * tq, lq) - 1
+                n = prefill_limit(lq, lkv, last, causal)
+                segs = sorted(cover.get((i, j), []))
+                if n == 0:
+                    assert segs == []
+                else:
+                    assert segs[0][0] == 0 and segs[-1][1] == n
+                    assert all(a[1] == b[0] for a, b in zip(segs, segs[1:]))
