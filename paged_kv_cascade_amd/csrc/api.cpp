@@ -199,7 +199,6 @@ pkc_status run_level(const pkc_plan_info* plan, int level, const void* q, const 
     p.table_stride = pf->max_blocks;
     p.grp_qo_indptr = pf->qo_indptr;
     p.grp_kv_lens = pf->kv_lens;
-    p.causal = pf->causal;
   } else {
     p.page_indptr = lv->kv_page_indptr;
     p.page_indices = lv->kv_page_indices;

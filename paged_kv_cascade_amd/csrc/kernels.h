@@ -57,13 +57,11 @@ struct PrefixParams {
   const int32_t* indptr;        // [#CTA + 1]
   const int32_t* items;
   // Ragged multi-token queries: page_indptr == nullptr selects a dense block table (group g's
-  // pages are page_indices[g * table_stride ..]); the causal kernel masks query i of group g
-  // (its queries are rows grp_qo_indptr[g] ..) to tokens t <= grp_kv_lens[g] - l_q(g) + i
-  // (causal records which kernel the host launched).
+  // pages are page_indices[g * table_stride ..]); the causal kernel variant masks query i of
+  // group g (its queries are rows grp_qo_indptr[g] ..) to tokens t <= grp_kv_lens[g] - l_q(g) + i.
   const int32_t* grp_qo_indptr;
   const int32_t* grp_kv_lens;
   int32_t table_stride;
-  int32_t causal;
 };
 
 // Plan-driven merge: request b merges merge_rows[merge_ptr[b*NL2 + l0] .. merge_ptr[b*NL2 + l1]).

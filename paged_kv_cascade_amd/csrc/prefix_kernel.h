@@ -391,16 +391,12 @@ __global__ __launch_bounds__(64 * prefix_detail::kWavesPerStream * NS, NS == 1 ?
 
     // Per lane and query tile nt: the causal limit of the lane's query column minus the offset
     // 4 * lg of its first S^T row, so that element (mt, i) of a tile starting at token tok0 is
-    // masked when tok0 + 16 mt + i > cbase[nt].  (A compile-time switch rather than a runtime
-    // flag: the kernel's scalar registers are nearly all taken, and the extra live values of a
-    // runtime branch push the loads' buffer descriptors out of them.)
+    // masked when tok0 + 16 mt + i > cbase[nt].  Causal masking is a compile-time variant, so
+    // the kernels without it carry none of its per-tile work.
     int cbase[2] = {0, 0};
-    int vtok0 = 0;   // first token of the stream's first tile, in a vector register
     if constexpr (CAUSAL) {
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) cbase[nt] = lim0 + (wq * kRowsPerWave + nt * 16 + l16) / G - 4 * lg;
-      vtok0 = t0 + stream * kTK;
-      __asm__ volatile("" : "+v"(vtok0));
     }
     auto compute = [&](const char* ks_s, const char* vs_s, uint32_t mask, int tok0) __attribute__((always_inline)) {
       if (!wave_active) return;
@@ -430,7 +426,7 @@ __global__ __launch_bounds__(64 * prefix_detail::kWavesPerStream * NS, NS == 1 ?
             s[mt][1][i] = v ? s[mt][1][i] : kNegInf;
           }
       }
-      // Causal mask, on tiles reaching past the smallest limit of the wave's queries.
+      // Causal mask, per query column.
       if constexpr (CAUSAL) {
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
@@ -438,12 +434,7 @@ __global__ __launch_bounds__(64 * prefix_detail::kWavesPerStream * NS, NS == 1 ?
           for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-            {
-              // Branch-free select on the vector unit (all-ones sign mask, bitfield insert), so
-              // the comparison needs no lane-mask registers.
-              const uint32_t neg = (uint32_t)((cbase[nt] - (tok0 + mt * 16 + i)) >> 31);
-              s[mt][nt][i] = __uint_as_float((neg & __float_as_uint(kNegInf)) | (~neg & __float_as_uint(s[mt][nt][i])));
-            }
+              s[mt][nt][i] = tok0 + mt * 16 + i > cbase[nt] ? kNegInf : s[mt][nt][i];
       }
       V16 pb[2];   // P^T operands per query tile nt (the tile's 32 tokens are one step)
       // bf16 weights go to the matrix cores as two bf16 terms (rounded weight and residual):
@@ -608,15 +599,7 @@ __global__ __launch_bounds__(64 * prefix_detail::kWavesPerStream * NS, NS == 1 ?
         issue(tt + AHEAD * NS, pg, lds_addr(sring) + N * SLOT, sfl + N);
         pg = fetch(tt + (AHEAD + 1) * NS);
         if (tt < ntiles) {
-          // The tile's first token, for the causal mask, is formed on the vector unit from
-          // opaque copies: shared with the scalar address arithmetic of the loads, the compiler
-          // would otherwise move that arithmetic to the vector unit as well.
-          int tok0 = 0;
-          if constexpr (CAUSAL) {
-            int jv = j;
-            __asm__ volatile("" : "+v"(jv));
-            tok0 = vtok0 + jv * (NS * kTK);
-          }
+          const int tok0 = t0 + tt * kTK;   // the tile's first token (causal mask)
           if constexpr (F8) compute(cb, cb + STB, mask, tok0);
           else compute(sring + S * SLOT, sring + S * SLOT + STB, mask, tok0);
         }
