@@ -396,6 +396,22 @@ pkc_status pkc_batch_prefill_paged(const pkc_plan_info* plan, const void* q, con
                                    float* lse, void* dev_ws, size_t dev_bytes, void* stream);
 
 /*
+ * pkc_batch_prefill_paged over FP8 K/V pools (paper summary, appendix F): OCP FP8 E4M3 codes
+ * with per-pool scales k_scale and v_scale (> 0); q and o are q_dtype (PKC_F16 or PKC_BF16).
+ * Arguments, plan and rules are those of pkc_batch_prefill_paged.  With one query per request
+ * this is also a batch decode whose grouped query heads go through the matrix cores.
+ */
+pkc_status pkc_batch_prefill_paged_fp8(const pkc_plan_info* plan, const void* q, const void* k_pool,
+                                       const void* v_pool, float k_scale, float v_scale,
+                                       int64_t num_pages, const int32_t* block_table,
+                                       int32_t max_blocks, const int32_t* qo_indptr,
+                                       const int32_t* kv_lens, int32_t num_requests,
+                                       int32_t total_q, int32_t num_qo_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t page_size, pkc_dtype q_dtype,
+                                       float sm_scale, int32_t causal, void* o, float* lse,
+                                       void* dev_ws, size_t dev_bytes, void* stream);
+
+/*
  * In-place KV append ("Paged attention" page, decode path: the cache is updated in place, and
  * its worked example places each sequence's next token at logical block cache_seqlens[b] / P,
  * slot cache_seqlens[b] % P of the sequence's block-table row).  For every request b, the new

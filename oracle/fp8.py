@@ -26,7 +26,7 @@ import math
 
 import numpy as np
 
-from .attention import batch_decode, cascade_decode, level_prefix_states
+from .attention import batch_decode, batch_prefill, cascade_decode, level_prefix_states
 
 BIAS = 7
 
@@ -91,3 +91,11 @@ def level_prefix_states_fp8(q, k_codes, v_codes, k_scale, v_scale, page_size, sm
     """``attention.level_prefix_states`` over the dequantised FP8 E4M3 pools."""
     return level_prefix_states(q, DequantizedPool(k_codes, k_scale), DequantizedPool(v_codes, v_scale),
                                page_size, sm_scale, level, num_requests)
+
+
+def batch_prefill_fp8(q, qo_indptr, k_codes, v_codes, k_scale, v_scale, block_table, kv_lens,
+                      page_size, sm_scale, causal, rows=None, heads=None):
+    """``attention.batch_prefill`` (ragged multi-token queries) over the dequantised FP8 E4M3
+    pools."""
+    return batch_prefill(q, qo_indptr, DequantizedPool(k_codes, k_scale), DequantizedPool(v_codes, v_scale),
+                         block_table, kv_lens, page_size, sm_scale, causal, rows=rows, heads=heads)

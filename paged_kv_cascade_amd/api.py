@@ -126,6 +126,9 @@ SIGNATURES = {
                                         _F, _P, _I32, _P, _P, _SZ, _P]),
     "pkc_batch_prefill_paged": (_I32, [ctypes.POINTER(PlanInfo), _P, _P, _P, _I64, _P, _I32, _P, _P, _I32,
                                        _I32, _I32, _I32, _I32, _I32, _I32, _F, _I32, _P, _P, _P, _SZ, _P]),
+    "pkc_batch_prefill_paged_fp8": (_I32, [ctypes.POINTER(PlanInfo), _P, _P, _P, _F, _F, _I64, _P, _I32, _P,
+                                           _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _F, _I32, _P, _P,
+                                           _P, _SZ, _P]),
     "pkc_cascade_decode_fp8": (_I32, [ctypes.POINTER(PlanInfo), _P, _P, _P, _F, _F, _I64,
                                       ctypes.POINTER(LevelDev), _I32, _P, _I32, _P, _I32, _I32, _I32,
                                       _I32, _I32, _I32, _F, _P, _P, _P, _SZ, _P]),
@@ -529,6 +532,31 @@ def batch_prefill_paged(plan_info: PlanInfo, q, k_pool, v_pool, block_table, qo_
                                        _ptr(block_table), block_table.shape[1], _ptr(qo_indptr), _ptr(kv_lens),
                                        B, T, Hq, Hkv, D, P, dtype_code(q.dtype), scale, 1 if causal else 0,
                                        _ptr(out), _ptr(lse), ws, wsn, _stream(dev)))
+    return out, lse
+
+
+def batch_prefill_paged_fp8(plan_info: PlanInfo, q, k_pool, v_pool, block_table, qo_indptr, kv_lens,
+                            k_scale=1.0, v_scale=1.0, causal=True, sm_scale=None, out=None, lse=None):
+    """pkc_batch_prefill_paged_fp8: batch_prefill_paged over OCP FP8 E4M3 pools (float8_e4m3fn
+    or uint8 codes) with per-pool scales; q and o fp16 / bf16."""
+    T, Hq, D = q.shape
+    N, P, Hkv, _ = k_pool.shape
+    dev = q.device
+    B = block_table.shape[0]
+    _check_fp8_pools(q, k_pool, v_pool)
+    for t, n in ((block_table, "block_table"), (qo_indptr, "qo_indptr"), (kv_lens, "kv_lens")):
+        _need(t, n, torch.int32, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(T, Hq, dtype=torch.float32, device=dev)
+    scale = 1.0 / math.sqrt(D) if sm_scale is None else float(sm_scale)
+    ws, wsn = _ws_of(plan_info)
+    _check(lib.pkc_batch_prefill_paged_fp8(ctypes.byref(plan_info), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                           float(k_scale), float(v_scale), N, _ptr(block_table),
+                                           block_table.shape[1], _ptr(qo_indptr), _ptr(kv_lens), B, T, Hq, Hkv,
+                                           D, P, dtype_code(q.dtype), scale, 1 if causal else 0, _ptr(out),
+                                           _ptr(lse), ws, wsn, _stream(dev)))
     return out, lse
 
 

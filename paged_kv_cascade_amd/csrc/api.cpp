@@ -228,8 +228,10 @@ pkc_status run_level(const pkc_plan_info* plan, int level, const void* q, const 
   }
   if (pf && pf->causal)
     return timed(1, s, "prefix kernel launch", [&] {
-      return pkc::launch_prefill_causal(dtype, plan->head_dim, g, plan->lvl_tile_q[level], streams, p,
-                                        plan->level_ctas, s);
+      return fp8 ? pkc::launch_prefill_causal_fp8(dtype, plan->head_dim, g, plan->lvl_tile_q[level], streams,
+                                                  p, plan->level_ctas, s)
+                 : pkc::launch_prefill_causal(dtype, plan->head_dim, g, plan->lvl_tile_q[level], streams, p,
+                                              plan->level_ctas, s);
     });
   return timed(1, s, "prefix kernel launch", [&] {
     return fp8 ? pkc::launch_prefix_fp8(dtype, plan->head_dim, g, plan->lvl_tile_q[level], streams, p,
@@ -530,18 +532,18 @@ pkc_status pkc_prefix_attention_fp8(const pkc_plan_info* plan, int32_t level, co
   PKC_TRY_END("pkc_prefix_attention_fp8")
 }
 
-pkc_status pkc_batch_prefill_paged(const pkc_plan_info* plan, const void* q, const void* k_pool,
-                                   const void* v_pool, int64_t num_pages,
-                                   const int32_t* block_table, int32_t max_blocks,
-                                   const int32_t* qo_indptr, const int32_t* kv_lens,
-                                   int32_t num_requests, int32_t total_q, int32_t num_qo_heads,
-                                   int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
-                                   pkc_dtype dtype, float sm_scale, int32_t causal, void* o,
-                                   float* lse, void* dev_ws, size_t dev_bytes, void* stream) {
-  PKC_TRY_BEGIN
+static pkc_status prefill_impl(bool fp8, float k_scale, float v_scale, const pkc_plan_info* plan,
+                               const void* q, const void* k_pool, const void* v_pool,
+                               int64_t num_pages, const int32_t* block_table, int32_t max_blocks,
+                               const int32_t* qo_indptr, const int32_t* kv_lens,
+                               int32_t num_requests, int32_t total_q, int32_t num_qo_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                               pkc_dtype dtype, float sm_scale, int32_t causal, void* o,
+                               float* lse, void* dev_ws, size_t dev_bytes, void* stream) {
   pkc_status st = check_shapes(total_q, num_qo_heads, num_kv_heads, head_dim, page_size, dtype, sm_scale);
   if (st != PKC_OK) return st;
   if ((st = check_prefix_supported(dtype, page_size)) != PKC_OK) return st;
+  if (fp8 && (st = check_fp8(dtype, k_scale, v_scale)) != PKC_OK) return st;
   if (!plan) return fail(PKC_ERR_INVALID_ARG, "batch prefill needs a plan");
   if (num_requests < 0) return fail(PKC_ERR_INVALID_ARG, "num_requests < 0");
   if ((st = check_plan(plan, total_q, num_qo_heads, num_kv_heads, head_dim, page_size, dev_ws, dev_bytes)) != PKC_OK)
@@ -563,12 +565,42 @@ pkc_status pkc_batch_prefill_paged(const pkc_plan_info* plan, const void* q, con
     return fail(PKC_ERR_INVALID_ARG, "block table too large for int32 offsets");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const PrefillLevel pf{block_table, max_blocks, qo_indptr, kv_lens, causal ? 1 : 0};
-  if ((st = run_level(plan, 0, q, k_pool, v_pool, num_pages, nullptr, dtype, sm_scale, dev_ws, s, false,
-                      1.f, 1.f, &pf)) != PKC_OK)
+  if ((st = run_level(plan, 0, q, k_pool, v_pool, num_pages, nullptr, dtype, sm_scale, dev_ws, s, fp8,
+                      k_scale, v_scale, &pf)) != PKC_OK)
     return st;
   pkc::MergePlanParams m = merge_params(plan, dev_ws, 0, 1, false, o, lse);
   return timed(2, s, "merge kernel launch", [&] { return pkc::launch_merge_plan(dtype, head_dim, m, s); });
+}
+
+pkc_status pkc_batch_prefill_paged(const pkc_plan_info* plan, const void* q, const void* k_pool,
+                                   const void* v_pool, int64_t num_pages,
+                                   const int32_t* block_table, int32_t max_blocks,
+                                   const int32_t* qo_indptr, const int32_t* kv_lens,
+                                   int32_t num_requests, int32_t total_q, int32_t num_qo_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                                   pkc_dtype dtype, float sm_scale, int32_t causal, void* o,
+                                   float* lse, void* dev_ws, size_t dev_bytes, void* stream) {
+  PKC_TRY_BEGIN
+  return prefill_impl(false, 1.f, 1.f, plan, q, k_pool, v_pool, num_pages, block_table, max_blocks,
+                      qo_indptr, kv_lens, num_requests, total_q, num_qo_heads, num_kv_heads, head_dim,
+                      page_size, dtype, sm_scale, causal, o, lse, dev_ws, dev_bytes, stream);
   PKC_TRY_END("pkc_batch_prefill_paged")
+}
+
+pkc_status pkc_batch_prefill_paged_fp8(const pkc_plan_info* plan, const void* q, const void* k_pool,
+                                       const void* v_pool, float k_scale, float v_scale,
+                                       int64_t num_pages, const int32_t* block_table,
+                                       int32_t max_blocks, const int32_t* qo_indptr,
+                                       const int32_t* kv_lens, int32_t num_requests,
+                                       int32_t total_q, int32_t num_qo_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t page_size, pkc_dtype q_dtype,
+                                       float sm_scale, int32_t causal, void* o, float* lse,
+                                       void* dev_ws, size_t dev_bytes, void* stream) {
+  PKC_TRY_BEGIN
+  return prefill_impl(true, k_scale, v_scale, plan, q, k_pool, v_pool, num_pages, block_table,
+                      max_blocks, qo_indptr, kv_lens, num_requests, total_q, num_qo_heads, num_kv_heads,
+                      head_dim, page_size, q_dtype, sm_scale, causal, o, lse, dev_ws, dev_bytes, stream);
+  PKC_TRY_END("pkc_batch_prefill_paged_fp8")
 }
 
 pkc_status pkc_merge_states(const void* o_states, pkc_dtype in_dtype, const float* lse_states,

@@ -116,6 +116,8 @@ hipError_t launch_prefix(pkc_dtype dt, int head_dim, int group, int tile_q, int 
 // The level kernel with the causal mask (ragged multi-token queries, fp16 / bf16 pools).
 hipError_t launch_prefill_causal(pkc_dtype dt, int head_dim, int group, int tile_q, int streams,
                                  const PrefixParams& p, int grid_x, hipStream_t s);
+hipError_t launch_prefill_causal_fp8(pkc_dtype q_dt, int head_dim, int group, int tile_q, int streams,
+                                     const PrefixParams& p, int grid_x, hipStream_t s);
 // The same over OCP FP8 E4M3 pools; q_dt (fp16 or bf16) is the query and operand type.
 hipError_t launch_prefix_fp8(pkc_dtype q_dt, int head_dim, int group, int tile_q, int streams,
                              const PrefixParams& p, int grid_x, hipStream_t s);

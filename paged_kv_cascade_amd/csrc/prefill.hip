@@ -1,6 +1,6 @@
 // Instantiations of the multi-query level kernel (prefix_kernel.h) with the causal mask, for
 // ragged multi-token queries over fp16 / bf16 pools (the non-causal case uses the plain level
-// kernel).
+// kernel; FP8 pools are in prefill_fp8.hip).
 #include "prefix_kernel.h"
 
 namespace pkc {

@@ -287,3 +287,54 @@ def test_fp8_prefix_attention_standalone(api, streams, monkeypatch):
         Lf = np.where(covered[:, None], L, -np.inf)
         Of = np.where(covered[:, None, None], O, 0.0)
         check_state(o, lse, Of, Lf, torch.float16, f"fp8 level {l}")
+
+
+# --- ragged multi-token queries over FP8 pools -------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(8))
+def test_fp8_ragged_prefill(api, seed):
+    from tests.test_gpu_prefill import _case
+    rng = random.Random(700 + seed)
+    qdt = [torch.float16, torch.bfloat16][seed % 2]
+    D = [128, 64][(seed // 2) % 2]
+    g = [1, 8, 2, 4][seed % 4]
+    P = [16, 4][seed % 2]
+    causal = seed % 3 != 1
+    B = rng.randint(1, 5)
+    lq = [rng.choice([1, 3, 40, 130]) for _ in range(B)]
+    lkv = [max(0, n + rng.choice([0, 2, 90, -2])) for n in lq]
+    ksc, vsc = [(1.0, 1.0), (0.4, 1.7)][seed % 2]
+    say(f"case: fp8 prefill seed={seed} q {qdt} D={D} g={g} P={P} causal={causal} lq={lq} lkv={lkv}")
+    q, k, v, bt = _case(800 + seed, lq, lkv, qdt, D, g, P)
+    k8, v8 = workloads.fp8_e4m3_pool(k, ksc), workloads.fp8_e4m3_pool(v, vsc)
+    info, ws, qi = api.prefill_plan(lq, lkv, q.shape[1], k.shape[2], D, P, level_ctas=rng.choice([0, 3]),
+                                    causal=causal)
+    qi_d = torch.tensor(qi, dtype=torch.int32, device="cuda")
+    kv_d = torch.tensor(lkv, dtype=torch.int32, device="cuda")
+    o, lse = api.batch_prefill_paged_fp8(info, q, k8, v8, bt.cuda(), qi_d, kv_d, k_scale=ksc, v_scale=vsc,
+                                         causal=causal, sm_scale=1.0 / math.sqrt(D))
+    torch.cuda.synchronize()
+    O, L = ofp8.batch_prefill_fp8(host(q), qi, CodeView(k8), CodeView(v8), ksc, vsc, bt.numpy(), lkv, P,
+                                  1.0 / math.sqrt(D), causal)
+    check_state(o, lse, O, L, qdt, f"fp8 prefill seed {seed}")
+
+
+def test_fp8_grouped_decode_through_matrix_cores(api):
+    """One query per request with 8 query heads per KV head: the prefill path (matrix cores)
+    and the vector-ALU decode kernel give the same decode."""
+    say("case: fp8 GQA g8 decode through the prefill path vs the decode kernel")
+    w = workloads.gqa_split(batch=24, heads=32, kv_heads=4, lo=16, hi=3000, device="cuda")
+    k8 = workloads.fp8_e4m3_pool(w.k_pool, 0.5)
+    v8 = workloads.fp8_e4m3_pool(w.v_pool, 0.5)
+    lens = w.cache_seqlens.cpu().tolist()
+    info, ws, qi = api.prefill_plan([1] * w.batch, lens, 32, 4, 128, 16, causal=False)
+    qi_d = torch.tensor(qi, dtype=torch.int32, device="cuda")
+    o, lse = api.batch_prefill_paged_fp8(info, w.q, k8, v8, w.block_table, qi_d, w.cache_seqlens,
+                                         k_scale=0.5, v_scale=0.5, causal=False, sm_scale=w.sm_scale)
+    o2, lse2 = api.batch_decode_paged_fp8(w.q, k8, v8, w.block_table, w.cache_seqlens, k_scale=0.5,
+                                          v_scale=0.5, sm_scale=w.sm_scale)
+    torch.cuda.synchronize()
+    reqs = [0, 5, 11, 23]
+    O, L = _oracle(w.q, k8, v8, 0.5, 0.5, w.block_table, w.cache_seqlens, 16, w.sm_scale, requests=reqs)
+    check_state(o, lse, O, L, torch.bfloat16, "fp8 g8 decode, matrix cores", rows=reqs)
+    check_state(o2, lse2, O, L, torch.bfloat16, "fp8 g8 decode, vector ALU", rows=reqs)

@@ -157,3 +157,17 @@ def test_fp8_cascade_and_level_states_equal_torch_decoded_pools():
         m = ~np.isnan(L)
         assert np.allclose(L8[m], L[m], rtol=1e-14, atol=1e-14)
         assert np.allclose(O8[m], O[m], rtol=1e-13, atol=1e-15)
+
+
+def test_fp8_prefill_equals_prefill_over_torch_decoded_pools():
+    q, kf, vf, bt, lens, P = _fp8_case(8)
+    qo = [0, 2, 3, 8, 9]          # 4 requests with 2, 1, 5, 1 queries
+    kc, vc = kf.view(torch.uint8).numpy(), vf.view(torch.uint8).numpy()
+    qq = np.concatenate([q, q[:1], q, q[:1]])[:9]
+    for causal in (False, True):
+        O8, L8 = fp8.batch_prefill_fp8(qq, qo, kc, vc, 0.5, 2.0, bt, lens, P, 0.25, causal)
+        O, L = attention.batch_prefill(qq, qo, 0.5 * kf.to(torch.float64).numpy(), 2.0 * vf.to(torch.float64).numpy(),
+                                       bt, lens, P, 0.25, causal)
+        fin = ~np.isneginf(L)
+        assert np.array_equal(np.isneginf(L8), ~fin)
+        assert np.allclose(O8, O, rtol=1e-13, atol=1e-15) and np.allclose(L8[fin], L[fin], rtol=1e-13)
