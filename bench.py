@@ -405,7 +405,7 @@ def load_traffic(src_hash):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+        print(json.dumps({"error": "this benchmark runs on one GPU; --gpus must be 1",
                           "n_gpus_requested": args.gpus}), flush=True)
         sys.exit(2)
     if args.cpu_baseline_only:
