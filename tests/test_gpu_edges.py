@@ -3,7 +3,6 @@ requests that all have empty token sets (the merge identity), the largest page s
 long sequence split across the whole chip, and shapes whose offsets would not fit in 32 bits
 (rejected before any launch)."""
 
-
 import pytest
 import torch
 
