@@ -388,6 +388,10 @@ __global__ __launch_bounds__(64 * prefix_detail::kWavesPerStream * NS, NS == 1 ?
       for (int nt = 0; nt < 2; ++nt) oacc[dm][nt] = f4_t{0.f, 0.f, 0.f, 0.f};
     float m_run[2] = {kNegInf, kNegInf};
     float l_run[2] = {0.f, 0.f};
+    // Derived from m_run, refreshed only when it moves: the raise bound m_run + kSlack and
+    // the exponent offset -mu (mu = m_run, or 0 while the column has seen no score).
+    float m_lim[2] = {kNegInf, kNegInf};
+    float nmu[2] = {-0.f, -0.f};
 
     // Per lane and query tile nt: the causal limit of the lane's query column minus the offset
     // 4 * lg of its first S^T row, so that element (mt, i) of a tile starting at token tok0 is
@@ -444,39 +448,41 @@ __global__ __launch_bounds__(64 * prefix_detail::kWavesPerStream * NS, NS == 1 ?
       V16 pl[2];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        float mx = kNegInf;
+        float pmx = kNegInf;   // this lane's share of the column maximum (raw scores)
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[mt][nt][i]);
-        mx = lane_groups_max(mx) * p.scale_log2;
+          for (int i = 0; i < 4; ++i) pmx = fmaxf(pmx, s[mt][nt][i]);
         // Lazy reference maximum: m_run moves only when a score exceeds it by more than
         // kSlack (log2 units), so O and l are rescaled only on such tiles (in practice the
         // first ones).  Weights stay below 2^kSlack, which fp32 and the 16-bit operand types
         // hold with their usual relative precision, and the final state (O / l, m + log2 l)
-        // does not depend on the reference used.  A fully masked column (mx = -inf) never
-        // raises its reference.
-        const bool raise = mx > m_run[nt] + kSlack;
-        if (wave_any(raise)) {
+        // does not depend on the reference used.  A fully masked column (max = -inf) never
+        // raises its reference.  A column's maximum exceeds the bound exactly when one of its
+        // lanes' shares does (scale_log2 > 0), so the cross-lane maximum is only formed on
+        // the tiles that raise some column.
+        if (wave_any(pmx * p.scale_log2 > m_lim[nt])) {
+          const float mx = lane_groups_max(pmx) * p.scale_log2;
+          const bool raise = mx > m_lim[nt];
           const float alpha = raise ? fast_exp2(m_run[nt] - mx) : 1.f;
           m_run[nt] = raise ? mx : m_run[nt];
+          m_lim[nt] = m_run[nt] + kSlack;
+          nmu[nt] = -((m_run[nt] == kNegInf) ? 0.f : m_run[nt]);
           l_run[nt] *= alpha;
 #pragma unroll
           for (int dm = 0; dm < DM; ++dm) oacc[dm][nt] *= alpha;
         }
-        const float mu = (m_run[nt] == kNegInf) ? 0.f : m_run[nt];
-        float psum = 0.f;
         float pr[2][4];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            // P enters the PV product rounded to the operand type, but the denominator
-            // (and so the LSE) sums the fp32 weights: with bf16, summing rounded weights
-            // would move LSE by up to 2^-9.
-            pr[mt][i] = fast_exp2(fmaf(s[mt][nt][i], p.scale_log2, -mu));
-            psum += pr[mt][i];
-          }
+          for (int i = 0; i < 4; ++i) pr[mt][i] = fast_exp2(fmaf(s[mt][nt][i], p.scale_log2, nmu[nt]));
+        // P enters the PV product rounded to the operand type, but the denominator (and so the
+        // LSE) sums the fp32 weights: with bf16, summing rounded weights would move LSE by up
+        // to 2^-9.
+        float psum = pr[0][0];
+#pragma unroll
+        for (int k = 1; k < 8; ++k) psum += pr[k >> 2][k & 3];
         l_run[nt] += psum;
         pb[nt].w[0] = Mfma<T>::pack(pr[0][0], pr[0][1]);
         pb[nt].w[1] = Mfma<T>::pack(pr[0][2], pr[0][3]);
