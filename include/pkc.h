@@ -109,7 +109,7 @@ typedef struct pkc_plan_params {
   int32_t num_ctas;     /* #CTA of the decode stage; 0 -> max(ceil(8 x compute units / Hkv),
                            batch): about 8 workgroups per compute unit, at least one CTA per
                            request */
-  int32_t level_ctas;   /* #CTA of every cascade level; 0 -> ceil(2 x compute units / Hkv) */
+  int32_t level_ctas;   /* #CTA of every cascade level; 0 -> max(1, floor(compute units / Hkv)) */
   int32_t level_tile_q; /* T_q of the cascade levels (queries per tile); 0 -> 128 / (Hq/Hkv) */
   int32_t chunk_align;  /* round L_kv up to a multiple of this; 0 or 1 -> no rounding */
   int32_t enable_split; /* 0 -> L_kv = longest KV length (one chunk per tile, no split-KV) */

@@ -494,8 +494,13 @@ def prefill_plan(qo_lens, kv_lens, num_qo_heads, num_kv_heads, head_dim, page_si
                  workspace: Workspace = None):
     """Plan of a batch prefill: every query row is one plan request (batch = total_q, no own
     KV) and one level whose groups are the requests (qo_indptr = cumulative query lengths,
-    kv_lens; causal: tiles weighed by the KV their last query sees).  Returns (plan_info,
-    workspace, qo_indptr list)."""
+    kv_lens; causal: tiles weighed by the KV their last query sees).  level_ctas = 0 takes
+    8 x floor(compute units / Hkv): a prefill level has many tiles per workgroup, and several
+    rounds of 4-wave workgroups balance them better than the one 8-wave workgroup per
+    compute unit that suits a decode step's level (causal 8 x 2048 at 32 heads: 585 against
+    700-760 us).  Returns (plan_info, workspace, qo_indptr list)."""
+    if level_ctas == 0:
+        level_ctas = 8 * max(1, device_info(torch.cuda.current_device())["num_cus"] // int(num_kv_heads))
     qo_lens = [int(x) for x in qo_lens]
     qo_indptr = [0]
     for n in qo_lens:

@@ -261,8 +261,12 @@ bool host_buf_is_pinned(const void* host_buf) {
 // several fit on a compute unit, so the decode default is about 8 workgroups per compute
 // unit and at least one CTA per request, #CTA = max(ceil(8 x CUs / Hkv), batch): a CTA that
 // walks two requests pays its start-up and drain twice, which costs more than an extra
-// round of workgroups.  A level's MFMA workgroup holds 64 KB of LDS, two fit on a compute
-// unit, so the level default is #CTA = ceil(2 x CUs / Hkv).
+// round of workgroups.  A level's default is one workgroup per compute unit,
+// #CTA = max(1, floor(CUs / Hkv)): such a grid runs 8-wave workgroups (two tile streams), and
+// a decode step's level then leaves half as many chunk states to fold as with two 4-wave
+// workgroups per compute unit (the 32K-prefix, batch-128 cascade step: 190 against 201 us;
+// with three levels 315 against 345 us).  Long multi-token levels (prefill) run faster with
+// more, smaller workgroups and should pass their own #CTA.
 pkc_status resolve_params(const pkc_plan_params* params, pkc::Resolved* r) {
   pkc_status st = pkc::check_params(params, false, r);
   if (st != PKC_OK) return st;
@@ -273,7 +277,7 @@ pkc_status resolve_params(const pkc_plan_params* params, pkc::Resolved* r) {
       r->p.num_ctas = (int32_t)std::max<int64_t>(
           std::max<int64_t>(1, r->p.batch), pkc::ceil_div(8 * (int64_t)cus, r->p.num_kv_heads));
     if (r->p.level_ctas == 0)
-      r->p.level_ctas = (int32_t)std::max<int64_t>(1, pkc::ceil_div(2 * (int64_t)cus, r->p.num_kv_heads));
+      r->p.level_ctas = (int32_t)std::max<int64_t>(1, (int64_t)cus / r->p.num_kv_heads);
   }
   return PKC_OK;
 }
