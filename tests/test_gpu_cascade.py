@@ -45,14 +45,23 @@ def _oracle(w, requests=None, heads=None):
                                requests=requests, heads=heads)
 
 
-def test_two_level_cascade_full_size(api):
+def _level_grid(api, grid, hkv):
+    """level_ctas of a grid choice: the default (one 8-wave workgroup per compute unit) or two
+    4-wave workgroups per compute unit."""
+    return 0 if grid == "default" else 2 * api.device_info(0)["num_cus"] // hkv
+
+
+@pytest.mark.parametrize("grid", ["default", "two_per_cu"])
+def test_two_level_cascade_full_size(api, grid):
     """Shared prefix 32768 tokens (pages 0..2047) + 256 unique tokens per request in
     permuted pages, batch 128, 32 heads x 128, fp16."""
-    say("case: two-level cascade prefix32768 suffix256 b128 h32 d128 p16 fp16 (full size, sampled oracle)")
+    say(f"case: two-level cascade prefix32768 suffix256 b128 h32 d128 p16 fp16 level grid {grid} "
+        "(full size, sampled oracle)")
     w = workloads.cascade_two_level(device="cuda")
     api.validate_block_table(w.block_table.cpu(), w.cache_seqlens.cpu(), w.page_size, w.num_pages)
-    o, lse, info, ws, devs, keep = _run_cascade(api, w)
-    o2, lse2, *_ = _run_cascade(api, w)
+    lc = _level_grid(api, grid, w.num_kv_heads)
+    o, lse, info, ws, devs, keep = _run_cascade(api, w, level_ctas=lc)
+    o2, lse2, *_ = _run_cascade(api, w, level_ctas=lc)
     torch.cuda.synchronize()
     assert torch.equal(o, o2) and torch.equal(lse, lse2), "repeat run differs"
     say(f"  plan: level chunk={info.lvl_kv_chunk[0]} level items={info.lvl_items[0]} "
@@ -62,11 +71,13 @@ def test_two_level_cascade_full_size(api):
     check_state(o, lse, O, L, torch.float16, "cascade 32K prefix", rows=reqs)
 
 
-def test_multi_level_cascade_full_size(api):
+@pytest.mark.parametrize("grid", ["default", "two_per_cu"])
+def test_multi_level_cascade_full_size(api, grid):
     """Global prefix 16384 + 4 groups x 4096 + 512 per request, batch 128, fp16."""
-    say("case: three-level cascade 16384 + 4x4096 + 512, b128 h32 d128 fp16 (full size, sampled oracle)")
+    say(f"case: three-level cascade 16384 + 4x4096 + 512, b128 h32 d128 fp16 level grid {grid} "
+        "(full size, sampled oracle)")
     w = workloads.cascade_multi_level(device="cuda")
-    o, lse, info, *_ = _run_cascade(api, w)
+    o, lse, info, *_ = _run_cascade(api, w, level_ctas=_level_grid(api, grid, w.num_kv_heads))
     torch.cuda.synchronize()
     reqs = [0, 40, 95, 127]
     O, L = _oracle(w, requests=reqs)

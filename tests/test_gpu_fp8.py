@@ -211,15 +211,20 @@ def _fp8_cascade_oracle(w, k8, v8, ksc, vsc, requests=None):
                                    w.cache_seqlens.cpu().numpy(), requests=requests)
 
 
-def test_fp8_two_level_cascade_full_size(api):
+@pytest.mark.parametrize("grid", ["default", "two_per_cu"])
+def test_fp8_two_level_cascade_full_size(api, grid):
     """The cascade workload (32768-token shared prefix + 256 tokens per request, batch 128,
-    32 heads x 128, page 16) with fp16 queries over E4M3 pools (k_scale 0.25, v_scale 0.125)."""
-    say("case: fp8 two-level cascade prefix32768 suffix256 b128 h32 d128 p16, fp16 q (sampled oracle)")
+    32 heads x 128, page 16) with fp16 queries over E4M3 pools (k_scale 0.25, v_scale 0.125),
+    on the default level grid (one 8-wave workgroup per compute unit) and on two 4-wave
+    workgroups per compute unit."""
+    say(f"case: fp8 two-level cascade prefix32768 suffix256 b128 h32 d128 p16, fp16 q, level grid {grid} "
+        "(sampled oracle)")
     w = workloads.cascade_two_level(device="cuda")
     k8 = workloads.fp8_e4m3_pool(w.k_pool, 0.25)
     v8 = workloads.fp8_e4m3_pool(w.v_pool, 0.125)
-    o, lse, info, *_ = _fp8_cascade_run(api, w, k8, v8, 0.25, 0.125)
-    o2, lse2, *_ = _fp8_cascade_run(api, w, k8, v8, 0.25, 0.125)
+    lc = 0 if grid == "default" else 2 * api.device_info(0)["num_cus"] // w.num_kv_heads
+    o, lse, info, *_ = _fp8_cascade_run(api, w, k8, v8, 0.25, 0.125, level_ctas=lc)
+    o2, lse2, *_ = _fp8_cascade_run(api, w, k8, v8, 0.25, 0.125, level_ctas=lc)
     torch.cuda.synchronize()
     assert torch.equal(o, o2) and torch.equal(lse, lse2), "repeat run differs"
     reqs = [0, 77, 127]
