@@ -120,6 +120,11 @@ typedef struct pkc_plan_params {
                            run captured in a HIP graph replays the launches it was captured
                            with, so plans replayed under one graph need a fixed value (and no
                            merge launch: enable_split = 0 in a cascade) */
+  int32_t level_write_through; /* 1 (batch prefill): in a plan with a single level, a tile of a
+                           group whose requests have no own KV and whose KV is one chunk writes its
+                           rows' final output (O in the query type, LSE) instead of a state, and
+                           the merge pass skips those rows; only pkc_batch_prefill_paged(_fp8)
+                           runs such plans.  0: every level item writes a state (cascades) */
 } pkc_plan_params;
 
 /* Host description of one cascade level: groups of consecutive requests sharing a KV run.
@@ -185,6 +190,7 @@ typedef struct pkc_plan_info {
   int64_t dev_bytes;       /* device workspace bytes this plan uses */
   uint64_t dev_ws;         /* address of the workspace the plan was copied to (0: host-only) */
   int32_t lvl_causal[PKC_MAX_LEVELS]; /* 1: the level was planned with causal tile extents */
+  int32_t lvl_write_through;  /* level items that write the final output (level_write_through) */
 } pkc_plan_info;
 
 /*

@@ -157,7 +157,7 @@ class CascadePlan:
 
 def cascade_plan(batch, levels, suffix_kv_lens, num_ctas, level_ctas,
                  level_tile_q, alpha=1, beta=1, chunk_align=1,
-                 enable_split=True) -> CascadePlan:
+                 enable_split=True, level_write_through=False) -> CascadePlan:
     """Plan of a cascade step (or of a plain batch decode when ``levels`` is
     empty).
 
@@ -175,6 +175,11 @@ def cascade_plan(batch, levels, suffix_kv_lens, num_ctas, level_ctas,
     request's own chunks ascending.  A merge entry is (stage, slot, row):
     stage is the level index or 'suffix', row the query's index inside its
     tile.
+
+    ``level_write_through`` (batch prefill, reading R30): with a single
+    level, the appendix D write-through rule also applies to the level, for
+    the groups none of whose requests has own KV: a tile with one chunk
+    writes its rows' final output, and those requests are not merged.
     """
     lvl_plans = []
     for li, lv in enumerate(levels):
@@ -182,7 +187,12 @@ def cascade_plan(batch, levels, suffix_kv_lens, num_ctas, level_ctas,
         qo_lens = [qi[g + 1] - qi[g] for g in range(len(qi) - 1)]
         st = lpt_plan(qo_lens, lv["kv_lens"], level_tile_q[li], level_ctas, alpha,
                       beta, chunk_align, enable_split, causal=bool(lv.get("causal", False)))
-        assign_slots(st, lambda r: False)
+        if level_write_through and len(levels) == 1:
+            no_own_kv = [all(int(suffix_kv_lens[b]) == 0 for b in range(qi[g], qi[g + 1]))
+                         for g in range(len(qo_lens))]
+            assign_slots(st, lambda g: no_own_kv[g])
+        else:
+            assign_slots(st, lambda g: False)
         lvl_plans.append(st)
 
     suf = lpt_plan([1] * batch, suffix_kv_lens, 1, num_ctas, alpha, beta,
@@ -197,7 +207,10 @@ def cascade_plan(batch, levels, suffix_kv_lens, num_ctas, level_ctas,
         for it in st.items:          # ascending w == ascending chunk per tile
             b0 = qi[it.req] + it.tile * tq
             for r in range(it.lq):
-                merge[b0 + r].append((li, st.slots[it.w], r))
+                if st.slots[it.w] < 0:
+                    wt[b0 + r] = True
+                else:
+                    merge[b0 + r].append((li, st.slots[it.w], r))
     for it in suf.items:
         if suf.slots[it.w] < 0:
             wt[it.req] = True

@@ -42,7 +42,8 @@ class PlanParams(ctypes.Structure):
                 ("page_size", ctypes.c_int32), ("num_ctas", ctypes.c_int32),
                 ("level_ctas", ctypes.c_int32), ("level_tile_q", ctypes.c_int32),
                 ("chunk_align", ctypes.c_int32), ("enable_split", ctypes.c_int32),
-                ("alpha", ctypes.c_int64), ("beta", ctypes.c_int64), ("decode_waves", ctypes.c_int32)]
+                ("alpha", ctypes.c_int64), ("beta", ctypes.c_int64), ("decode_waves", ctypes.c_int32),
+                ("level_write_through", ctypes.c_int32)]
 
 
 class LevelHost(ctypes.Structure):
@@ -77,7 +78,8 @@ class PlanInfo(ctypes.Structure):
                 ("off_req_flags", ctypes.c_int64), ("off_req_levels", ctypes.c_int64),
                 ("int_bytes", ctypes.c_int64),
                 ("off_state_o", ctypes.c_int64), ("off_state_lse", ctypes.c_int64),
-                ("dev_bytes", ctypes.c_int64), ("dev_ws", ctypes.c_uint64), ("lvl_causal", _L8)]
+                ("dev_bytes", ctypes.c_int64), ("dev_ws", ctypes.c_uint64), ("lvl_causal", _L8),
+                ("lvl_write_through", ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p
@@ -200,9 +202,10 @@ def device_info(device: int = 0):
 
 def make_params(batch, num_qo_heads, num_kv_heads, head_dim, page_size, num_ctas=0, level_ctas=0,
                 level_tile_q=0, chunk_align=1, enable_split=True, alpha=1, beta=1,
-                decode_waves=0) -> PlanParams:
+                decode_waves=0, level_write_through=False) -> PlanParams:
     return PlanParams(batch, num_qo_heads, num_kv_heads, head_dim, page_size, num_ctas, level_ctas,
-                      level_tile_q, chunk_align, 1 if enable_split else 0, alpha, beta, decode_waves)
+                      level_tile_q, chunk_align, 1 if enable_split else 0, alpha, beta, decode_waves,
+                      1 if level_write_through else 0)
 
 
 class _Levels:
@@ -491,14 +494,16 @@ def cascade_decode_fp8(plan_info: PlanInfo, q, k_pool, v_pool, lvl_devs: Sequenc
 
 def prefill_plan(qo_lens, kv_lens, num_qo_heads, num_kv_heads, head_dim, page_size, level_ctas=0,
                  level_tile_q=0, enable_split=True, alpha=1, beta=1, causal=True,
-                 workspace: Workspace = None):
+                 workspace: Workspace = None, write_through=True):
     """Plan of a batch prefill: every query row is one plan request (batch = total_q, no own
     KV) and one level whose groups are the requests (qo_indptr = cumulative query lengths,
     kv_lens; causal: tiles weighed by the KV their last query sees).  level_ctas = 0 takes
     8 x floor(compute units / Hkv): a prefill level has many tiles per workgroup, and several
     rounds of 4-wave workgroups balance them better than the one 8-wave workgroup per
     compute unit that suits a decode step's level (causal 8 x 2048 at 32 heads: 585 against
-    700-760 us).  Returns (plan_info, workspace, qo_indptr list)."""
+    700-760 us).  write_through: query tiles whose KV is a single chunk write their final
+    output from the level kernel, and only the other rows go through the merge pass.  Returns
+    (plan_info, workspace, qo_indptr list)."""
     if level_ctas == 0:
         level_ctas = 8 * max(1, device_info(torch.cuda.current_device())["num_cus"] // int(num_kv_heads))
     qo_lens = [int(x) for x in qo_lens]
@@ -508,7 +513,7 @@ def prefill_plan(qo_lens, kv_lens, num_qo_heads, num_kv_heads, head_dim, page_si
     total_q = qo_indptr[-1]
     params = make_params(total_q, num_qo_heads, num_kv_heads, head_dim, page_size, num_ctas=1,
                          level_ctas=level_ctas, level_tile_q=level_tile_q, enable_split=enable_split,
-                         alpha=alpha, beta=beta)
+                         alpha=alpha, beta=beta, level_write_through=write_through)
     levels = [{"qo_indptr": qo_indptr, "kv_lens": [int(x) for x in kv_lens], "causal": bool(causal)}]
     if workspace is None:
         workspace = Workspace(params, levels)

@@ -178,6 +178,8 @@ struct PrefillLevel {
   const int32_t* qo_indptr;
   const int32_t* kv_lens;
   int32_t causal;
+  void* o;      // final output of write-through items
+  float* lse;
 };
 
 // FP8 pools (fp8 = true): k_scale folds into the softmax scale, v_scale into the state.
@@ -199,7 +201,13 @@ pkc_status run_level(const pkc_plan_info* plan, int level, const void* q, const 
     p.table_stride = pf->max_blocks;
     p.grp_qo_indptr = pf->qo_indptr;
     p.grp_kv_lens = pf->kv_lens;
+    p.o = pf->o;
+    p.lse = pf->lse;
   } else {
+    // Only batch prefill passes an output for write-through level items.
+    if (plan->lvl_write_through != 0)
+      return fail(PKC_ERR_PLAN_MISMATCH, "a plan with level write-through (batch prefill) runs only "
+                                         "through pkc_batch_prefill_paged");
     p.page_indptr = lv->kv_page_indptr;
     p.page_indices = lv->kv_page_indices;
     p.num_page_indices = lv->num_page_indices;
@@ -568,11 +576,13 @@ static pkc_status prefill_impl(bool fp8, float k_scale, float v_scale, const pkc
   if ((int64_t)max_blocks * page_size > INT32_MAX || (int64_t)max_blocks * num_requests > INT32_MAX)
     return fail(PKC_ERR_INVALID_ARG, "block table too large for int32 offsets");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const PrefillLevel pf{block_table, max_blocks, qo_indptr, kv_lens, causal ? 1 : 0};
+  const PrefillLevel pf{block_table, max_blocks, qo_indptr, kv_lens, causal ? 1 : 0, o, lse};
   if ((st = run_level(plan, 0, q, k_pool, v_pool, num_pages, nullptr, dtype, sm_scale, dev_ws, s, fp8,
                       k_scale, v_scale, &pf)) != PKC_OK)
     return st;
-  pkc::MergePlanParams m = merge_params(plan, dev_ws, 0, 1, false, o, lse);
+  // Query rows written through by their tile's only item are flagged and skipped.
+  if (plan->num_merge == 0) return PKC_OK;
+  pkc::MergePlanParams m = merge_params(plan, dev_ws, 0, 1, true, o, lse);
   return timed(2, s, "merge kernel launch", [&] { return pkc::launch_merge_plan(dtype, head_dim, m, s); });
 }
 

@@ -62,6 +62,10 @@ struct PrefixParams {
   const int32_t* grp_qo_indptr;
   const int32_t* grp_kv_lens;
   int32_t table_stride;
+  // Items with state row -1 (level write-through, batch prefill) write their query rows' final
+  // output here instead: O [rows, hq, D] in the operand type, LSE [rows, hq] fp32.
+  void* o;
+  float* lse;
 };
 
 // Plan-driven merge: request b merges merge_rows[merge_ptr[b*NL2 + l0] .. merge_ptr[b*NL2 + l1]).

@@ -11,7 +11,10 @@
 //   * a min-priority queue of (cost, CTA), ties to the smaller CTA index, receives the items
 //     in that order;
 //   * tiles with a single chunk write their state straight to the final output
-//     (write-through); every other item gets the next partial-state slot in ascending w;
+//     (write-through); every other item gets the next partial-state slot in ascending w.
+//     Cascade levels always write states (they are merged with the suffix), except when the
+//     caller asks for level write-through (batch prefill): then a level tile with a single
+//     chunk, in a plan with one level whose group has no own KV, writes the final output too;
 //   * buffers are sized from upper bounds so that their addresses never change.
 #include <algorithm>
 #include <cstring>
@@ -131,6 +134,8 @@ pkc_status check_params(const pkc_plan_params* params, bool need_ctas, Resolved*
   if (p.chunk_align < 0) return fail(PKC_ERR_INVALID_ARG, "chunk_align must be >= 0");
   if (!(p.decode_waves == 0 || p.decode_waves == 1 || p.decode_waves == 2 || p.decode_waves == 4))
     return fail(PKC_ERR_INVALID_ARG, "decode_waves must be 0, 1, 2 or 4");
+  if (!(p.level_write_through == 0 || p.level_write_through == 1))
+    return fail(PKC_ERR_INVALID_ARG, "level_write_through must be 0 or 1");
   if (p.num_ctas < 0 || p.level_ctas < 0 || p.level_tile_q < 0)
     return fail(PKC_ERR_INVALID_ARG, "num_ctas, level_ctas, level_tile_q must be >= 0");
   if (need_ctas && (p.num_ctas == 0 || p.level_ctas == 0))
@@ -245,8 +250,10 @@ pkc_status build_plan_host(const Resolved& r, const int32_t* kv_lens_h,
   P.num_ctas = p.num_ctas;
   P.level_ctas = p.level_ctas;
 
-  // Levels: every item gets a state block of T_q rows; rows numbered level by level.
+  // Levels: every item gets a state block of T_q rows (rows numbered level by level), except
+  // write-through level items, which write their rows' final output.
   std::vector<Stage> lv(num_levels);
+  std::vector<int32_t> flags(B, 0);   // 1: the request's output is written by one item
   int32_t row = 0;
   for (int32_t l = 0; l < num_levels; ++l) {
     const pkc_level_host& h = levels[l];
@@ -261,10 +268,37 @@ pkc_status build_plan_host(const Resolved& r, const int32_t* kv_lens_h,
     P.lvl_items[l] = (int32_t)lv[l].items.size();
     P.lvl_kv_chunk[l] = lv[l].kv_chunk;
     P.lvl_row_base[l] = row;
-    for (Item& it : lv[l].items) {
+    // Write-through candidates: groups none of whose requests has own KV, when this is the
+    // plan's only level; among their items, those whose tile has a single chunk.
+    std::vector<char> wt_group(h.num_groups, 0);
+    if (p.level_write_through && num_levels == 1) {
+      for (int32_t g = 0; g < h.num_groups; ++g) {
+        bool own = false;
+        for (int32_t b = h.qo_indptr[g]; b < h.qo_indptr[g + 1]; ++b) own = own || kv_lens_h[b] > 0;
+        wt_group[g] = own ? 0 : 1;
+      }
+    }
+    // Chunks per tile: the items of one tile are consecutive in w order.
+    std::vector<int32_t> chunks_of(lv[l].items.size(), 0);
+    for (size_t i = 0; i < lv[l].items.size();) {
+      size_t j = i;
+      while (j < lv[l].items.size() && lv[l].items[j].req == lv[l].items[i].req &&
+             lv[l].items[j].tile == lv[l].items[i].tile)
+        ++j;
+      for (size_t k = i; k < j; ++k) chunks_of[k] = (int32_t)(j - i);
+      i = j;
+    }
+    for (size_t i = 0; i < lv[l].items.size(); ++i) {
+      Item& it = lv[l].items[i];
       it.q0 += h.qo_indptr[it.req];
-      it.row = row;
-      row += p.level_tile_q;
+      if (wt_group[it.req] && chunks_of[i] == 1) {
+        it.row = -1;
+        for (int32_t q = 0; q < it.nq; ++q) flags[it.q0 + q] = 1;
+        ++P.lvl_write_through;
+      } else {
+        it.row = row;
+        row += p.level_tile_q;
+      }
     }
   }
   // Decode stage over every request's own KV (one query per request, T_q = 1).
@@ -276,7 +310,6 @@ pkc_status build_plan_host(const Resolved& r, const int32_t* kv_lens_h,
   for (const Item& it : dec.items) chunks[it.req]++;
   P.dec_row_base = row;
   int32_t slots = 0;
-  std::vector<int32_t> flags(B, 0);
   // A request whose own KV is a single chunk is finished by that chunk's workgroup: it folds
   // in the request's level states (its merge list) and writes the final output.
   for (Item& it : dec.items) {
@@ -328,8 +361,9 @@ pkc_status build_plan_host(const Resolved& r, const int32_t* kv_lens_h,
   std::vector<std::vector<int32_t>> per_req_lvl((size_t)B * (num_levels + 1));
   for (int32_t l = 0; l < num_levels; ++l)
     for (const Item& it : lv[l].items)
-      for (int32_t q = 0; q < it.nq; ++q)
-        per_req_lvl[(size_t)(it.q0 + q) * (num_levels + 1) + l].push_back(it.row + q);
+      if (it.row >= 0)
+        for (int32_t q = 0; q < it.nq; ++q)
+          per_req_lvl[(size_t)(it.q0 + q) * (num_levels + 1) + l].push_back(it.row + q);
   for (const Item& it : dec.items)
     if (it.row >= 0) per_req_lvl[(size_t)it.req * (num_levels + 1) + num_levels].push_back(it.row);
   int32_t* rlev = reinterpret_cast<int32_t*>(base + L.off_req_levels);

@@ -670,16 +670,30 @@ __global__ __launch_bounds__(64 * prefix_detail::kWavesPerStream * NS, NS == 1 ?
         if (r < nrows) {
           float inv = lt > 0.f ? 1.f / lt : 0.f;
           if constexpr (F8) inv *= p.v_scale;
-          const int64_t srow_q = (int64_t)srow + r / G;
           const int h = hk * G + r % G;
-          float* dst = p.st_o + (srow_q * p.hq + h) * D;
+          const float lse_r = lt > 0.f ? (m_run[nt] + log2f(lt)) * kLn2 : kNegInf;
+          if (srow >= 0) {
+            const int64_t srow_q = (int64_t)srow + r / G;
+            float* dst = p.st_o + (srow_q * p.hq + h) * D;
 #pragma unroll
-          for (int dm = 0; dm < DM; ++dm) {
-            const f4_t o = oacc[dm][nt] * inv;
-            *reinterpret_cast<float4*>(dst + dm * 16 + 4 * lg) = make_float4(o[0], o[1], o[2], o[3]);
+            for (int dm = 0; dm < DM; ++dm) {
+              const f4_t o = oacc[dm][nt] * inv;
+              *reinterpret_cast<float4*>(dst + dm * 16 + 4 * lg) = make_float4(o[0], o[1], o[2], o[3]);
+            }
+            if (lg == 0) p.st_lse[srow_q * p.hq + h] = lse_r;
+          } else if (p.o) {
+            // Write-through: the tile is its rows' only item, so this is their final output
+            // (O rounded once to the operand type).
+            const int64_t orow = (int64_t)q0 + r / G;
+            char* dst = static_cast<char*>(p.o) + (orow * p.hq + h) * (D * ES);
+#pragma unroll
+            for (int dm = 0; dm < DM; ++dm) {
+              const f4_t o = oacc[dm][nt] * inv;
+              *reinterpret_cast<uint2*>(dst + (dm * 16 + 4 * lg) * ES) =
+                  make_uint2(Mfma<T>::pack(o[0], o[1]), Mfma<T>::pack(o[2], o[3]));
+            }
+            if (lg == 0) p.lse[orow * p.hq + h] = lse_r;
           }
-          if (lg == 0)
-            p.st_lse[srow_q * p.hq + h] = lt > 0.f ? (m_run[nt] + log2f(lt)) * kLn2 : kNegInf;
         }
       }
     }

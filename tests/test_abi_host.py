@@ -75,7 +75,8 @@ def _compare_plan(api, info, hb, o, levels, tile_q):
                 [(w, st.items[w].req, st.items[w].tile, st.items[w].kv_begin, st.items[w].kv_end) for w in exp]
             for r in recs:
                 it = st.items[r[7]]
-                assert r[5] == info.lvl_row_base[l] + st.slots[it.w] * tile_q
+                slot = st.slots[it.w]
+                assert r[5] == (-1 if slot < 0 else info.lvl_row_base[l] + slot * tile_q)
                 assert r[1] == qi[it.req] + it.tile * tile_q and r[2] == it.lq
     # merge lists and flags
     nl = len(levels)
@@ -157,11 +158,16 @@ def test_causal_prefill_plan_matches_oracle(api, seed):
     tile_q = rng.choice([0, 4, 16 // g])
     lctas = rng.choice([1, 5, 32])
     levels = [{"qo_indptr": qi, "kv_lens": kv, "causal": seed % 4 != 3}]
-    p = api.make_params(T, 4 * g, 4, 128, 16, num_ctas=1, level_ctas=lctas, level_tile_q=tile_q)
+    wt = seed % 3 != 0
+    p = api.make_params(T, 4 * g, 4, 128, 16, num_ctas=1, level_ctas=lctas, level_tile_q=tile_q,
+                        level_write_through=wt)
     info, hb = api.plan_host(p, [0] * T, levels)
     tq = tile_q or 128 // g
-    o = oplan.cascade_plan(T, levels, [0] * T, num_ctas=1, level_ctas=lctas, level_tile_q=[tq], alpha=1, beta=1)
+    o = oplan.cascade_plan(T, levels, [0] * T, num_ctas=1, level_ctas=lctas, level_tile_q=[tq], alpha=1, beta=1,
+                           level_write_through=wt)
     _compare_plan(api, info, hb, o, levels, tq)
+    n_wt = sum(1 for s in o.levels[0].slots if s < 0)
+    assert info.lvl_write_through == n_wt and (wt or n_wt == 0)
 
 
 def test_standard_workload_plans_match_oracle(api):

@@ -54,11 +54,11 @@ def _case(seed, lq, lkv, dtype, D, g, P, hkv=2, scale=1.0):
     return q, k, v, bt
 
 
-def _run(api, q, k, v, bt, lq, lkv, causal, level_ctas=0, tile_q=0):
+def _run(api, q, k, v, bt, lq, lkv, causal, level_ctas=0, tile_q=0, write_through=True):
     T, Hq, D = q.shape
     P, Hkv = k.shape[1], k.shape[2]
     info, ws, qi = api.prefill_plan(lq, lkv, Hq, Hkv, D, P, level_ctas=level_ctas, level_tile_q=tile_q,
-                                    causal=causal)
+                                    causal=causal, write_through=write_through)
     qi_d = torch.tensor(qi, dtype=torch.int32, device="cuda")
     kv_d = torch.tensor(lkv, dtype=torch.int32, device="cuda")
     o, lse = api.batch_prefill_paged(info, q, k, v, bt.cuda(), qi_d, kv_d, causal=causal,
@@ -143,3 +143,33 @@ def test_prefill_rejects_plan_of_other_shape(api):
         api.batch_prefill_paged(info, q.float(), k.float(), v.float(), bt.cuda(), qi_d, kv_d)
     with pytest.raises(api.PkcError):   # a causal plan run without the mask
         api.batch_prefill_paged(info, q, k, v, bt.cuda(), qi_d, kv_d, causal=False)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_write_through_and_merged_rows_agree(api, causal):
+    """Tiles whose KV is one chunk write their rows' output from the level kernel; the same
+    batch planned without write-through sends every row through the merge pass.  Both match
+    the oracle, and the write-through plan merges fewer rows."""
+    lq, lkv = [300, 5, 130, 1, 64], [300, 900, 17, 0, 2000]
+    say(f"case: prefill write-through vs merged, causal={causal}, bf16 D128 g2 P16 lq={lq} lkv={lkv}")
+    q, k, v, bt = _case(77, lq, lkv, torch.bfloat16, 128, 2, 16)
+    res = {}
+    for wt in (True, False):
+        res[wt] = _run(api, q, k, v, bt, lq, lkv, causal, level_ctas=8, write_through=wt)
+    info_wt, info_m = res[True][3], res[False][3]
+    assert info_wt.lvl_write_through > 0 and info_m.lvl_write_through == 0
+    assert info_wt.num_merge < info_m.num_merge == sum(lq)
+    O, L = _oracle(q, k, v, bt, res[True][2], lkv, causal)
+    for wt in (True, False):
+        check_state(res[wt][0], res[wt][1], O, L, torch.bfloat16, f"write_through={wt}")
+
+
+def test_write_through_plan_runs_only_as_prefill(api):
+    say("case: a level write-through plan is rejected by prefix_attention before any launch")
+    lq, lkv = [3, 2], [4, 9]
+    q, k, v, bt = _case(5, lq, lkv, torch.float16, 64, 1, 4)
+    info, ws, qi = api.prefill_plan(lq, lkv, 2, 2, 64, 4, level_ctas=2)
+    assert info.lvl_write_through > 0
+    d, keep = api.level_dev({"kv_page_indptr": [0, 1, 2], "kv_page_indices": [0, 1]})
+    with pytest.raises(api.PkcError):
+        api.prefix_attention(info, 0, q, k, v, d)

@@ -216,3 +216,27 @@ def test_causal_extent_is_the_last_querys_visible_length(seed):
                 else:
                     assert segs[0][0] == 0 and segs[-1][1] == n
                     assert all(a[1] == b[0] for a, b in zip(segs, segs[1:]))
+
+
+def test_level_write_through_hand_example():
+    """Prefill-shaped plan (one level, no own KV): query lengths [3, 1], KV lengths [3, 40],
+    T_q = 2, #CTA = 2.  S = 2 * 3 + 1 * 40 = 46, L = 23: request 0's two tiles are one chunk
+    each and write through; request 1's tile is cut into [0, 23) and [23, 40), whose states
+    take slots 0 and 1 and are merged.  Worked by hand from the scheduler's steps."""
+    levels = [{"qo_indptr": [0, 3, 4], "kv_lens": [3, 40]}]
+    o = plan.cascade_plan(4, levels, [0] * 4, num_ctas=1, level_ctas=2, level_tile_q=[2],
+                          level_write_through=True)
+    st = o.levels[0]
+    assert st.kv_chunk == 23
+    assert [(it.req, it.tile, it.kv_begin, it.kv_end) for it in st.items] == \
+        [(0, 0, 0, 3), (0, 1, 0, 3), (1, 0, 0, 23), (1, 0, 23, 40)]
+    assert st.slots == [-1, -1, 0, 1]
+    assert o.write_through == [True, True, True, False]
+    assert o.merge == [[], [], [], [(0, 0, 0), (0, 1, 0)]]
+    # Without the flag, or with a second level, or with own KV in the group, nothing writes
+    # through at the level.
+    o2 = plan.cascade_plan(4, levels, [0] * 4, num_ctas=1, level_ctas=2, level_tile_q=[2])
+    assert o2.levels[0].slots == [0, 1, 2, 3] and not any(o2.write_through)
+    o3 = plan.cascade_plan(4, levels, [0, 0, 5, 0], num_ctas=1, level_ctas=2, level_tile_q=[2],
+                           level_write_through=True)
+    assert o3.levels[0].slots == [0, 1, 2, 3]
