@@ -17,8 +17,9 @@ back, and with the last-level cache evicted before each run); the same step with
 cascade (every request reads the shared prefix through its own full page list) with the
 largest output difference between the two; the in-place append of one token per request; and
 the LLaMA2-7B decode shape (64 x 4096 tokens) over fp16 pools and over FP8 E4M3 pools; and
-the same cascade step over FP8 E4M3 pools; and a causal prefill of ragged multi-token queries
-(matrix-core TFLOP/s).
+the same cascade step over FP8 E4M3 pools; a causal prefill of ragged multi-token queries
+(matrix-core TFLOP/s); and the load-balanced split-KV decode with grouped heads (256 requests,
+32 / 8 heads, bf16, log-uniform lengths 128..32768).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 """
@@ -231,6 +232,47 @@ def noncascade_comparison(api, w, step, info, runs=5):
     return {"ms_per_step": round(ms, 4), "alg_kv_bytes_per_step": nbytes,
             "alg_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1), "runs": runs,
             "max_abs_diff_vs_cascade": {"o": d_o, "lse": d_l}}
+
+
+def gqa_decode_timing(api, workloads, runs=20):
+    """Load-balanced split-KV decode with grouped heads: 256 requests, 32 query / 8 KV heads,
+    bf16, lengths log-uniform in [128, 32768], through the plan over #CTA = 2 x compute units
+    (alpha = beta = 1) and over the library's default #CTA; algorithmic bytes = every request's
+    K and V once."""
+    import torch
+    w = workloads.gqa_split(device="cuda")
+    lens = w.cache_seqlens.cpu().tolist()
+    alg = sum(lens) * w.num_kv_heads * w.head_dim * 2 * w.esize
+    cus = api.device_info(0)["num_cus"]
+    o = torch.empty_like(w.q)
+    lse = torch.empty(w.batch, w.num_qo_heads, dtype=torch.float32, device="cuda")
+    out = {"workload": w.name, "alg_bytes": alg}
+    for name, nc in (("plan_2x_cus", 2 * cus), ("plan_default", 0)):
+        params = api.make_params(w.batch, w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size,
+                                 num_ctas=nc, alpha=1, beta=1)
+        ws = api.Workspace(params)
+        info = api.plan(params, lens, workspace=ws)
+
+        def run():
+            api.batch_decode_paged(w.q, w.k_pool, w.v_pool, w.block_table, w.cache_seqlens,
+                                   sm_scale=w.sm_scale, plan_info=info, out=o, lse=lse)
+
+        for _ in range(5):
+            run()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(runs):
+            run()
+        b.record()
+        torch.cuda.synchronize()
+        us = 1e3 * a.elapsed_time(b) / runs
+        out[name] = {"num_ctas": info.num_ctas, "items": info.dec_items, "merged_requests": info.num_merge,
+                     "us_per_run": round(us, 1), "alg_GBps": round(alg / us / 1e3, 1),
+                     "frac_of_peak": round(alg / us / 1e3 / PEAK_HBM_GBPS, 4)}
+    del w
+    torch.cuda.empty_cache()
+    return out
 
 
 def fp8_decode_comparison(api, workloads, runs=10):
@@ -506,6 +548,7 @@ def main():
     fp8c = fp8_cascade_timing(api, workloads, w, step, info)
     pre = prefill_timing(api)
     fp8 = fp8_decode_comparison(api, workloads)
+    gqa = gqa_decode_timing(api, workloads)
 
     # The device's achievable read rate: one nontemporal 16-byte-load stream over 2 GiB.
     buf = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
@@ -553,6 +596,7 @@ def main():
         "noncascade_same_step": nonc,
         "append_kv": app,
         "fp8_kv_decode": fp8,
+        "gqa_split_decode": gqa,
         "fp8_kv_cascade": fp8c,
         "prefill": pre,
         "kernel_source_hash": src_hash,
