@@ -116,3 +116,38 @@ def append_kv(k_pool, v_pool, k_new, v_new, block_table, cache_seqlens, page_siz
         v[tgt[0], tgt[1]] = v_new[b]
         lens[b] += 1
     return k, v, lens
+
+
+def append_kv_ragged(k_pool, v_pool, k_new, v_new, new_indptr, block_table, cache_seqlens,
+                     page_size):
+    """Multi-token append (prefill / append path over the paged cache): request b's new rows
+    k_new[new_indptr[b] + i], v_new[...] (i < n_b = new_indptr[b+1] - new_indptr[b]) go to
+    token positions cache_seqlens[b] + i, i.e. block (cache_seqlens[b] + i) // P of its
+    block-table row at slot (cache_seqlens[b] + i) % P -- the rule of the "Paged attention"
+    page's next-token bullets applied to every new token in order.  Reading adopted for
+    failures: a request all of whose target blocks are allocated (inside the row, not -1, a
+    page of the pool) writes every row and its length becomes cache_seqlens[b] + n_b; otherwise
+    it writes nothing and keeps its length (with n_b = 1 this is the one-token append above).
+    Returns copies of the pools and the new lengths."""
+    k = np.array(k_pool, copy=True)
+    v = np.array(v_pool, copy=True)
+    num_pages = k.shape[0]
+    lens = [int(x) for x in cache_seqlens]
+    for b, row in enumerate(block_table):
+        lo, hi = int(new_indptr[b]), int(new_indptr[b + 1])
+        targets = []
+        for i in range(hi - lo):
+            t = lens[b] + i
+            j = t // page_size
+            page = int(row[j]) if j < len(row) else -1
+            if page < 0 or page >= num_pages:
+                targets = None
+                break
+            targets.append((page, t % page_size))
+        if targets is None:
+            continue
+        for i, (page, slot) in enumerate(targets):
+            k[page, slot] = k_new[lo + i]
+            v[page, slot] = v_new[lo + i]
+        lens[b] += hi - lo
+    return k, v, lens

@@ -439,3 +439,62 @@ def test_gqa_head_map_is_contiguous():
     v_pool[:, :, 1, 0] = 2.0
     O, _ = attention.batch_decode(rng.normal(size=(1, 4, 4)), k_pool, v_pool, [[0, 1]], [7], P, 1.0)
     assert np.allclose(O[0, :, 0], [1, 1, 2, 2], atol=1e-14)
+
+
+def test_ragged_append_of_one_token_each_equals_the_one_token_append():
+    g = _golden("hf_paged_decode_example.json")
+    P = g["page_size"]
+    rng = np.random.default_rng(5)
+    k_pool = rng.normal(size=(8, P, 1, 4))
+    v_pool = rng.normal(size=(8, P, 1, 4))
+    k_new = rng.normal(size=(3, 1, 4))
+    v_new = rng.normal(size=(3, 1, 4))
+    a = indexing.append_kv(k_pool, v_pool, k_new, v_new, g["block_table"], g["cache_seqlens"], P)
+    b = indexing.append_kv_ragged(k_pool, v_pool, k_new, v_new, [0, 1, 2, 3], g["block_table"],
+                                  g["cache_seqlens"], P)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]) and a[2] == b[2]
+
+
+def test_ragged_append_on_the_worked_example():
+    """Sequence 0 (30 tokens in page 2, block 1 unallocated) appends 2 tokens: slots 30 and 31
+    of page 2.  Sequence 1 (32 tokens, pre-allocated block 1 = page 1) appends 3: page 1 slots
+    0..2.  Sequence 2 (70 tokens over pages 3, 5, 6) appends 1: page 6 slot 6.  A third token
+    for sequence 0 would need block 1 (-1): then sequence 0 writes nothing."""
+    g = _golden("hf_paged_decode_example.json")
+    P = g["page_size"]
+    k_pool = np.zeros((8, P, 1, 2))
+    ids = np.arange(1, 7, dtype=np.float64)
+    k_new = np.stack([np.full((1, 2), x) for x in ids])
+    k2, _, lens = indexing.append_kv_ragged(k_pool, k_pool, k_new, k_new, [0, 2, 5, 6], g["block_table"],
+                                            g["cache_seqlens"], P)
+    assert lens == [32, 35, 71]
+    assert [tuple(x) for x in np.argwhere(k2[..., 0, 0] != 0).tolist()] == \
+        [(1, 0), (1, 1), (1, 2), (2, 30), (2, 31), (6, 6)]
+    assert [k2[2, 30, 0, 0], k2[2, 31, 0, 0], k2[1, 0, 0, 0], k2[1, 2, 0, 0], k2[6, 6, 0, 0]] == [1, 2, 3, 5, 6]
+    k3, _, lens3 = indexing.append_kv_ragged(k_pool, k_pool, np.ones((4, 1, 2)), np.ones((4, 1, 2)),
+                                             [0, 3, 3, 4], g["block_table"], g["cache_seqlens"], P)
+    assert lens3 == [30, 32, 71] and not k3[2].any() and k3[6, 6].all()
+
+
+def test_ragged_append_then_attention_sees_every_new_token():
+    """Brute force: after the append, walking each request's first new-length tokens through
+    the block table gives the old rows followed by exactly the new rows, in order."""
+    rng = np.random.default_rng(9)
+    P, B = 4, 5
+    bt = np.full((B, 6), -1, dtype=np.int32)
+    perm = rng.permutation(30)
+    lens = [3, 0, 8, 5, 1]
+    new = [6, 2, 0, 9, 3]
+    for b in range(B):
+        n = -(-(lens[b] + new[b]) // P)
+        bt[b, :n] = perm[6 * b: 6 * b + n]
+    k_pool = rng.normal(size=(30, P, 2, 2))
+    indptr = np.concatenate([[0], np.cumsum(new)])
+    k_new = rng.normal(size=(int(indptr[-1]), 2, 2))
+    k2, _, lens2 = indexing.append_kv_ragged(k_pool, k_pool, k_new, k_new, indptr, bt, lens, P)
+    assert lens2 == [lens[b] + new[b] for b in range(B)]
+    for b in range(B):
+        rows = [k2[bt[b, t // P], t % P] for t in range(lens2[b])]
+        old = [k_pool[bt[b, t // P], t % P] for t in range(lens[b])]
+        assert all(np.array_equal(x, y) for x, y in zip(rows[:lens[b]], old))
+        assert all(np.array_equal(rows[lens[b] + i], k_new[indptr[b] + i]) for i in range(new[b]))
