@@ -438,6 +438,28 @@ pkc_status pkc_append_kv(const void* k_new, const void* v_new, void* k_pool, voi
                          pkc_dtype dtype, void* stream);
 
 /*
+ * Multi-token in-place append (the append / prefill path; "Paged attention" page, decode path:
+ * the cache is updated in place at the next-token position of each sequence, applied here to
+ * every new token in order).  Request b's new rows are k_new / v_new rows new_indptr[b] ..
+ * new_indptr[b+1]-1 ([total_new, Hkv, D] each, the dtype of the pools); row new_indptr[b] + i
+ * goes to row (block_table[b][(cache_seqlens[b] + i) / P], (cache_seqlens[b] + i) % P) of
+ * k_pool and v_pool, and new_seqlens[b] = cache_seqlens[b] + n_b (n_b = new_indptr[b+1] -
+ * new_indptr[b]); a prefill over new_seqlens then attends over the new tokens.  A request with
+ * a missing target block (outside the row, -1, or a page outside [0, num_pages)), or with an
+ * inconsistent row range (decreasing indptr, rows past total_new), is a caller error: nothing
+ * is written for it and new_seqlens[b] keeps the old length.  new_seqlens may be NULL and must
+ * not alias cache_seqlens.  new_indptr, cache_seqlens, new_seqlens and the tensors are device
+ * pointers owned by the caller; the work is enqueued on `stream`.  Returns
+ * PKC_ERR_INVALID_ARG / PKC_ERR_UNSUPPORTED on bad sizes, NULL pointers or aliasing.
+ */
+pkc_status pkc_append_kv_ragged(const void* k_new, const void* v_new, int64_t total_new,
+                                const int32_t* new_indptr, void* k_pool, void* v_pool,
+                                int64_t num_pages, const int32_t* block_table, int32_t max_blocks,
+                                const int32_t* cache_seqlens, int32_t* new_seqlens, int32_t batch,
+                                int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                                pkc_dtype dtype, void* stream);
+
+/*
  * Host-side check of block-table contents (host arrays): every block holding one of the
  * tokens [kv_start[b], cache_seqlens[b]) must name a page in [0, num_pages).  Returns
  * PKC_ERR_INVALID_ARG naming the first bad (request, block) otherwise.  Not on the hot path.

@@ -120,6 +120,8 @@ SIGNATURES = {
     "pkc_timing_read": (_I32, [_I32, ctypes.POINTER(_I64), ctypes.POINTER(ctypes.c_double)]),
     "pkc_read_stream_probe": (_I32, [_P, _I64, _P, _I64, _P]),
     "pkc_append_kv": (_I32, [_P, _P, _P, _P, _I64, _P, _I32, _P, _P, _I32, _I32, _I32, _I32, _I32, _P]),
+    "pkc_append_kv_ragged": (_I32, [_P, _P, _I64, _P, _P, _P, _I64, _P, _I32, _P, _P, _I32, _I32, _I32,
+                                    _I32, _I32, _P]),
     "pkc_batch_decode_paged_fp8": (_I32, [ctypes.POINTER(PlanInfo), _P, _P, _P, _F, _F, _I64, _P, _I32,
                                           _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _F, _P, _P, _P,
                                           _SZ, _P]),
@@ -325,6 +327,33 @@ def append_kv(k_new, v_new, k_pool, v_pool, block_table, cache_seqlens, new_seql
     _check(lib.pkc_append_kv(_ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), N, _ptr(block_table),
                              block_table.shape[1], _ptr(cache_seqlens), _ptr(new_seqlens), B, Hkv, D, P,
                              dtype_code(k_pool.dtype), _stream(dev)))
+    return new_seqlens
+
+
+
+def append_kv_ragged(k_new, v_new, new_indptr, k_pool, v_pool, block_table, cache_seqlens,
+                     new_seqlens=None):
+    """pkc_append_kv_ragged: request b's new rows k_new / v_new[new_indptr[b] .. new_indptr[b+1])
+    ([total_new, Hkv, D]) go to positions cache_seqlens[b] + i of its block-table row, in place.
+    new_indptr and cache_seqlens are int32 device tensors.  Returns the new lengths (allocated
+    when None; must not be cache_seqlens)."""
+    T, Hkv, D = k_new.shape
+    N, P, Hkv2, D2 = k_pool.shape
+    dev = k_pool.device
+    if (Hkv, D) != (Hkv2, D2) or tuple(v_new.shape) != tuple(k_new.shape) or tuple(v_pool.shape) != tuple(k_pool.shape):
+        raise PkcError(1, "append_kv_ragged: shape mismatch")
+    for t, n in ((k_new, "k_new"), (v_new, "v_new"), (k_pool, "k_pool"), (v_pool, "v_pool")):
+        _need(t, n, k_pool.dtype, dev)
+    for t, n in ((block_table, "block_table"), (cache_seqlens, "cache_seqlens"), (new_indptr, "new_indptr")):
+        _need(t, n, torch.int32, dev)
+    B = cache_seqlens.numel()
+    if new_indptr.numel() != B + 1:
+        raise PkcError(1, "append_kv_ragged: new_indptr must have batch + 1 entries")
+    if new_seqlens is None:
+        new_seqlens = torch.empty_like(cache_seqlens)
+    _check(lib.pkc_append_kv_ragged(_ptr(k_new), _ptr(v_new), T, _ptr(new_indptr), _ptr(k_pool), _ptr(v_pool),
+                                    N, _ptr(block_table), block_table.shape[1], _ptr(cache_seqlens),
+                                    _ptr(new_seqlens), B, Hkv, D, P, dtype_code(k_pool.dtype), _stream(dev)))
     return new_seqlens
 
 

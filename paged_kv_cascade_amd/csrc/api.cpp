@@ -843,6 +843,45 @@ pkc_status pkc_append_kv(const void* k_new, const void* v_new, void* k_pool, voi
   PKC_TRY_END("pkc_append_kv")
 }
 
+pkc_status pkc_append_kv_ragged(const void* k_new, const void* v_new, int64_t total_new,
+                                const int32_t* new_indptr, void* k_pool, void* v_pool,
+                                int64_t num_pages, const int32_t* block_table, int32_t max_blocks,
+                                const int32_t* cache_seqlens, int32_t* new_seqlens, int32_t batch,
+                                int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                                pkc_dtype dtype, void* stream) {
+  PKC_TRY_BEGIN
+  if (batch < 0 || batch > 65535 || num_kv_heads <= 0 || max_blocks < 0 || num_pages < 0 || total_new < 0)
+    return fail(PKC_ERR_INVALID_ARG, "append: bad sizes (batch must be in [0, 65535])");
+  if (!(head_dim == 64 || head_dim == 128)) return fail(PKC_ERR_UNSUPPORTED, "append: head_dim must be 64 or 128");
+  if (!pkc::is_pow2(page_size) || page_size > 1024)
+    return fail(PKC_ERR_UNSUPPORTED, "append: page_size must be a power of two in [1, 1024]");
+  if (dtype != PKC_F32 && dtype != PKC_F16 && dtype != PKC_BF16) return fail(PKC_ERR_UNSUPPORTED, "append: dtype");
+  if (batch == 0) return PKC_OK;
+  if (!k_new || !v_new || !k_pool || !v_pool || !block_table || !cache_seqlens || !new_indptr)
+    return fail(PKC_ERR_INVALID_ARG, "append: NULL pointer");
+  if (new_seqlens == cache_seqlens)
+    return fail(PKC_ERR_INVALID_ARG, "append: new_seqlens must not alias cache_seqlens (several "
+                                     "workgroups of a request read its old length)");
+  pkc::AppendRaggedParams p{};
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.k_pool = k_pool;
+  p.v_pool = v_pool;
+  p.num_pages = num_pages;
+  p.block_table = block_table;
+  p.max_blocks = max_blocks;
+  p.page_shift = log2i(page_size);
+  p.seqlens = cache_seqlens;
+  p.new_indptr = new_indptr;
+  p.total_new = total_new;
+  p.seqlens_out = new_seqlens;
+  p.row_bytes = (int64_t)num_kv_heads * head_dim * (dtype == PKC_F32 ? 4 : 2);
+  hipError_t e = pkc::launch_append_kv_ragged(p, batch, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  return PKC_OK;
+  PKC_TRY_END("pkc_append_kv_ragged")
+}
+
 pkc_status pkc_read_stream_probe(const void* src, int64_t bytes, uint32_t* sink, int64_t sink_len,
                                  void* stream) {
   PKC_TRY_BEGIN

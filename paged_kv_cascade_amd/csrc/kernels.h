@@ -108,6 +108,23 @@ struct AppendParams {
   int64_t row_bytes;         // multiple of 16
 };
 
+// Multi-token append: request b's rows new_indptr[b] .. new_indptr[b+1]-1 of k_new / v_new.
+struct AppendRaggedParams {
+  const void* k_new;
+  const void* v_new;
+  void* k_pool;
+  void* v_pool;
+  int64_t num_pages;
+  const int32_t* block_table;
+  int32_t max_blocks;
+  int32_t page_shift;
+  const int32_t* seqlens;
+  const int32_t* new_indptr;   // [B+1]
+  int64_t total_new;           // rows of k_new / v_new
+  int32_t* seqlens_out;        // nullable; never aliases seqlens
+  int64_t row_bytes;           // multiple of 16
+};
+
 hipError_t launch_decode(pkc_dtype dt, int head_dim, int group, int waves, const DecodeParams& p,
                          int grid_x, hipStream_t s);
 // OCP FP8 E4M3 pools; q_dt (fp16 or bf16) is the type of q and o.
@@ -135,6 +152,7 @@ hipError_t launch_merge_inplace(pkc_dtype dt, int head_dim, void* o_a, float* ls
 // Copies `bytes` (a multiple of 16, 16-byte aligned) from pinned host memory to the device.
 hipError_t launch_plan_upload(const void* host_src, void* dev_dst, int64_t bytes, hipStream_t s);
 hipError_t launch_append_kv(const AppendParams& p, int32_t batch, hipStream_t s);
+hipError_t launch_append_kv_ragged(const AppendRaggedParams& p, int32_t batch, hipStream_t s);
 // Reads `mib` MiB of src (16-byte aligned) once as a nontemporal stream; sink gets mib * 256
 // uint32 values.
 hipError_t launch_read_stream(const void* src, int64_t mib, uint32_t* sink, hipStream_t s);

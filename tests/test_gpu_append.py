@@ -105,3 +105,103 @@ def test_append_to_unallocated_block_is_skipped(api):
     ones = torch.ones(3, H, D, device="cuda")
     new = _append_and_check(api, k_pool, v_pool, ones, ones, bt, lens, P)
     assert new.cpu().tolist() == [4, 8, 4] and not k_pool.any() and not v_pool.any()
+
+
+# --- multi-token (ragged) append ----------------------------------------------------------------
+
+def _ragged_case(seed, dtype, B, P, hkv=4, D=64):
+    """Random ragged append: per request an old length, a number of new rows (some 0), a table
+    row with room for them except for one request whose next block is -1 (all-or-nothing)."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(0, 3 * P, size=B)
+    new = rng.choice([0, 1, 3, P, 2 * P + 1, 5 * P], size=B)
+    nblk = [-(-(int(lens[b]) + int(new[b])) // P) for b in range(B)]
+    width = max(nblk + [1]) + 1
+    num_pages = sum(nblk) + 4
+    perm = rng.permutation(num_pages)
+    bt = np.full((B, width), -1, dtype=np.int32)
+    off = 0
+    for b in range(B):
+        bt[b, :nblk[b]] = perm[off:off + nblk[b]]
+        off += nblk[b]
+    holes = [b for b in range(B) if new[b] > 0 and (int(lens[b]) + int(new[b]) - 1) // P > int(lens[b]) // P]
+    if holes:   # one request loses its last target block: it must write nothing
+        b = holes[0]
+        bt[b, (int(lens[b]) + int(new[b]) - 1) // P] = -1
+    indptr = np.concatenate([[0], np.cumsum(new)]).astype(np.int32)
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    k_pool = torch.randn(num_pages, P, hkv, D, generator=g, device="cuda").to(dtype)
+    v_pool = torch.randn(num_pages, P, hkv, D, generator=g, device="cuda").to(dtype)
+    k_new = torch.randn(int(indptr[-1]), hkv, D, generator=g, device="cuda").to(dtype)
+    v_new = torch.randn(int(indptr[-1]), hkv, D, generator=g, device="cuda").to(dtype)
+    return k_pool, v_pool, k_new, v_new, bt, lens.astype(np.int32), indptr, holes[:1]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_ragged_append_matches_oracle_bitwise(api, seed):
+    dtype = [torch.float16, torch.bfloat16, torch.float32][seed % 3]
+    P = [16, 4, 1][seed % 3] if seed < 3 else [32, 8, 2][seed % 3]
+    B = 7
+    say(f"case: ragged append seed={seed} {dtype} P={P} B={B}")
+    k_pool, v_pool, k_new, v_new, bt, lens, indptr, holes = _ragged_case(1500 + seed, dtype, B, P)
+    k_ref, v_ref, lens_ref = oidx.append_kv_ragged(_bits(k_pool), _bits(v_pool), _bits(k_new), _bits(v_new),
+                                                   indptr.tolist(), bt.tolist(), lens.tolist(), P)
+    for b in holes:
+        assert lens_ref[b] == lens[b]
+    new = api.append_kv_ragged(k_new, v_new, torch.tensor(indptr, device="cuda"), k_pool, v_pool,
+                               torch.tensor(bt, device="cuda"), torch.tensor(lens, device="cuda"))
+    torch.cuda.synchronize()
+    assert new.cpu().tolist() == lens_ref
+    assert np.array_equal(_bits(k_pool), k_ref), "K pool differs from the oracle's append (bitwise)"
+    assert np.array_equal(_bits(v_pool), v_ref), "V pool differs from the oracle's append (bitwise)"
+
+
+def test_ragged_append_then_causal_prefill(api):
+    """Append each request's new tokens, then run the causal prefill of those tokens over the
+    new lengths: equal to the oracle's prefill over the oracle-appended pools."""
+    import math
+    B, P, hkv, g, D = 4, 16, 2, 2, 128
+    lens = [0, 37, 100, 5]
+    new = [40, 1, 77, 16]
+    say(f"case: ragged append then causal prefill, lens={lens} new={new} fp16 P={P}")
+    nblk = [-(-(lens[b] + new[b]) // P) for b in range(B)]
+    perm = torch.randperm(sum(nblk) + 2, generator=torch.Generator().manual_seed(3)).tolist()
+    bt = torch.full((B, max(nblk) + 1), -1, dtype=torch.int32)
+    off = 0
+    for b in range(B):
+        bt[b, :nblk[b]] = torch.tensor(perm[off:off + nblk[b]], dtype=torch.int32)
+        off += nblk[b]
+    gen = torch.Generator(device="cuda").manual_seed(4)
+    num_pages = sum(nblk) + 2
+    k_pool = (torch.randn(num_pages, P, hkv, D, generator=gen, device="cuda") * 0.5).half()
+    v_pool = (torch.randn(num_pages, P, hkv, D, generator=gen, device="cuda") * 0.5).half()
+    T = sum(new)
+    k_new = (torch.randn(T, hkv, D, generator=gen, device="cuda") * 0.5).half()
+    v_new = (torch.randn(T, hkv, D, generator=gen, device="cuda") * 0.5).half()
+    q = (torch.randn(T, hkv * g, D, generator=gen, device="cuda") * 0.5).half()
+    indptr = [0]
+    for n in new:
+        indptr.append(indptr[-1] + n)
+    k_ref, v_ref, lens_ref = oidx.append_kv_ragged(host(k_pool), host(v_pool), host(k_new), host(v_new), indptr,
+                                                   bt.numpy(), lens, P)
+    new_lens = api.append_kv_ragged(k_new, v_new, torch.tensor(indptr, dtype=torch.int32, device="cuda"),
+                                    k_pool, v_pool, bt.cuda(), torch.tensor(lens, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert new_lens.cpu().tolist() == lens_ref == [lens[b] + new[b] for b in range(B)]
+    info, ws, qi = api.prefill_plan(new, lens_ref, hkv * g, hkv, D, P, causal=True)
+    o, lse = api.batch_prefill_paged(info, q, k_pool, v_pool, bt.cuda(), torch.tensor(qi, dtype=torch.int32, device="cuda"),
+                                     new_lens, causal=True, sm_scale=1.0 / math.sqrt(D))
+    torch.cuda.synchronize()
+    O, L = oatt.batch_prefill(host(q), qi, k_ref, v_ref, bt.numpy(), lens_ref, P, 1.0 / math.sqrt(D), True)
+    check_state(o, lse, O, L, torch.float16, "prefill after ragged append")
+
+
+def test_ragged_append_rejects_aliased_lengths(api):
+    say("case: ragged append with new_seqlens aliasing cache_seqlens is rejected before any launch")
+    k_pool = torch.zeros(4, 16, 2, 64, dtype=torch.float16, device="cuda")
+    k_new = torch.zeros(3, 2, 64, dtype=torch.float16, device="cuda")
+    lens = torch.zeros(2, dtype=torch.int32, device="cuda")
+    bt = torch.zeros(2, 1, dtype=torch.int32, device="cuda")
+    with pytest.raises(api.PkcError):
+        api.append_kv_ragged(k_new, k_new, torch.tensor([0, 1, 3], dtype=torch.int32, device="cuda"), k_pool,
+                             k_pool, bt, lens, new_seqlens=lens)
