@@ -190,7 +190,7 @@ def prefill_limit(lq, lkv, i, causal):
 
 
 def batch_prefill(q, qo_indptr, k_pool, v_pool, block_table, kv_lens, page_size, sm_scale,
-                  causal, rows=None, heads=None):
+                  causal, rows=None, heads=None, tree_masks=None):
     """Ragged multi-token queries over a paged KV cache.
 
     q: [total_q, Hq, D], packed without padding: request b's queries are rows
@@ -199,6 +199,10 @@ def batch_prefill(q, qo_indptr, k_pool, v_pool, block_table, kv_lens, page_size,
     KV is its block-table row over kv_lens[b] tokens (decode-path indexing), already holding
     the new tokens.  Query i of request b attends over the first prefill_limit(...) tokens.
     ``rows`` restricts the work to some query rows (sampled parity); other rows are NaN.
+    ``tree_masks`` (tree / speculative decoding: the paper summary's logits mask, section A2
+    and the JIT variant functors of A3; reading R32): per request None or an [lq, lq] boolean
+    matrix over its new tokens.  Query i then sees the tokens before the new ones and new token
+    j only where mask[i][j] holds, inside its causal limit.
     Returns (O [total_q, Hq, D], LSE [total_q, Hq])."""
     q = np.asarray(q, dtype=np.float64)
     T, Hq, D = q.shape
@@ -216,5 +220,10 @@ def batch_prefill(q, qo_indptr, k_pool, v_pool, block_table, kv_lens, page_size,
                 continue
             n = prefill_limit(lq, lkv, i, causal)
             pages, slots = token_pages(block_table[b], 0, n, page_size)
+            tm = None if tree_masks is None else tree_masks[b]
+            if tm is not None:
+                base = lkv - lq   # position of the first new token
+                keep = np.array([t < base or bool(tm[i][t - base]) for t in range(n)], dtype=bool)
+                pages, slots = np.asarray(pages)[keep], np.asarray(slots)[keep]
             O[r], L[r] = _state_over_rows(q[r], k_pool, v_pool, pages, slots, sm_scale, hs)
     return O, L

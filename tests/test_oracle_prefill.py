@@ -130,3 +130,66 @@ def test_prefill_limit_cases():
     assert attention.prefill_limit(3, 1, 2, True) == 1
     assert attention.prefill_limit(4, 0, 3, True) == 0
     assert attention.prefill_limit(3, 10, 0, False) == 10
+
+
+def test_tree_mask_of_ones_is_the_causal_mask():
+    """A tree mask that lets every new token see every new token refines nothing: within the
+    causal limit the result is the causal prefill."""
+    lq, lkv = [4, 6], [9, 6]
+    q, qo, k, v, bt, lkv_a, P = _case(11, lq, lkv)
+    masks = [np.ones((n, n), dtype=bool) for n in lq]
+    O1, L1 = attention.batch_prefill(q, qo, k, v, bt, lkv_a, P, 0.3, True, tree_masks=masks)
+    O2, L2 = attention.batch_prefill(q, qo, k, v, bt, lkv_a, P, 0.3, True)
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+
+
+def test_tree_mask_matches_dense_masked_softmax():
+    """Independent formulation: contiguous K/V per request, a dense [lq, lkv] visibility matrix
+    built with numpy (all old tokens, then the tree mask restricted to the lower triangle over
+    the new tokens), softmax over the visible entries.  The masks are random ancestor sets of a
+    random tree (each new token sees itself and its chain of parents)."""
+    rng = np.random.default_rng(12)
+    lq, lkv = [5, 7, 1], [12, 7, 3]
+    q, qo, k, v, bt, lkv_a, P = _case(13, lq, lkv)
+    masks = []
+    for n in lq:
+        parent = [-1] + [int(rng.integers(0, i)) for i in range(1, n)]
+        m = np.zeros((n, n), dtype=bool)
+        for i in range(n):
+            j = i
+            while j >= 0:
+                m[i, j] = True
+                j = parent[j]
+        masks.append(m)
+    O, L = attention.batch_prefill(q, qo, k, v, bt, lkv_a, P, 0.5, True, tree_masks=masks)
+    Hq, D = q.shape[1], q.shape[2]
+    hkv = k.shape[2]
+    g = Hq // hkv
+    for b in range(len(lq)):
+        n = lkv[b]
+        rows_k = np.array([k[bt[b, t // P], t % P] for t in range(n)])
+        rows_v = np.array([v[bt[b, t // P], t % P] for t in range(n)])
+        vis = np.ones((lq[b], n), dtype=bool)
+        vis[:, n - lq[b]:] = np.tril(masks[b])
+        for h in range(Hq):
+            S = 0.5 * q[qo[b]:qo[b + 1], h] @ rows_k[:, h // g].T
+            for i in range(lq[b]):
+                s = S[i][vis[i]]
+                m = s.max()
+                lse = m + math.log(np.exp(s - m).sum())
+                w = np.exp(S[i] - lse) * vis[i]
+                assert abs(L[qo[b] + i, h] - lse) < 1e-12
+                assert np.allclose(O[qo[b] + i, h], w @ rows_v[:, h // g], rtol=1e-11, atol=1e-13)
+
+
+def test_tree_mask_identity_sees_prefix_and_itself():
+    """Uniform scores (q = 0) with an identity tree mask: each new token sees the old tokens and
+    itself, so LSE = ln(lkv - lq + 1) for every query."""
+    lq, lkv = [3, 2], [10, 2]
+    q, qo, k, v, bt, lkv_a, P = _case(14, lq, lkv)
+    q = np.zeros_like(q)
+    masks = [np.eye(n, dtype=bool) for n in lq]
+    O, L = attention.batch_prefill(q, qo, k, v, bt, lkv_a, P, 1.0, True, tree_masks=masks)
+    for b in range(2):
+        for i in range(lq[b]):
+            assert np.all(np.abs(L[qo[b] + i] - math.log(lkv[b] - lq[b] + 1)) < 1e-14)
