@@ -402,6 +402,28 @@ pkc_status pkc_batch_prefill_paged(const pkc_plan_info* plan, const void* q, con
                                    float* lse, void* dev_ws, size_t dev_bytes, void* stream);
 
 /*
+ * Tree (speculative) decoding over ragged queries: pkc_batch_prefill_paged with causal = 1 and
+ * a logits mask (paper summary: tree decoding in speculative decoding, section A2; the
+ * LogitsMask of the attention-variant functors, section A3).  Request b's mask is the
+ * l_q x l_q byte matrix at tree_mask + mask_indptr[b] (l_q = qo_indptr[b+1] - qo_indptr[b];
+ * row i = query i, column j = new token j, the request's last l_q KV tokens; nonzero =
+ * visible).  Query i sees every token before the new ones and new token j where the byte is
+ * set, within its causal limit (bytes above the diagonal are ignored).  tree_mask (mask_bytes
+ * bytes) and mask_indptr ([num_requests]) are device buffers; bytes past mask_bytes read as 0.
+ * The plan is a causal prefill plan; other arguments and rules are those of
+ * pkc_batch_prefill_paged.
+ */
+pkc_status pkc_batch_prefill_paged_tree(const pkc_plan_info* plan, const void* q, const void* k_pool,
+                                        const void* v_pool, int64_t num_pages,
+                                        const int32_t* block_table, int32_t max_blocks,
+                                        const int32_t* qo_indptr, const int32_t* kv_lens,
+                                        const uint8_t* tree_mask, const int32_t* mask_indptr,
+                                        int32_t mask_bytes, int32_t num_requests, int32_t total_q,
+                                        int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                                        int32_t page_size, pkc_dtype dtype, float sm_scale, void* o,
+                                        float* lse, void* dev_ws, size_t dev_bytes, void* stream);
+
+/*
  * pkc_batch_prefill_paged over FP8 K/V pools (paper summary, appendix F): OCP FP8 E4M3 codes
  * with per-pool scales k_scale and v_scale (> 0); q and o are q_dtype (PKC_F16 or PKC_BF16).
  * Arguments, plan and rules are those of pkc_batch_prefill_paged.  With one query per request

@@ -130,6 +130,9 @@ SIGNATURES = {
                                         _F, _P, _I32, _P, _P, _SZ, _P]),
     "pkc_batch_prefill_paged": (_I32, [ctypes.POINTER(PlanInfo), _P, _P, _P, _I64, _P, _I32, _P, _P, _I32,
                                        _I32, _I32, _I32, _I32, _I32, _I32, _F, _I32, _P, _P, _P, _SZ, _P]),
+    "pkc_batch_prefill_paged_tree": (_I32, [ctypes.POINTER(PlanInfo), _P, _P, _P, _I64, _P, _I32, _P, _P, _P,
+                                            _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _F, _P, _P,
+                                            _P, _SZ, _P]),
     "pkc_batch_prefill_paged_fp8": (_I32, [ctypes.POINTER(PlanInfo), _P, _P, _P, _F, _F, _I64, _P, _I32, _P,
                                            _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _F, _I32, _P, _P,
                                            _P, _SZ, _P]),
@@ -571,6 +574,33 @@ def batch_prefill_paged(plan_info: PlanInfo, q, k_pool, v_pool, block_table, qo_
                                        _ptr(block_table), block_table.shape[1], _ptr(qo_indptr), _ptr(kv_lens),
                                        B, T, Hq, Hkv, D, P, dtype_code(q.dtype), scale, 1 if causal else 0,
                                        _ptr(out), _ptr(lse), ws, wsn, _stream(dev)))
+    return out, lse
+
+
+def batch_prefill_paged_tree(plan_info: PlanInfo, q, k_pool, v_pool, block_table, qo_indptr, kv_lens,
+                             tree_mask, mask_indptr, sm_scale=None, out=None, lse=None):
+    """pkc_batch_prefill_paged_tree: causal ragged queries with per-request tree masks
+    (tree_mask: uint8 device tensor holding every request's l_q x l_q byte matrix, request b's
+    at byte mask_indptr[b]; mask_indptr: int32 device tensor [num_requests])."""
+    T, Hq, D = q.shape
+    N, P, Hkv, _ = k_pool.shape
+    dev = q.device
+    B = block_table.shape[0]
+    for t, n in ((block_table, "block_table"), (qo_indptr, "qo_indptr"), (kv_lens, "kv_lens"),
+                 (mask_indptr, "mask_indptr")):
+        _need(t, n, torch.int32, dev)
+    _need(tree_mask, "tree_mask", torch.uint8, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(T, Hq, dtype=torch.float32, device=dev)
+    scale = 1.0 / math.sqrt(D) if sm_scale is None else float(sm_scale)
+    ws, wsn = _ws_of(plan_info)
+    _check(lib.pkc_batch_prefill_paged_tree(ctypes.byref(plan_info), _ptr(q), _ptr(k_pool), _ptr(v_pool), N,
+                                            _ptr(block_table), block_table.shape[1], _ptr(qo_indptr),
+                                            _ptr(kv_lens), _ptr(tree_mask), _ptr(mask_indptr), tree_mask.numel(),
+                                            B, T, Hq, Hkv, D, P, dtype_code(q.dtype), scale, _ptr(out), _ptr(lse),
+                                            ws, wsn, _stream(dev)))
     return out, lse
 
 

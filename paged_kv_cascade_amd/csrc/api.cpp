@@ -180,6 +180,9 @@ struct PrefillLevel {
   int32_t causal;
   void* o;      // final output of write-through items
   float* lse;
+  const uint8_t* tree_mask = nullptr;   // optional tree masks (causal only)
+  const int32_t* mask_indptr = nullptr;
+  int32_t mask_bytes = 0;
 };
 
 // FP8 pools (fp8 = true): k_scale folds into the softmax scale, v_scale into the state.
@@ -203,6 +206,9 @@ pkc_status run_level(const pkc_plan_info* plan, int level, const void* q, const 
     p.grp_kv_lens = pf->kv_lens;
     p.o = pf->o;
     p.lse = pf->lse;
+    p.tree_mask = pf->tree_mask;
+    p.mask_indptr = pf->mask_indptr;
+    p.mask_bytes = pf->mask_bytes;
   } else {
     // Only batch prefill passes an output for write-through level items.
     if (plan->lvl_write_through != 0)
@@ -551,7 +557,9 @@ static pkc_status prefill_impl(bool fp8, float k_scale, float v_scale, const pkc
                                int32_t num_requests, int32_t total_q, int32_t num_qo_heads,
                                int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
                                pkc_dtype dtype, float sm_scale, int32_t causal, void* o,
-                               float* lse, void* dev_ws, size_t dev_bytes, void* stream) {
+                               float* lse, void* dev_ws, size_t dev_bytes, void* stream,
+                               const uint8_t* tree_mask = nullptr, const int32_t* mask_indptr = nullptr,
+                               int32_t mask_bytes = 0) {
   pkc_status st = check_shapes(total_q, num_qo_heads, num_kv_heads, head_dim, page_size, dtype, sm_scale);
   if (st != PKC_OK) return st;
   if ((st = check_prefix_supported(dtype, page_size)) != PKC_OK) return st;
@@ -576,7 +584,11 @@ static pkc_status prefill_impl(bool fp8, float k_scale, float v_scale, const pkc
   if ((int64_t)max_blocks * page_size > INT32_MAX || (int64_t)max_blocks * num_requests > INT32_MAX)
     return fail(PKC_ERR_INVALID_ARG, "block table too large for int32 offsets");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const PrefillLevel pf{block_table, max_blocks, qo_indptr, kv_lens, causal ? 1 : 0, o, lse};
+  if (tree_mask && (!causal || !mask_indptr || mask_bytes < 0))
+    return fail(PKC_ERR_INVALID_ARG, "tree masks refine the causal mask: they need causal = 1, "
+                                     "mask_indptr and mask_bytes >= 0");
+  const PrefillLevel pf{block_table, max_blocks, qo_indptr, kv_lens, causal ? 1 : 0, o, lse,
+                        tree_mask, mask_indptr, mask_bytes};
   if ((st = run_level(plan, 0, q, k_pool, v_pool, num_pages, nullptr, dtype, sm_scale, dev_ws, s, fp8,
                       k_scale, v_scale, &pf)) != PKC_OK)
     return st;
@@ -599,6 +611,24 @@ pkc_status pkc_batch_prefill_paged(const pkc_plan_info* plan, const void* q, con
                       qo_indptr, kv_lens, num_requests, total_q, num_qo_heads, num_kv_heads, head_dim,
                       page_size, dtype, sm_scale, causal, o, lse, dev_ws, dev_bytes, stream);
   PKC_TRY_END("pkc_batch_prefill_paged")
+}
+
+pkc_status pkc_batch_prefill_paged_tree(const pkc_plan_info* plan, const void* q, const void* k_pool,
+                                        const void* v_pool, int64_t num_pages,
+                                        const int32_t* block_table, int32_t max_blocks,
+                                        const int32_t* qo_indptr, const int32_t* kv_lens,
+                                        const uint8_t* tree_mask, const int32_t* mask_indptr,
+                                        int32_t mask_bytes, int32_t num_requests, int32_t total_q,
+                                        int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                                        int32_t page_size, pkc_dtype dtype, float sm_scale, void* o,
+                                        float* lse, void* dev_ws, size_t dev_bytes, void* stream) {
+  PKC_TRY_BEGIN
+  if (!tree_mask) return fail(PKC_ERR_INVALID_ARG, "tree_mask is NULL");
+  return prefill_impl(false, 1.f, 1.f, plan, q, k_pool, v_pool, num_pages, block_table, max_blocks,
+                      qo_indptr, kv_lens, num_requests, total_q, num_qo_heads, num_kv_heads, head_dim,
+                      page_size, dtype, sm_scale, 1, o, lse, dev_ws, dev_bytes, stream, tree_mask,
+                      mask_indptr, mask_bytes);
+  PKC_TRY_END("pkc_batch_prefill_paged_tree")
 }
 
 pkc_status pkc_batch_prefill_paged_fp8(const pkc_plan_info* plan, const void* q, const void* k_pool,

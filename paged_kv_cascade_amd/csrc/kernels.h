@@ -66,6 +66,12 @@ struct PrefixParams {
   // output here instead: O [rows, hq, D] in the operand type, LSE [rows, hq] fp32.
   void* o;
   float* lse;
+  // Tree masks (causal variant only; nullptr: none): group g's mask is the l_q x l_q byte
+  // matrix at tree_mask + mask_indptr[g] (row = query, column = new token, nonzero = visible),
+  // inside a buffer of mask_bytes bytes.
+  const uint8_t* tree_mask;
+  const int32_t* mask_indptr;
+  int32_t mask_bytes;
 };
 
 // Plan-driven merge: request b merges merge_rows[merge_ptr[b*NL2 + l0] .. merge_ptr[b*NL2 + l1]).

@@ -305,10 +305,21 @@ __global__ __launch_bounds__(64 * prefix_detail::kWavesPerStream * NS, NS == 1 ?
     // is the limit of the item's first query (its queries are the group's last l_q tokens).
     // Tokens past the last query's limit are not visited at all.
     int lim0 = 0;
+    // Tree mask of the group (causal variant): its new tokens start at tbase, the item's first
+    // query is the group's query tq0, and (query qi, token t >= tbase) is byte
+    // tmoff + qi * tlq + (t - tbase) of the mask.
+    int tbase = 0, tq0 = 0, tlq = 0, tmoff = 0;
     if constexpr (CAUSAL) {
       const int gq0 = scalar_load(p.grp_qo_indptr + grp), gq1 = scalar_load(p.grp_qo_indptr + grp + 1);
-      lim0 = scalar_load(p.grp_kv_lens + grp) - (gq1 - gq0) + (q0 - gq0);
+      const int kvl = scalar_load(p.grp_kv_lens + grp);
+      lim0 = kvl - (gq1 - gq0) + (q0 - gq0);
       ke = min(ke, lim0 + nq);
+      if (p.tree_mask) {
+        tlq = gq1 - gq0;
+        tbase = kvl - tlq;
+        tq0 = q0 - gq0;
+        tmoff = scalar_load(p.mask_indptr + grp);
+      }
     }
     const int t0 = (kb / kTK) * kTK;
     // A group without pages holds no tokens (its kv_len is then a caller error).
@@ -439,6 +450,26 @@ __global__ __launch_bounds__(64 * prefix_detail::kWavesPerStream * NS, NS == 1 ?
 #pragma unroll
             for (int i = 0; i < 4; ++i)
               s[mt][nt][i] = tok0 + mt * 16 + i > cbase[nt] ? kNegInf : s[mt][nt][i];
+        // Tree mask on the tiles that reach the new tokens: a new token is visible to a query
+        // where its mask byte is set (the causal limit above still applies).  Bytes of tokens
+        // before the new ones are not read (an out-of-range offset reads zero).
+        if (p.tree_mask != nullptr && tok0 + kTK > tbase) {
+          const rsrc_t mr = make_rsrc(p.tree_mask, p.mask_bytes);
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) {
+            const int qi = tq0 + (wq * kRowsPerWave + nt * 16 + l16) / G;
+            const int rowoff = tmoff + qi * tlq - tbase;
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int t = tok0 + mt * 16 + 4 * lg + i;
+                const int32_t off = t >= tbase ? rowoff + t : kOffsetNone;
+                const uint32_t vis = __builtin_amdgcn_raw_buffer_load_b8(mr, off, 0, 0);
+                s[mt][nt][i] = (t < tbase || vis != 0) ? s[mt][nt][i] : kNegInf;
+              }
+          }
+        }
       }
       V16 pb[2];   // P^T operands per query tile nt (the tile's 32 tokens are one step)
       // bf16 weights go to the matrix cores as two bf16 terms (rounded weight and residual):

@@ -173,3 +173,76 @@ def test_write_through_plan_runs_only_as_prefill(api):
     d, keep = api.level_dev({"kv_page_indptr": [0, 1, 2], "kv_page_indices": [0, 1]})
     with pytest.raises(api.PkcError):
         api.prefix_attention(info, 0, q, k, v, d)
+
+
+# --- tree (speculative) decoding masks ------------------------------------------------------------
+
+def _tree_masks(rng, lq):
+    """Per request: each new token sees itself and its chain of parents in a random tree, plus
+    random bytes above the diagonal (which the causal limit must ignore)."""
+    masks = []
+    for n in lq:
+        parent = [-1] + [int(rng.integers(0, i)) for i in range(1, n)]
+        m = np.zeros((n, n), dtype=bool)
+        for i in range(n):
+            j = i
+            while j >= 0:
+                m[i, j] = True
+                j = parent[j]
+        m |= np.triu(rng.random((n, n)) < 0.5, k=1)
+        masks.append(m)
+    return masks
+
+
+def _run_tree(api, q, k, v, bt, lq, lkv, masks, level_ctas=0):
+    T, Hq, D = q.shape
+    P, Hkv = k.shape[1], k.shape[2]
+    info, ws, qi = api.prefill_plan(lq, lkv, Hq, Hkv, D, P, level_ctas=level_ctas, causal=True)
+    flat = np.concatenate([m.astype(np.uint8).ravel() for m in masks] + [np.zeros(1, np.uint8)])
+    offs = np.concatenate([[0], np.cumsum([m.size for m in masks])[:-1]]).astype(np.int32)
+    o, lse = api.batch_prefill_paged_tree(info, q, k, v, bt.cuda(), torch.tensor(qi, dtype=torch.int32, device="cuda"),
+                                          torch.tensor(lkv, dtype=torch.int32, device="cuda"),
+                                          torch.from_numpy(flat).cuda(), torch.from_numpy(offs).cuda(),
+                                          sm_scale=1.0 / math.sqrt(D))
+    torch.cuda.synchronize()
+    return o, lse, qi
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_tree_masked_prefill(api, seed):
+    rng = np.random.default_rng(2200 + seed)
+    dtype = [torch.float16, torch.bfloat16][seed % 2]
+    D = [128, 64][(seed // 2) % 2]
+    g = [1, 2, 4][seed % 3]
+    P = [16, 4][seed % 2]
+    lq = [int(x) for x in rng.choice([1, 4, 7, 33, 64], size=4)]
+    lkv = [n + int(x) for n, x in zip(lq, rng.choice([0, 5, 100, 700], size=4))]
+    lctas = int(rng.choice([0, 3, 8]))
+    say(f"case: tree-masked prefill seed={seed} {dtype} D={D} g={g} P={P} lq={lq} lkv={lkv} level_ctas={lctas}")
+    masks = _tree_masks(rng, lq)
+    q, k, v, bt = _case(2300 + seed, lq, lkv, dtype, D, g, P)
+    o, lse, qi = _run_tree(api, q, k, v, bt, lq, lkv, masks, level_ctas=lctas)
+    O, L = oatt.batch_prefill(host(q), qi, PoolView(k), PoolView(v), bt.numpy(), lkv, P, 1.0 / math.sqrt(D), True,
+                              tree_masks=masks)
+    check_state(o, lse, O, L, dtype, f"tree prefill seed {seed}")
+
+
+def test_tree_mask_of_ones_is_the_causal_prefill(api):
+    lq, lkv = [5, 40], [30, 40]
+    say("case: all-ones tree masks vs the causal prefill, fp16 D128 g2 P16")
+    q, k, v, bt = _case(2400, lq, lkv, torch.float16, 128, 2, 16)
+    o, lse, qi = _run_tree(api, q, k, v, bt, lq, lkv, [np.ones((n, n), dtype=bool) for n in lq])
+    o2, lse2, _, _ = _run(api, q, k, v, bt, lq, lkv, True)
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+
+
+def test_tree_mask_needs_a_causal_plan(api):
+    say("case: tree-masked prefill with a non-causal plan is rejected before any launch")
+    lq, lkv = [3, 2], [4, 9]
+    q, k, v, bt = _case(5, lq, lkv, torch.float16, 64, 1, 4)
+    info, ws, qi = api.prefill_plan(lq, lkv, 2, 2, 64, 4, causal=False)
+    with pytest.raises(api.PkcError):
+        api.batch_prefill_paged_tree(info, q, k, v, bt.cuda(), torch.tensor(qi, dtype=torch.int32, device="cuda"),
+                                     torch.tensor(lkv, dtype=torch.int32, device="cuda"),
+                                     torch.ones(13, dtype=torch.uint8, device="cuda"),
+                                     torch.tensor([0, 9], dtype=torch.int32, device="cuda"))
