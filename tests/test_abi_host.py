@@ -281,3 +281,28 @@ def test_validate_block_table_worked_example(api):
     # starting past the unallocated block makes it legal again
     api.validate_block_table(bt, torch.tensor([30, 32, 70], dtype=torch.int32), g["page_size"], 8,
                              kv_start=torch.tensor([0, 0, 0], dtype=torch.int32))
+
+
+def test_append_and_tree_validation_before_any_launch(api):
+    """Argument errors of the multi-token append and of the tree-masked prefill are reported
+    before any HIP call (dummy non-NULL pointers are never dereferenced)."""
+    lib = api.lib
+    d = ctypes.c_void_p(0x1000)
+    e = ctypes.c_void_p(0x2000)
+    # ragged append: too many requests for the grid, unsupported head_dim, aliased lengths
+    assert lib.pkc_append_kv_ragged(d, d, 4, d, d, d, 8, d, 2, d, e, 70000, 2, 128, 16, 1, None) == 1
+    assert lib.pkc_append_kv_ragged(d, d, 4, d, d, d, 8, d, 2, d, e, 2, 2, 96, 16, 1, None) == 2
+    assert lib.pkc_append_kv_ragged(d, d, 4, d, d, d, 8, d, 2, d, d, 2, 2, 128, 16, 1, None) == 1
+    assert "alias" in lib.pkc_last_error().decode()
+    assert lib.pkc_append_kv_ragged(d, d, 4, None, d, d, 8, d, 2, d, e, 2, 2, 128, 16, 1, None) == 1
+    # tree-masked prefill without a mask
+    assert lib.pkc_batch_prefill_paged_tree(None, d, d, d, 8, d, 2, d, d, None, d, 4, 2, 4, 2, 2, 128, 16,
+                                            1, 1.0, d, d, None, 0, None) == 1
+    # a plan with level write-through is refused by the level-only call before any launch
+    p = api.make_params(3, 2, 2, 64, 4, num_ctas=1, level_ctas=2, level_write_through=True)
+    info, _ = api.plan_host(p, [0, 0, 0], [{"qo_indptr": [0, 2, 3], "kv_lens": [4, 9], "causal": True}])
+    assert info.lvl_write_through > 0
+    p2 = api.make_params(2, 4, 4, 128, 16, num_ctas=1, level_ctas=1, level_write_through=True)
+    p2.level_write_through = 3
+    with pytest.raises(api.PkcError):
+        api.plan_host(p2, [1, 2])
