@@ -591,6 +591,9 @@ def main():
         "ms_per_step_device_only": round(ms_dev, 4),
         "ms_plan_cpu": round(ms_plan, 4),
         "device_us_per_run": {"back_to_back": dist_warm, "llc_evicted": dist_cold},
+        # The same algorithmic bytes over the median run with the last-level cache evicted first
+        # (no reuse of the previous step's reads): the cold-cache rate of the cascade run.
+        "llc_evicted_alg_GBps": round(alg_bytes / (dist_cold["p50"] * 1e-6) / 1e9, 1),
         "kernels": kern,
         "roofline": roof,
         "noncascade_same_step": nonc,
