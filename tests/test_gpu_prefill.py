@@ -208,12 +208,12 @@ def _run_tree(api, q, k, v, bt, lq, lkv, masks, level_ctas=0):
     return o, lse, qi
 
 
-@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("seed", range(8))
 def test_tree_masked_prefill(api, seed):
     rng = np.random.default_rng(2200 + seed)
     dtype = [torch.float16, torch.bfloat16][seed % 2]
     D = [128, 64][(seed // 2) % 2]
-    g = [1, 2, 4][seed % 3]
+    g = [1, 2, 4, 8][seed % 4]
     P = [16, 4][seed % 2]
     lq = [int(x) for x in rng.choice([1, 4, 7, 33, 64], size=4)]
     lkv = [n + int(x) for n, x in zip(lq, rng.choice([0, 5, 100, 700], size=4))]
