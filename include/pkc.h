@@ -51,7 +51,8 @@
  * hipStream_t; NULL = the null stream) and calls return without synchronising.  The library
  * never allocates or frees device or pinned memory; the plan and the partial states live in a
  * caller-provided device workspace whose size pkc_plan_buffer_sizes returns.  The only global
- * state is cached device properties and the optional timing ring.
+ * state is cached device properties and the optional timing ring (pkc_timing_*); no
+ * environment variable is read.
  */
 #ifndef PKC_H
 #define PKC_H
@@ -115,16 +116,20 @@ typedef struct pkc_plan_params {
   int32_t enable_split; /* 0 -> L_kv = longest KV length (one chunk per tile, no split-KV) */
   int64_t alpha;        /* cost per query row (>= 0) */
   int64_t beta;         /* cost per KV token (>= 0) */
-  int32_t decode_waves; /* waves per decode workgroup: 0 -> chosen from the plan's average item
-                           length (4 from 256 tokens, 2 from 64, else 1); 1, 2 or 4 fix it.  A
-                           run captured in a HIP graph replays the launches it was captured
-                           with, so plans replayed under one graph need a fixed value (and no
-                           merge launch: enable_split = 0 in a cascade) */
+  int32_t decode_waves; /* waves per decode workgroup: 0 -> 4; 1, 2 or 4.  Short items (a few
+                           dozen tokens) run faster on 1 or 2 waves.  Like every launch shape of a
+                           run, it depends on the parameters only, never on the lengths of a step,
+                           so one run captured in a HIP graph stays valid for every plan built
+                           from the same parameters into the same workspace */
   int32_t level_write_through; /* 1 (batch prefill): in a plan with a single level, a tile of a
                            group whose requests have no own KV and whose KV is one chunk writes its
                            rows' final output (O in the query type, LSE) instead of a state, and
                            the merge pass skips those rows; only pkc_batch_prefill_paged(_fp8)
                            runs such plans.  0: every level item writes a state (cascades) */
+  int32_t level_streams; /* tile streams per level workgroup: 0 -> 2 when level_ctas x Hkv is at
+                           most the compute-unit count (one 8-wave workgroup per compute unit,
+                           two 4-wave streams over alternate KV tiles, merged at the end), else
+                           1 (4-wave workgroups); 1 or 2 fix it */
 } pkc_plan_params;
 
 /* Host description of one cascade level: groups of consecutive requests sharing a KV run.
@@ -147,7 +152,7 @@ typedef struct pkc_level_host {
 typedef struct pkc_level_dev {
   const int32_t* kv_page_indptr;  /* [G+1] device */
   const int32_t* kv_page_indices; /* [nnz] device */
-  int32_t num_page_indices;       /* nnz (host value, for validation) */
+  int32_t num_page_indices;       /* nnz: the kernel clamps every group's run into the list */
 } pkc_level_dev;
 
 /*
@@ -166,7 +171,7 @@ typedef struct pkc_plan_info {
   int32_t dec_items;       /* work items of the decode stage */
   int32_t dec_slots;       /* partial slots of the decode stage */
   int32_t dec_kv_chunk;    /* L_kv of the decode stage */
-  int32_t dec_waves;       /* waves per decode workgroup (1, 2 or 4) chosen from the item sizes */
+  int32_t dec_waves;       /* waves per decode workgroup (1, 2 or 4), from the parameters */
   int32_t lvl_groups[PKC_MAX_LEVELS];
   int32_t lvl_tile_q[PKC_MAX_LEVELS];
   int32_t lvl_items[PKC_MAX_LEVELS];
@@ -191,6 +196,7 @@ typedef struct pkc_plan_info {
   uint64_t dev_ws;         /* address of the workspace the plan was copied to (0: host-only) */
   int32_t lvl_causal[PKC_MAX_LEVELS]; /* 1: the level was planned with causal tile extents */
   int32_t lvl_write_through;  /* level items that write the final output (level_write_through) */
+  int32_t lvl_streams;     /* tile streams per level workgroup (1 or 2), from the parameters */
 } pkc_plan_info;
 
 /*
@@ -309,6 +315,11 @@ pkc_status pkc_merge_state_inplace(void* o_a, float* lse_a, const void* o_b, con
  * ascending, own KV last.  The plan must have been built with the same levels and with
  * kv_lens_h == suffix_seqlens.  A request whose own KV is a single chunk is finished by the
  * decode kernel (which folds in its level states); the merge kernel finishes the others.
+ * With a plan, every run call enqueues the same kernels with the same arguments for every plan
+ * built from the same parameters and level shapes into the same workspace (the merge kernel is
+ * always enqueued and skips the requests flagged as finished), so a run captured in a HIP graph
+ * can be replayed after any later pkc_plan into that workspace (paper summary, section A3:
+ * plan outside the graph, run inside it).
  */
 pkc_status pkc_cascade_decode(const pkc_plan_info* plan, const void* q, const void* k_pool,
                               const void* v_pool, int64_t num_pages,

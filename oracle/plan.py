@@ -166,10 +166,10 @@ def cascade_plan(batch, levels, suffix_kv_lens, num_ctas, level_ctas,
     Each level is one stage: the query tile of a group is T_q consecutive
     requests of the group, its KV is the group's shared run.  Level items
     always write partial states.  The decode stage has one query per request
-    (T_q = 1); an item that is its request's only chunk writes the final
-    output (write-through), after folding in the request's level states
-    listed in its merge list (reading R24); every other request is finished
-    by the merge pass.
+    (T_q = 1).  Appendix D's write-through rule: an item writes the final
+    output only when it is its request's only state, i.e. the request's own
+    KV is one chunk and no level covers the request; every other request is
+    finished by the merge pass over its merge list.
 
     Merge order (reading R9): levels in order, chunks ascending, then the
     request's own chunks ascending.  A merge entry is (stage, slot, row):
@@ -182,6 +182,7 @@ def cascade_plan(batch, levels, suffix_kv_lens, num_ctas, level_ctas,
     writes its rows' final output, and those requests are not merged.
     """
     lvl_plans = []
+    covered = [False] * batch   # some level holds a state of the request
     for li, lv in enumerate(levels):
         qi = [int(x) for x in lv["qo_indptr"]]
         qo_lens = [qi[g + 1] - qi[g] for g in range(len(qi) - 1)]
@@ -193,11 +194,15 @@ def cascade_plan(batch, levels, suffix_kv_lens, num_ctas, level_ctas,
             assign_slots(st, lambda g: no_own_kv[g])
         else:
             assign_slots(st, lambda g: False)
+        for it in st.items:
+            b0 = qi[it.req] + it.tile * level_tile_q[li]
+            for b in range(b0, b0 + it.lq):
+                covered[b] = True
         lvl_plans.append(st)
 
     suf = lpt_plan([1] * batch, suffix_kv_lens, 1, num_ctas, alpha, beta,
                    chunk_align, enable_split)
-    assign_slots(suf, lambda r: True)
+    assign_slots(suf, lambda r: not covered[r])
 
     merge = [[] for _ in range(batch)]
     wt = [False] * batch

@@ -229,17 +229,8 @@ pkc_status run_level(const pkc_plan_info* plan, int level, const void* q, const 
   p.indptr = at<int32_t>(ws, plan->off_lvl_indptr[level]);
   p.items = at<int32_t>(ws, plan->off_lvl_items[level]);
   const int g = plan->num_qo_heads / plan->num_kv_heads;
-  // A level whose workgroups fit one per compute unit runs them with 8 waves (two tile streams
-  // merged at the end of each item), so every SIMD still holds two waves; otherwise 4-wave
-  // workgroups, two per compute unit.  PKC_PREFIX_STREAMS (1 or 2) overrides, for measurements.
-  int32_t cus = 0;
-  pkc_status st = device_cus(&cus);
-  if (st != PKC_OK) return st;
-  int streams = (int64_t)plan->level_ctas * plan->num_kv_heads <= cus ? 2 : 1;
-  if (const char* e = std::getenv("PKC_PREFIX_STREAMS")) {
-    const int v = std::atoi(e);
-    if (v == 1 || v == 2) streams = v;
-  }
+  const int streams = plan->lvl_streams;
+  if (streams != 1 && streams != 2) return fail(PKC_ERR_PLAN_MISMATCH, "plan has no level stream count");
   if (pf && pf->causal)
     return timed(1, s, "prefix kernel launch", [&] {
       return fp8 ? pkc::launch_prefill_causal_fp8(dtype, plan->head_dim, g, plan->lvl_tile_q[level], streams,
@@ -281,18 +272,25 @@ bool host_buf_is_pinned(const void* host_buf) {
 // workgroups per compute unit (the 32K-prefix, batch-128 cascade step: 190 against 201 us;
 // with three levels 315 against 345 us).  Long multi-token levels (prefill) run faster with
 // more, smaller workgroups and should pass their own #CTA.
-pkc_status resolve_params(const pkc_plan_params* params, pkc::Resolved* r) {
+// with_streams: also resolve the level stream count (pkc_plan; buffer sizes do not depend on it,
+// and host-side sizing of explicit-#CTA parameters then needs no device).
+pkc_status resolve_params(const pkc_plan_params* params, pkc::Resolved* r, bool with_streams) {
   pkc_status st = pkc::check_params(params, false, r);
   if (st != PKC_OK) return st;
-  if (r->p.num_ctas == 0 || r->p.level_ctas == 0) {
-    int32_t cus = 0;
-    if ((st = device_cus(&cus)) != PKC_OK) return st;
-    if (r->p.num_ctas == 0)
-      r->p.num_ctas = (int32_t)std::max<int64_t>(
-          std::max<int64_t>(1, r->p.batch), pkc::ceil_div(8 * (int64_t)cus, r->p.num_kv_heads));
-    if (r->p.level_ctas == 0)
-      r->p.level_ctas = (int32_t)std::max<int64_t>(1, (int64_t)cus / r->p.num_kv_heads);
-  }
+  if (r->p.num_ctas != 0 && r->p.level_ctas != 0 && (!with_streams || r->p.level_streams != 0))
+    return PKC_OK;
+  int32_t cus = 0;
+  if ((st = device_cus(&cus)) != PKC_OK) return st;
+  if (r->p.num_ctas == 0)
+    r->p.num_ctas = (int32_t)std::max<int64_t>(
+        std::max<int64_t>(1, r->p.batch), pkc::ceil_div(8 * (int64_t)cus, r->p.num_kv_heads));
+  if (r->p.level_ctas == 0)
+    r->p.level_ctas = (int32_t)std::max<int64_t>(1, (int64_t)cus / r->p.num_kv_heads);
+  // A level whose workgroups fit one per compute unit runs them with 8 waves (two tile streams
+  // merged at the end of each item), so every SIMD still holds two waves; otherwise 4-wave
+  // workgroups, two per compute unit.
+  if (with_streams && r->p.level_streams == 0)
+    r->p.level_streams = (int64_t)r->p.level_ctas * r->p.num_kv_heads <= cus ? 2 : 1;
   return PKC_OK;
 }
 
@@ -368,7 +366,7 @@ pkc_status pkc_plan_buffer_sizes(const pkc_plan_params* params, const pkc_level_
                                  int32_t num_levels, size_t* host_bytes, size_t* device_bytes) {
   PKC_TRY_BEGIN
   pkc::Resolved r;
-  pkc_status st = resolve_params(params, &r);
+  pkc_status st = resolve_params(params, &r, false);
   if (st != PKC_OK) return st;
   if ((st = pkc::check_levels(levels, num_levels, r.p.batch, false)) != PKC_OK) return st;
   pkc::Layout L;
@@ -385,7 +383,7 @@ pkc_status pkc_plan(const pkc_plan_params* params, const int32_t* kv_lens_h,
                     pkc_plan_info* out) {
   PKC_TRY_BEGIN
   pkc::Resolved r;
-  pkc_status st = resolve_params(params, &r);
+  pkc_status st = resolve_params(params, &r, true);
   if (st != PKC_OK) return st;
   if (!dev_ws || ((uintptr_t)dev_ws & 255)) return fail(PKC_ERR_INVALID_ARG, "dev_ws must be 256-byte aligned");
   if ((st = pkc::build_plan_host(r, kv_lens_h, levels_h, num_levels, host_buf, host_bytes, out)) != PKC_OK)
@@ -453,7 +451,9 @@ static pkc_status decode_impl(bool fp8, float k_scale, float v_scale,
                     : pkc::launch_decode(dtype, head_dim, g, waves, p, grid_x, s);
        })) != PKC_OK)
     return st;
-  if (plan && plan->num_merge > 0) {
+  if (plan) {
+    // Always enqueued (it skips the requests flagged as written through), so the launches of a
+    // run do not depend on the plan's lengths.
     pkc::MergePlanParams m = merge_params(plan, dev_ws, 0, 1, true, o, lse);
     if ((st = timed(2, s, "merge kernel launch", [&] { return pkc::launch_merge_plan(dtype, head_dim, m, s); })) != PKC_OK)
       return st;
@@ -592,8 +592,8 @@ static pkc_status prefill_impl(bool fp8, float k_scale, float v_scale, const pkc
   if ((st = run_level(plan, 0, q, k_pool, v_pool, num_pages, nullptr, dtype, sm_scale, dev_ws, s, fp8,
                       k_scale, v_scale, &pf)) != PKC_OK)
     return st;
-  // Query rows written through by their tile's only item are flagged and skipped.
-  if (plan->num_merge == 0) return PKC_OK;
+  // Query rows written through by their tile's only item are flagged and skipped; the merge is
+  // enqueued even when every row is (launches independent of the plan's lengths).
   pkc::MergePlanParams m = merge_params(plan, dev_ws, 0, 1, true, o, lse);
   return timed(2, s, "merge kernel launch", [&] { return pkc::launch_merge_plan(dtype, head_dim, m, s); });
 }
@@ -747,10 +747,13 @@ static pkc_status cascade_impl(bool fp8, float k_scale, float v_scale, const pkc
     p.num_levels = num_levels;
     for (int32_t l = 0; l < num_levels; ++l) p.lvl_tile_q[l] = plan->lvl_tile_q[l];
     p.req_levels = at<int32_t>(dev_ws, plan->off_req_levels);
-    const int64_t o_bytes = (int64_t)plan->state_rows * num_qo_heads * head_dim * 4;
-    if (o_bytes <= INT32_MAX) {
+    // Bounds of the state buffers for the fold's buffer loads: the workspace's capacity (fixed
+    // by the parameters and level shapes, like every other launch argument).
+    const int64_t o_bytes = plan->off_state_lse - plan->off_state_o;
+    const int64_t lse_bytes = plan->dev_bytes - plan->off_state_lse;
+    if (o_bytes <= INT32_MAX && lse_bytes <= INT32_MAX) {
       p.fold_o_bytes = (int32_t)o_bytes;
-      p.fold_lse_bytes = plan->state_rows * num_qo_heads * 4;
+      p.fold_lse_bytes = (int32_t)lse_bytes;
     }
   }
   const int g = num_qo_heads / num_kv_heads;
@@ -759,12 +762,10 @@ static pkc_status cascade_impl(bool fp8, float k_scale, float v_scale, const pkc
                     : pkc::launch_decode(dtype, head_dim, g, plan->dec_waves, p, plan->num_ctas, s);
        })) != PKC_OK)
     return st;
-  if (plan->num_merge > 0) {
-    pkc::MergePlanParams m = merge_params(plan, dev_ws, 0, num_levels + 1, true, o, lse);
-    if ((st = timed(2, s, "merge kernel launch", [&] { return pkc::launch_merge_plan(dtype, head_dim, m, s); })) != PKC_OK)
-      return st;
-  }
-  return PKC_OK;
+  // Always enqueued (it skips the requests finished by the decode kernel): the launches of a run
+  // do not depend on the plan's lengths, so a captured run stays valid across re-plans.
+  pkc::MergePlanParams m = merge_params(plan, dev_ws, 0, num_levels + 1, true, o, lse);
+  return timed(2, s, "merge kernel launch", [&] { return pkc::launch_merge_plan(dtype, head_dim, m, s); });
 }
 
 pkc_status pkc_cascade_decode(const pkc_plan_info* plan, const void* q, const void* k_pool,

@@ -7,7 +7,6 @@ namespace pkc {
 hipError_t launch_decode(pkc_dtype dt, int head_dim, int group, int waves, const DecodeParams& p,
                          int grid_x, hipStream_t s) {
   if (grid_x <= 0) return hipSuccess;
-  if (env_waves()) waves = env_waves();
   switch (dt) {
     case PKC_F32: return launch_decode_d<F32>(head_dim, group, waves, p, grid_x, s);
     case PKC_F16: return launch_decode_d<F16>(head_dim, group, waves, p, grid_x, s);

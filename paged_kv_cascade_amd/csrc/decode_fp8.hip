@@ -7,7 +7,6 @@ namespace pkc {
 hipError_t launch_decode_fp8(pkc_dtype q_dt, int head_dim, int group, int waves,
                              const DecodeParams& p, int grid_x, hipStream_t s) {
   if (grid_x <= 0) return hipSuccess;
-  if (env_waves()) waves = env_waves();
   switch (q_dt) {
     case PKC_F16: return launch_decode_d<KV8<F16>>(head_dim, group, waves, p, grid_x, s);
     case PKC_BF16: return launch_decode_d<KV8<BF16>>(head_dim, group, waves, p, grid_x, s);

@@ -417,17 +417,6 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(const DecodeParams p) {
   }
 }
 
-// Waves per workgroup: the environment variable PKC_DECODE_WAVES (1, 2 or 4) overrides the
-// choice made by the caller (used for tuning measurements).
-inline int env_waves() {
-  static int w = [] {
-    const char* s = std::getenv("PKC_DECODE_WAVES");
-    const int v = s ? std::atoi(s) : 0;
-    return (v == 1 || v == 2 || v == 4) ? v : 0;
-  }();
-  return w;
-}
-
 template <typename T, int D, int G, int NW, int PM>
 inline hipError_t launch_decode_t(const DecodeParams& p, int grid_x, hipStream_t s) {
   dim3 grid(grid_x, p.hkv), block(64 * NW);

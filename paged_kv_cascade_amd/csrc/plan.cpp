@@ -136,6 +136,8 @@ pkc_status check_params(const pkc_plan_params* params, bool need_ctas, Resolved*
     return fail(PKC_ERR_INVALID_ARG, "decode_waves must be 0, 1, 2 or 4");
   if (!(p.level_write_through == 0 || p.level_write_through == 1))
     return fail(PKC_ERR_INVALID_ARG, "level_write_through must be 0 or 1");
+  if (!(p.level_streams == 0 || p.level_streams == 1 || p.level_streams == 2))
+    return fail(PKC_ERR_INVALID_ARG, "level_streams must be 0, 1 or 2");
   if (p.num_ctas < 0 || p.level_ctas < 0 || p.level_tile_q < 0)
     return fail(PKC_ERR_INVALID_ARG, "num_ctas, level_ctas, level_tile_q must be >= 0");
   if (need_ctas && (p.num_ctas == 0 || p.level_ctas == 0))
@@ -249,6 +251,7 @@ pkc_status build_plan_host(const Resolved& r, const int32_t* kv_lens_h,
   P.num_levels = num_levels;
   P.num_ctas = p.num_ctas;
   P.level_ctas = p.level_ctas;
+  P.lvl_streams = p.level_streams;   // resolved from the device by pkc_plan (0 in host-only plans)
 
   // Levels: every item gets a state block of T_q rows (rows numbered level by level), except
   // write-through level items, which write their rows' final output.
@@ -323,14 +326,9 @@ pkc_status build_plan_host(const Resolved& r, const int32_t* kv_lens_h,
   }
   row += slots;
   P.dec_items = (int32_t)dec.items.size();
-  // Waves per decode workgroup: a workgroup splits its item's pages over its waves, so short
-  // items run on fewer waves (less merging, more steps per wave) and long ones on four.
-  {
-    int64_t tokens = 0;
-    for (const Item& it : dec.items) tokens += it.ke - it.kb;
-    const int64_t avg = dec.items.empty() ? 0 : tokens / (int64_t)dec.items.size();
-    P.dec_waves = p.decode_waves ? p.decode_waves : (avg >= 256 ? 4 : (avg >= 64 ? 2 : 1));
-  }
+  // Waves per decode workgroup (its waves split an item's pages): a launch shape, so it comes
+  // from the parameters only and stays the same for every plan of one workspace.
+  P.dec_waves = p.decode_waves ? p.decode_waves : 4;
   P.dec_slots = slots;
   P.dec_kv_chunk = dec.kv_chunk;
   P.state_rows = row;

@@ -298,8 +298,16 @@ __global__ __launch_bounds__(64 * prefix_detail::kWavesPerStream * NS, NS == 1 ?
     const int kb = scalar_load(rec + 3), srow = scalar_load(rec + 5);
     int ke = scalar_load(rec + 4);
     const int nrows = nq * G;
-    const int pbeg = p.page_indptr ? scalar_load(p.page_indptr + grp) : grp * p.table_stride;
-    const int npages_grp = p.page_indptr ? scalar_load(p.page_indptr + grp + 1) - pbeg : p.table_stride;
+    // A group's page run [pbeg, pbeg + npages_grp) is clamped into the page list, so a
+    // malformed indptr cannot make the scalar loads below read past it.
+    int pbeg, npages_grp;
+    if (p.page_indptr) {
+      pbeg = min(max(scalar_load(p.page_indptr + grp), 0), p.num_page_indices);
+      npages_grp = min(max(scalar_load(p.page_indptr + grp + 1) - pbeg, 0), p.num_page_indices - pbeg);
+    } else {
+      pbeg = grp * p.table_stride;
+      npages_grp = p.table_stride;
+    }
     const int32_t* pages = p.page_indices + pbeg;
     // Causal mask: query i of the item (rows i * G ..) sees tokens t <= lim0 + i, where lim0
     // is the limit of the item's first query (its queries are the group's last l_q tokens).

@@ -37,6 +37,27 @@ class PoolView:
         return self.t[p, s, int(head)].float().cpu().numpy()
 
 
+class HostPool:
+    """Like PoolView, over a host copy of the pool taken once (the full-size tests gather every
+    request's rows for several heads; one device-to-host copy is much cheaper than a copy per
+    request).  Rows come back upcast exactly to float32."""
+
+    def __init__(self, t):
+        self.t = t.detach().cpu()
+        self.shape = tuple(t.shape)
+
+    def __getitem__(self, idx):
+        pages, slots, head = idx
+        p = torch.as_tensor(np.asarray(pages), dtype=torch.long)
+        s = torch.as_tensor(np.asarray(slots), dtype=torch.long)
+        return self.t[p, s, int(head)].float().numpy()
+
+
+# Query heads compared at full size: every request (so every row of the 128-row MFMA tile and
+# every decode workgroup's item) on three heads spread over the head range.
+FULL_SIZE_HEADS = [0, 13, 31]
+
+
 def host(t):
     """Exact float64 host copy of a small device tensor."""
     return t.detach().float().cpu().double().numpy()
@@ -47,15 +68,21 @@ def host(t):
 OUT_PRECISION = {torch.float16: 11, torch.bfloat16: 8, torch.float32: 24}
 
 
-def check_state(o, lse, o_ref, lse_ref, dtype, label="", rows=None):
+def check_state(o, lse, o_ref, lse_ref, dtype, label="", rows=None, rounding_allowance=False):
     """Max |dO| and |dLSE| against the oracle over the computed (non-NaN) reference entries.
 
-    `dtype` is the input dtype: it sets the accumulation budget (2e-3 / 1e-3 for 16-bit
-    inputs, 1e-5 for fp32).  On top of it, O may differ by the one final rounding to its own
-    storage dtype, |O_ref| * 2^-p (p = 11 for fp16, 8 for bf16).  LSE is always fp32.
+    `dtype` is the input dtype and sets the bound: |dO| <= 2e-3 and |dLSE| <= 1e-3 for 16-bit
+    inputs with fp32 accumulation, 1e-5 for fp32 inputs (elementwise, absolute).
+
+    ``rounding_allowance`` is for the stress cases with N(0, 1) inputs only: there a few
+    tokens can give |O| near 1 or above, and the one final rounding of O to a bf16 output
+    alone moves it by up to |O| * 2^-8 (3.9e-3 at |O| = 1), more than the absolute budget.
+    With it, O may also differ by |O_ref| * 2^-p (p = 11 for fp16, 8 for bf16).  The standard
+    workloads (values N(0, 1) * 0.5, |O| well below 0.5) are checked without it.
+
     -inf LSE must match exactly, and the output must be finite there."""
     tol_o, tol_l = TOL[dtype]
-    rnd = 2.0 ** -OUT_PRECISION[o.dtype]
+    rnd = 2.0 ** -OUT_PRECISION[o.dtype] if rounding_allowance else 0.0
     o = host(o)
     lse = lse.detach().cpu().double().numpy()
     mask = ~np.isnan(lse_ref)
@@ -73,8 +100,9 @@ def check_state(o, lse, o_ref, lse_ref, dtype, label="", rows=None):
     allowed = tol_o + np.abs(o_ref[mask]) * rnd
     d_o = float(np.max(err))
     worst = float(np.max(err - allowed))
-    say(f"  {label}: max|dO| = {d_o:.3e} (tol {tol_o:g} + |O|*2^-{-int(np.log2(rnd))}), "
-        f"max|dLSE| = {d_l:.3e} (tol {tol_l:g})")
+    bound = f"tol {tol_o:g} + |O|*2^-{-int(np.log2(rnd))}" if rnd else f"tol {tol_o:g}"
+    say(f"  {label}: max|dO| = {d_o:.3e} ({bound}), max|dLSE| = {d_l:.3e} (tol {tol_l:g}), "
+        f"{int(mask.sum())} (row, head) states compared")
     assert worst <= 0.0, f"{label}: |dO| exceeds its bound by {worst} (max|dO| {d_o})"
     assert d_l <= tol_l, f"{label}: max|dLSE| {d_l} > {tol_l}"
     return d_o, d_l
@@ -98,3 +126,17 @@ class CodeView:
         p = torch.as_tensor(np.asarray(pages), dtype=torch.long, device=dev)
         s = torch.as_tensor(np.asarray(slots), dtype=torch.long, device=dev)
         return self.t[p, s, int(head)].cpu().numpy()
+
+
+class HostCodeView:
+    """Like CodeView, over a host copy of the FP8 pool's bytes taken once."""
+
+    def __init__(self, t):
+        self.t = t.detach().view(torch.uint8).cpu()
+        self.shape = tuple(t.shape)
+
+    def __getitem__(self, idx):
+        pages, slots, head = idx
+        p = torch.as_tensor(np.asarray(pages), dtype=torch.long)
+        s = torch.as_tensor(np.asarray(slots), dtype=torch.long)
+        return self.t[p, s, int(head)].numpy()

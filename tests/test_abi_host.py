@@ -3,7 +3,11 @@
 * libpkc.so loads and exports every function include/pkc.h declares;
 * the C++ plan (pkc_plan_host) equals the oracle plan bit for bit: work items,
   their CTA assignment and order, partial-state rows, merge lists and
-  write-through flags, for plain split-KV decode and for cascades;
+  write-through flags, for plain split-KV decode and for cascades.  The oracle
+  plan follows appendix D's write-through rule; the library also finishes a
+  request whose merge list is its level states plus one own chunk in that
+  chunk's decode item, so the comparison is against ``fused_fold`` of the
+  oracle plan (tests/plan_transform.py);
 * argument validation rejects bad shapes before any HIP call;
 * the host block-table validator on the "Paged attention" worked example.
 """
@@ -18,6 +22,7 @@ import pytest
 import torch
 
 from oracle import plan as oplan
+from plan_transform import fused_fold
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "pkc.h")
@@ -53,6 +58,7 @@ def test_abi_struct_sizes(api):
 
 
 def _compare_plan(api, info, hb, o, levels, tile_q):
+    o = fused_fold(o)
     arr = api.read_plan_arrays(info, hb)
     # decode stage
     for c, recs in enumerate(arr["decode"]):

@@ -11,7 +11,7 @@ import torch
 
 from oracle import attention as oatt
 from paged_kv_cascade_amd import workloads
-from tests.gpu_helpers import PoolView, check_state, gpu, host, needs_gpu, say
+from tests.gpu_helpers import FULL_SIZE_HEADS, HostPool, PoolView, check_state, gpu, host, needs_gpu, say
 
 pytestmark = [gpu, needs_gpu]
 
@@ -39,8 +39,9 @@ def _run_cascade(api, w, level_ctas=0, num_ctas=0, enable_split=True, tile_q=0):
     return o, lse, info, ws, devs, keep
 
 
-def _oracle(w, requests=None, heads=None):
-    return oatt.cascade_decode(host(w.q), PoolView(w.k_pool), PoolView(w.v_pool), w.page_size, w.sm_scale,
+def _oracle(w, requests=None, heads=None, pools=None):
+    kp, vp = pools if pools is not None else (PoolView(w.k_pool), PoolView(w.v_pool))
+    return oatt.cascade_decode(host(w.q), kp, vp, w.page_size, w.sm_scale,
                                w.levels, w.block_table.cpu().numpy(), w.cache_seqlens.cpu().numpy(),
                                requests=requests, heads=heads)
 
@@ -56,7 +57,7 @@ def test_two_level_cascade_full_size(api, grid):
     """Shared prefix 32768 tokens (pages 0..2047) + 256 unique tokens per request in
     permuted pages, batch 128, 32 heads x 128, fp16."""
     say(f"case: two-level cascade prefix32768 suffix256 b128 h32 d128 p16 fp16 level grid {grid} "
-        "(full size, sampled oracle)")
+        "(full size, every request on heads 0, 13, 31)")
     w = workloads.cascade_two_level(device="cuda")
     api.validate_block_table(w.block_table.cpu(), w.cache_seqlens.cpu(), w.page_size, w.num_pages)
     lc = _level_grid(api, grid, w.num_kv_heads)
@@ -66,22 +67,20 @@ def test_two_level_cascade_full_size(api, grid):
     assert torch.equal(o, o2) and torch.equal(lse, lse2), "repeat run differs"
     say(f"  plan: level chunk={info.lvl_kv_chunk[0]} level items={info.lvl_items[0]} "
         f"suffix items={info.dec_items} rows={info.state_rows}")
-    reqs = [0, 77, 127]
-    O, L = _oracle(w, requests=reqs)
-    check_state(o, lse, O, L, torch.float16, "cascade 32K prefix", rows=reqs)
+    O, L = _oracle(w, heads=FULL_SIZE_HEADS, pools=(HostPool(w.k_pool), HostPool(w.v_pool)))
+    check_state(o, lse, O, L, torch.float16, "cascade 32K prefix")
 
 
 @pytest.mark.parametrize("grid", ["default", "two_per_cu"])
 def test_multi_level_cascade_full_size(api, grid):
     """Global prefix 16384 + 4 groups x 4096 + 512 per request, batch 128, fp16."""
     say(f"case: three-level cascade 16384 + 4x4096 + 512, b128 h32 d128 fp16 level grid {grid} "
-        "(full size, sampled oracle)")
+        "(full size, every request on heads 0, 13, 31)")
     w = workloads.cascade_multi_level(device="cuda")
     o, lse, info, *_ = _run_cascade(api, w, level_ctas=_level_grid(api, grid, w.num_kv_heads))
     torch.cuda.synchronize()
-    reqs = [0, 40, 95, 127]
-    O, L = _oracle(w, requests=reqs)
-    check_state(o, lse, O, L, torch.float16, "cascade 3 levels", rows=reqs)
+    O, L = _oracle(w, heads=FULL_SIZE_HEADS, pools=(HostPool(w.k_pool), HostPool(w.v_pool)))
+    check_state(o, lse, O, L, torch.float16, "cascade 3 levels")
 
 
 def _small_cascade(seed, dtype, D, g, P, hkv=2):
@@ -153,7 +152,7 @@ def test_small_cascades(api, seed):
             for kk in range(mx):
                 assert tr[c, kk].tolist() == (list(recs[kk]) if kk < len(recs) else [-1] * 8)
     O, L = _oracle(w)
-    check_state(o, lse, O, L, dtype, f"small cascade {seed}")
+    check_state(o, lse, O, L, dtype, f"small cascade {seed}", rounding_allowance=True)
 
 
 def test_prefix_attention_standalone(api):

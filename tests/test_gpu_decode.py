@@ -18,7 +18,7 @@ from oracle import attention as oatt
 from oracle import indexing as oidx
 from oracle import merge as omerge
 from paged_kv_cascade_amd import workloads
-from tests.gpu_helpers import PoolView, check_state, gpu, host, needs_gpu, say
+from tests.gpu_helpers import FULL_SIZE_HEADS, HostPool, PoolView, check_state, gpu, host, needs_gpu, say
 
 pytestmark = [gpu, needs_gpu]
 
@@ -101,7 +101,8 @@ def test_gather_rows_worked_example_bit_exact(api):
 
 
 def test_llama_shape_decode_full_size(api):
-    say("case: paged decode b64 h32 d128 len4096 p16 fp16, permuted pages (full size, sampled oracle)")
+    say("case: paged decode b64 h32 d128 len4096 p16 fp16, permuted pages (full size, every request on "
+        "heads 0, 13, 31)")
     w = workloads.paged_decode(device="cuda")
     api.validate_block_table(w.block_table.cpu(), w.cache_seqlens.cpu(), w.page_size, w.num_pages)
     o, lse = api.batch_decode_paged(w.q, w.k_pool, w.v_pool, w.block_table, w.cache_seqlens,
@@ -110,9 +111,9 @@ def test_llama_shape_decode_full_size(api):
                                       sm_scale=w.sm_scale)
     torch.cuda.synchronize()
     assert torch.equal(o, o2) and torch.equal(lse, lse2), "repeat run differs"
-    reqs = [0, 17, 42, 63]
-    O, L = _oracle_decode(w, requests=reqs)
-    check_state(o, lse, O, L, torch.float16, "decode b64 len4096", rows=reqs)
+    O, L = oatt.batch_decode(host(w.q), HostPool(w.k_pool), HostPool(w.v_pool), w.block_table.cpu().numpy(),
+                             w.cache_seqlens.cpu().numpy(), w.page_size, w.sm_scale, heads=FULL_SIZE_HEADS)
+    check_state(o, lse, O, L, torch.float16, "decode b64 len4096")
 
 
 def test_uniform_scores_count_tokens(api):
@@ -203,7 +204,7 @@ def test_ragged_decode_matrix(api, dtype, D, g, P):
     torch.cuda.synchronize()
     O, L = oatt.batch_decode(host(q), PoolView(k), PoolView(v), bt.numpy(), lens.numpy(), P,
                              1.0 / math.sqrt(D), kv_start=None if ks is None else ks.numpy())
-    check_state(o, lse, O, L, dtype, f"ragged {dtype} D{D} g{g} P{P}")
+    check_state(o, lse, O, L, dtype, f"ragged {dtype} D{D} g{g} P{P}", rounding_allowance=True)
 
 
 @pytest.mark.parametrize("in_dt,out_dt", [(torch.float32, torch.float32), (torch.float32, torch.float16),
@@ -230,11 +231,11 @@ def test_merge_states_matches_oracle(api, in_dt, out_dt, D):
     for i, idx in enumerate(lists):
         ref_o[i], ref_l[i] = omerge.merge_many(O[idx], Ls[idx]) if idx else omerge.merge_many(np.zeros((0, H, D)), np.zeros((0, H)))
     tol = torch.float32 if (in_dt == torch.float32 and out_dt == torch.float32) else torch.float16
-    check_state(mo, ml, ref_o, ref_l, tol, "merge csr")
+    check_state(mo, ml, ref_o, ref_l, tol, "merge csr", rounding_allowance=True)
     # dense form: 8 outputs x 5 states each
     mo, ml = api.merge_states(o, lse, states_per_output=5, out_dtype=out_dt)
     ref = [omerge.merge_many(O[5 * i:5 * i + 5], Ls[5 * i:5 * i + 5]) for i in range(8)]
-    check_state(mo, ml, np.stack([r[0] for r in ref]), np.stack([r[1] for r in ref]), tol, "merge dense")
+    check_state(mo, ml, np.stack([r[0] for r in ref]), np.stack([r[1] for r in ref]), tol, "merge dense", rounding_allowance=True)
 
 
 def test_merge_inplace_matches_oracle_and_is_symmetric(api):
@@ -254,5 +255,5 @@ def test_merge_inplace_matches_oracle_and_is_symmetric(api):
         y, yl = b.clone(), lb.clone()
         api.merge_state_inplace(y, yl, a, la)
         torch.cuda.synchronize()
-        check_state(x, xl, ro, rl, torch.float32 if dt == torch.float32 else torch.float16, f"inplace {dt}")
+        check_state(x, xl, ro, rl, torch.float32 if dt == torch.float32 else torch.float16, f"inplace {dt}", rounding_allowance=True)
         assert torch.equal(x, y) and torch.equal(xl, yl)

@@ -104,7 +104,7 @@ def test_random_ragged_prefill(api, seed):
     q, k, v, bt = _case(900 + seed, lq, lkv, dtype, D, g, P)
     o, lse, qi, _ = _run(api, q, k, v, bt, lq, lkv, causal, level_ctas=lctas, tile_q=tile_q)
     O, L = _oracle(q, k, v, bt, qi, lkv, causal)
-    check_state(o, lse, O, L, dtype, f"prefill seed {seed}")
+    check_state(o, lse, O, L, dtype, f"prefill seed {seed}", rounding_allowance=True)
 
 
 def test_long_causal_prefill_sampled(api):

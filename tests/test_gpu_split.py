@@ -12,7 +12,7 @@ import torch
 from oracle import attention as oatt
 from oracle import plan as oplan
 from paged_kv_cascade_amd import workloads
-from tests.gpu_helpers import PoolView, check_state, gpu, host, needs_gpu, say
+from tests.gpu_helpers import FULL_SIZE_HEADS, HostPool, PoolView, check_state, gpu, host, needs_gpu, say
 
 pytestmark = [gpu, needs_gpu]
 
@@ -56,11 +56,10 @@ def test_gqa_split_full_size(api):
     o_plan = oplan.cascade_plan(w.batch, [], lens, num_ctas=2 * cus, level_ctas=1, level_tile_q=[])
     for c, recs in enumerate(arr["decode"]):
         assert [r[7] for r in recs] == o_plan.suffix.cta_items[c]
-    order = np.argsort(lens)
-    reqs = sorted({int(order[0]), int(order[1]), int(order[-1]), int(order[-2]), 5, 100, 200})
-    O, L = oatt.batch_decode(host(w.q), PoolView(w.k_pool), PoolView(w.v_pool),
-                             w.block_table.cpu().numpy(), np.array(lens), 16, w.sm_scale, requests=reqs)
-    check_state(o, lse, O, L, torch.bfloat16, "GQA split-KV", rows=reqs)
+    # every request on query heads 0, 13, 31 (kv heads 0, 3, 7): every decode workgroup's items
+    O, L = oatt.batch_decode(host(w.q), HostPool(w.k_pool), HostPool(w.v_pool),
+                             w.block_table.cpu().numpy(), np.array(lens), 16, w.sm_scale, heads=FULL_SIZE_HEADS)
+    check_state(o, lse, O, L, torch.bfloat16, "GQA split-KV")
 
 
 @pytest.mark.parametrize("seed", range(6))
@@ -100,8 +99,8 @@ def test_split_ragged_random(api, seed):
     arr = api.read_plan_arrays(info, ws.host)
     _check_trace(api, info, arr["decode"], 0)
     O, L = oatt.batch_decode(host(q), PoolView(k), PoolView(v), bt.numpy(), np.array(lens), P, 0.3)
-    check_state(o, lse, O, L, dtype, "split plan")
-    check_state(o_ref, l_ref, O, L, dtype, "no plan")
+    check_state(o, lse, O, L, dtype, "split plan", rounding_allowance=True)
+    check_state(o_ref, l_ref, O, L, dtype, "no plan", rounding_allowance=True)
 
 
 def test_plan_reuse_across_steps(api):

@@ -140,7 +140,9 @@ def test_lpt_graham_bound(seed):
 
 def test_cascade_plan_merge_lists():
     """Level states first (levels in order, chunks ascending), then the
-    request's own chunks; write-through only for requests no level covers."""
+    request's own chunks; write-through (appendix D) only for an item that is
+    its request's only state: one own chunk and no level covering the request.
+    Worked by hand from the scheduler's steps."""
     levels = [{"qo_indptr": [0, 4], "kv_lens": [40]},
               {"qo_indptr": [0, 2, 3], "kv_lens": [10, 0]}]
     cp = plan.cascade_plan(5, levels, [8, 0, 30, 3, 4], num_ctas=4, level_ctas=2,
@@ -157,16 +159,78 @@ def test_cascade_plan_merge_lists():
     assert cp.suffix.kv_chunk == 12
     assert [(it.req, it.kv_begin, it.kv_end) for it in cp.suffix.items] == \
         [(0, 0, 8), (2, 0, 12), (2, 12, 24), (2, 24, 30), (3, 0, 3), (4, 0, 4)]
-    # single-chunk requests (0, 3, 4) are finished by their decode item, which folds in the
-    # level states of their merge list; request 2 (3 chunks) and request 1 (no own KV) are
-    # finished by the merge pass
-    assert cp.suffix.slots == [-1, 0, 1, 2, -1, -1]
-    assert cp.write_through == [True, False, False, True, True]
-    assert cp.merge[0] == [(0, 0, 0), (1, 0, 0)]
+    # requests 0..3 are covered by level 0, so their own chunks are partial states even when
+    # single (requests 0 and 3); request 4 (no level, one chunk) writes through
+    assert cp.suffix.slots == [0, 1, 2, 3, 4, -1]
+    assert cp.write_through == [False, False, False, False, True]
+    assert cp.merge[0] == [(0, 0, 0), (1, 0, 0), ("suffix", 0, 0)]
     assert cp.merge[1] == [(0, 0, 1), (1, 1, 0)]
-    assert cp.merge[2] == [(0, 1, 0), ("suffix", 0, 0), ("suffix", 1, 0), ("suffix", 2, 0)]
-    assert cp.merge[3] == [(0, 1, 1)]
+    assert cp.merge[2] == [(0, 1, 0), ("suffix", 1, 0), ("suffix", 2, 0), ("suffix", 3, 0)]
+    assert cp.merge[3] == [(0, 1, 1), ("suffix", 4, 0)]
     assert cp.merge[4] == []
+
+
+def test_fused_fold_transform_hand_example():
+    """The library finishes a request whose merge list is its level states plus one own chunk
+    in that chunk's decode item (the item folds the level states in): the transform of the
+    appendix-D plan above makes requests 0 and 3 write-through, drops their own chunk from
+    their merge lists and renumbers the remaining partial slots densely in ascending w."""
+    from plan_transform import fused_fold
+    levels = [{"qo_indptr": [0, 4], "kv_lens": [40]},
+              {"qo_indptr": [0, 2, 3], "kv_lens": [10, 0]}]
+    cp = plan.cascade_plan(5, levels, [8, 0, 30, 3, 4], num_ctas=4, level_ctas=2,
+                           level_tile_q=[2, 1], alpha=1, beta=1)
+    f = fused_fold(cp)
+    assert f.suffix.slots == [-1, 0, 1, 2, -1, -1]
+    assert f.write_through == [True, False, False, True, True]
+    assert f.merge[0] == [(0, 0, 0), (1, 0, 0)]
+    assert f.merge[1] == [(0, 0, 1), (1, 1, 0)]
+    assert f.merge[2] == [(0, 1, 0), ("suffix", 0, 0), ("suffix", 1, 0), ("suffix", 2, 0)]
+    assert f.merge[3] == [(0, 1, 1)]
+    assert f.merge[4] == []
+    # the appendix-D plan itself is unchanged
+    assert cp.suffix.slots == [0, 1, 2, 3, 4, -1]
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_fused_fold_keeps_items_and_states(seed):
+    """The fold moves no work: the same items on the same CTAs in the same order, level slots
+    unchanged, and per request the same set of states combined (a folded request's own chunk
+    is the finishing item itself instead of a merge-list entry)."""
+    from plan_transform import fused_fold
+    rng = random.Random(seed)
+    B = rng.randint(1, 40)
+    levels = []
+    for _ in range(rng.randint(0, 3)):
+        cuts = sorted(rng.sample(range(0, B + 1), min(rng.randint(2, 5), B + 1)))
+        if len(cuts) < 2:
+            cuts = [0, B]
+        levels.append({"qo_indptr": cuts, "kv_lens": [rng.choice([0, 7, rng.randint(1, 900)])
+                                                       for _ in range(len(cuts) - 1)]})
+    kv = [rng.choice([0, 3, 64, rng.randint(0, 700)]) for _ in range(B)]
+    tq = [rng.choice([1, 2, 8]) for _ in levels]
+    cp = plan.cascade_plan(B, levels, kv, num_ctas=rng.choice([1, 4, 16]), level_ctas=rng.choice([1, 3]),
+                           level_tile_q=tq, enable_split=rng.random() < 0.8)
+    f = fused_fold(cp)
+    assert [it.w for it in f.suffix.items] == [it.w for it in cp.suffix.items]
+    assert f.suffix.cta_items == cp.suffix.cta_items
+    assert [st.slots for st in f.levels] == [st.slots for st in cp.levels]
+    n_slots = sum(1 for s in f.suffix.slots if s >= 0)
+    assert sorted(s for s in f.suffix.slots if s >= 0) == list(range(n_slots))
+    own = {}
+    for it in cp.suffix.items:
+        own.setdefault(it.req, []).append(it.w)
+    for b in range(B):
+        lv_a = [e for e in cp.merge[b] if e[0] != "suffix"]
+        lv_b = [e for e in f.merge[b] if e[0] != "suffix"]
+        assert lv_a == lv_b
+        states_a = sorted(cp.suffix.slots.index(e[1]) for e in cp.merge[b] if e[0] == "suffix")
+        states_b = sorted(f.suffix.slots.index(e[1]) for e in f.merge[b] if e[0] == "suffix")
+        if f.write_through[b] and not cp.write_through[b]:
+            assert len(own.get(b, [])) == 1 and states_b == [] and states_a == own[b]
+            assert f.suffix.slots[own[b][0]] == -1
+        else:
+            assert states_a == states_b and f.write_through[b] == cp.write_through[b]
 
 
 # --- causal query tiles (ragged multi-token queries) -----------------------------------------
