@@ -92,7 +92,8 @@ def test_append_twice_in_place_then_decode(api, dtype):
     torch.cuda.synchronize()
     O, L = oatt.batch_decode(host(q), PoolView(k_pool), PoolView(v_pool), bt.cpu().numpy(), lens.cpu().numpy(), P,
                              1.0 / np.sqrt(D))
-    check_state(o, lse, O, L, dtype, "decode after two appends")
+    # requests of 0..2 cached tokens give |O| near 1: bf16 output rounding alone exceeds 2e-3
+    check_state(o, lse, O, L, dtype, "decode after two appends", rounding_allowance=dtype == torch.bfloat16)
 
 
 def test_append_to_unallocated_block_is_skipped(api):

@@ -127,8 +127,9 @@ def test_single_token_requests_match_decode(api):
                                       sm_scale=1.0 / math.sqrt(128))
     torch.cuda.synchronize()
     O, L = _oracle(q, k, v, bt, qi, lkv, True)
-    check_state(o, lse, O, L, torch.bfloat16, "prefill l_q = 1")
-    check_state(od, lsed, O, L, torch.bfloat16, "decode")
+    # one- and two-token requests give |O| near 1: bf16 output rounding alone exceeds 2e-3
+    check_state(o, lse, O, L, torch.bfloat16, "prefill l_q = 1", rounding_allowance=True)
+    check_state(od, lsed, O, L, torch.bfloat16, "decode", rounding_allowance=True)
 
 
 def test_prefill_rejects_plan_of_other_shape(api):
@@ -161,7 +162,8 @@ def test_write_through_and_merged_rows_agree(api, causal):
     assert info_wt.num_merge < info_m.num_merge == sum(lq)
     O, L = _oracle(q, k, v, bt, res[True][2], lkv, causal)
     for wt in (True, False):
-        check_state(res[wt][0], res[wt][1], O, L, torch.bfloat16, f"write_through={wt}")
+        # causal first rows see one or two tokens (|O| near 1; bf16 output rounding)
+        check_state(res[wt][0], res[wt][1], O, L, torch.bfloat16, f"write_through={wt}", rounding_allowance=True)
 
 
 def test_write_through_plan_runs_only_as_prefill(api):
@@ -224,7 +226,8 @@ def test_tree_masked_prefill(api, seed):
     o, lse, qi = _run_tree(api, q, k, v, bt, lq, lkv, masks, level_ctas=lctas)
     O, L = oatt.batch_prefill(host(q), qi, PoolView(k), PoolView(v), bt.numpy(), lkv, P, 1.0 / math.sqrt(D), True,
                               tree_masks=masks)
-    check_state(o, lse, O, L, dtype, f"tree prefill seed {seed}")
+    # tree rows see few tokens (|O| near 1): bf16 output rounding alone exceeds 2e-3
+    check_state(o, lse, O, L, dtype, f"tree prefill seed {seed}", rounding_allowance=dtype == torch.bfloat16)
 
 
 def test_tree_mask_of_ones_is_the_causal_prefill(api):
