@@ -331,6 +331,34 @@ pkc_status pkc_cascade_decode(const pkc_plan_info* plan, const void* q, const vo
                               size_t dev_bytes, void* stream);
 
 /*
+ * Allocation-free split-KV batch decode, for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * computation and kernels as pkc_batch_decode_paged with a plan, but the workspace is a fixed
+ * device array inside the library (PKC_NOALLOC_SCRATCH_BYTES per GPU, held by every GPU the
+ * library runs on until the process ends) instead of a caller-provided one; the call
+ * allocates and frees nothing.
+ *   plan:          a plan without levels built by pkc_plan_host (or pkc_plan: its workspace is
+ *                  ignored) for these shapes; its integer arrays are in plan_host_buf
+ *                  (plan_host_bytes >= plan->int_bytes).  The call enqueues their copy into the
+ *                  array on `stream` before the kernels; a page-locked buffer is read by a
+ *                  kernel and must stay untouched until that copy has run.
+ *   other arguments: as pkc_batch_decode_paged.
+ * Errors: PKC_ERR_WORKSPACE_TOO_SMALL when the plan needs more than PKC_NOALLOC_SCRATCH_BYTES of
+ * workspace (plan->dev_bytes; decided before any HIP call), PKC_ERR_PLAN_MISMATCH for a plan
+ * with levels or other shapes.  Every call on one GPU shares that GPU's array: calls that
+ * overlap on one GPU (different streams or threads) race; calls on one stream run in order.
+ */
+#define PKC_NOALLOC_SCRATCH_BYTES (32u << 20)
+pkc_status pkc_batch_decode_paged_noalloc(const pkc_plan_info* plan, const void* plan_host_buf,
+                                          size_t plan_host_bytes, const void* q, const void* k_pool,
+                                          const void* v_pool, int64_t num_pages,
+                                          const int32_t* block_table, int32_t max_blocks,
+                                          const int32_t* cache_seqlens, const int32_t* kv_start,
+                                          int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
+                                          int32_t head_dim, int32_t page_size, pkc_dtype dtype,
+                                          float sm_scale, void* o, float* lse, void* stream);
+
+/*
  * Paged batch decode over FP8 K/V pools (the FlashInfer paper summary, appendix F: KV in fp8
  * with fp16 queries and outputs).  The pools hold OCP FP8 E4M3 codes, one byte per element,
  * same layout [num_pages, P, Hkv, D]; element value = decoded code * k_scale (K) or * v_scale

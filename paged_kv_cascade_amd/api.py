@@ -103,6 +103,8 @@ SIGNATURES = {
                              ctypes.POINTER(LevelHost), _I32, _P, _SZ, ctypes.POINTER(PlanInfo)]),
     "pkc_batch_decode_paged": (_I32, [ctypes.POINTER(PlanInfo), _P, _P, _P, _I64, _P, _I32, _P, _P,
                                       _I32, _I32, _I32, _I32, _I32, _I32, _F, _P, _P, _P, _SZ, _P]),
+    "pkc_batch_decode_paged_noalloc": (_I32, [ctypes.POINTER(PlanInfo), _P, _SZ, _P, _P, _P, _I64, _P, _I32,
+                                              _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _F, _P, _P, _P]),
     "pkc_prefix_attention": (_I32, [ctypes.POINTER(PlanInfo), _I32, _P, _P, _P, _I64,
                                     ctypes.POINTER(LevelDev), _I32, _I32, _I32, _I32, _I32, _I32,
                                     _F, _P, _I32, _P, _P, _SZ, _P]),
@@ -310,6 +312,35 @@ def batch_decode_paged(q, k_pool, v_pool, block_table, cache_seqlens, kv_start=N
                                       B, Hq, Hkv, D, P, dtype_code(q.dtype), scale, _ptr(out),
                                       _ptr(lse), ws, wsn, _stream(dev)))
     return out, lse
+
+
+def batch_decode_paged_noalloc(plan_info: PlanInfo, plan_host_buf, q, k_pool, v_pool, block_table,
+                               cache_seqlens, kv_start=None, sm_scale=None, out=None, lse=None):
+    """pkc_batch_decode_paged_noalloc: split-KV decode from a host-built plan (plan_host) whose
+    workspace is the library's fixed device array.  Returns (o, lse); with ``out`` and ``lse``
+    given, nothing is allocated on the device."""
+    B, Hq, D = q.shape
+    N, P, Hkv, D2 = k_pool.shape
+    dev = q.device
+    for t, n in ((q, "q"), (k_pool, "k_pool"), (v_pool, "v_pool")):
+        _need(t, n, q.dtype, dev)
+    _need(block_table, "block_table", torch.int32, dev)
+    if kv_start is not None:
+        _need(kv_start, "kv_start", torch.int32, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+    scale = 1.0 / math.sqrt(D) if sm_scale is None else float(sm_scale)
+    _check(lib.pkc_batch_decode_paged_noalloc(ctypes.byref(plan_info), _ptr(plan_host_buf), plan_host_buf.numel(),
+                                              _ptr(q), _ptr(k_pool), _ptr(v_pool), N, _ptr(block_table),
+                                              block_table.shape[1], _ptr(cache_seqlens), _ptr(kv_start),
+                                              B, Hq, Hkv, D, P, dtype_code(q.dtype), scale, _ptr(out),
+                                              _ptr(lse), _stream(dev)))
+    return out, lse
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 def append_kv(k_new, v_new, k_pool, v_pool, block_table, cache_seqlens, new_seqlens=None):

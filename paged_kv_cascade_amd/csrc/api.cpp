@@ -10,6 +10,7 @@
 #include <string>
 #include <vector>
 
+#include "api_internal.h"
 #include "kernels.h"
 #include "plan_core.h"
 
@@ -246,9 +247,11 @@ pkc_status run_level(const pkc_plan_info* plan, int level, const void* q, const 
   });
 }
 
+}  // namespace
+
 // True when host_buf is page-locked host memory the device can read (hipHostMalloc / torch
 // pin_memory); the last answer is cached per pointer.
-bool host_buf_is_pinned(const void* host_buf) {
+bool pkc::host_buf_is_pinned(const void* host_buf) {
   static thread_local const void* last = nullptr;
   static thread_local bool last_pinned = false;
   if (host_buf == last) return last_pinned;
@@ -260,6 +263,8 @@ bool host_buf_is_pinned(const void* host_buf) {
   last_pinned = pinned;
   return pinned;
 }
+
+namespace {
 
 // Checks the parameters and fills #CTA defaults from the current device.  A stage launches
 // #CTA x Hkv workgroups.  Decode workgroups are small (4 waves, a few dozen VGPRs each) and
@@ -392,7 +397,7 @@ pkc_status pkc_plan(const pkc_plan_params* params, const int32_t* kv_lens_h,
     return fail(PKC_ERR_WORKSPACE_TOO_SMALL, "device workspace smaller than " + std::to_string(out->dev_bytes) + " bytes");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
-  if (host_buf_is_pinned(host_buf)) {
+  if (pkc::host_buf_is_pinned(host_buf)) {
     // A kernel on the caller's queue reads the pinned buffer: no copy-engine synchronisation.
     e = pkc::launch_plan_upload(host_buf, dev_ws, out->int_bytes, s);
     if (e != hipSuccess) return hip_fail(e, "plan upload launch");
@@ -405,15 +410,15 @@ pkc_status pkc_plan(const pkc_plan_params* params, const int32_t* kv_lens_h,
   PKC_TRY_END("pkc_plan")
 }
 
-static pkc_status decode_impl(bool fp8, float k_scale, float v_scale,
-                              const pkc_plan_info* plan, const void* q, const void* k_pool,
-                                  const void* v_pool, int64_t num_pages,
-                                  const int32_t* block_table, int32_t max_blocks,
-                                  const int32_t* cache_seqlens, const int32_t* kv_start,
-                                  int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
-                                  int32_t head_dim, int32_t page_size, pkc_dtype dtype,
-                                  float sm_scale, void* o, float* lse, void* dev_ws,
-                                  size_t dev_bytes, void* stream) {
+}  // extern "C"
+
+pkc_status pkc::decode_run(bool fp8, float k_scale, float v_scale, const pkc_plan_info* plan,
+                           const void* q, const void* k_pool, const void* v_pool, int64_t num_pages,
+                           const int32_t* block_table, int32_t max_blocks,
+                           const int32_t* cache_seqlens, const int32_t* kv_start, int32_t batch,
+                           int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t page_size, pkc_dtype dtype, float sm_scale, void* o, float* lse,
+                           void* dev_ws, size_t dev_bytes, void* stream, const void* plan_upload_src) {
   pkc_status st = check_shapes(batch, num_qo_heads, num_kv_heads, head_dim, page_size, dtype, sm_scale);
   if (st != PKC_OK) return st;
   if (fp8 && (st = check_fp8(dtype, k_scale, v_scale)) != PKC_OK) return st;
@@ -444,6 +449,15 @@ static pkc_status decode_impl(bool fp8, float k_scale, float v_scale,
     p.indptr = at<int32_t>(dev_ws, plan->off_dec_indptr);
     p.items = at<int32_t>(dev_ws, plan->off_dec_items);
     grid_x = plan->num_ctas;
+    if (plan_upload_src) {
+      // Every check has passed: copy the plan's integer arrays from the host buffer into the
+      // workspace on the same stream, ahead of the kernels that read them.
+      hipError_t e = pkc::host_buf_is_pinned(plan_upload_src)
+                         ? pkc::launch_plan_upload(plan_upload_src, dev_ws, plan->int_bytes, s)
+                         : hipMemcpyAsync(dev_ws, plan_upload_src, (size_t)plan->int_bytes,
+                                          hipMemcpyHostToDevice, s);
+      if (e != hipSuccess) return hip_fail(e, "plan upload");
+    }
   }
   const int waves = plan ? plan->dec_waves : 4;
   if ((st = timed(0, s, "decode kernel launch", [&] {
@@ -461,6 +475,8 @@ static pkc_status decode_impl(bool fp8, float k_scale, float v_scale,
   return PKC_OK;
 }
 
+extern "C" {
+
 pkc_status pkc_batch_decode_paged(const pkc_plan_info* plan, const void* q, const void* k_pool,
                                   const void* v_pool, int64_t num_pages,
                                   const int32_t* block_table, int32_t max_blocks,
@@ -470,10 +486,9 @@ pkc_status pkc_batch_decode_paged(const pkc_plan_info* plan, const void* q, cons
                                   float sm_scale, void* o, float* lse, void* dev_ws,
                                   size_t dev_bytes, void* stream) {
   PKC_TRY_BEGIN
-  return decode_impl(false, 1.f, 1.f, plan, q, k_pool, v_pool, num_pages,
-                     block_table, max_blocks, cache_seqlens, kv_start, batch, num_qo_heads,
-                     num_kv_heads, head_dim, page_size, dtype, sm_scale, o, lse, dev_ws, dev_bytes,
-                     stream);
+  return pkc::decode_run(false, 1.f, 1.f, plan, q, k_pool, v_pool, num_pages, block_table, max_blocks,
+                         cache_seqlens, kv_start, batch, num_qo_heads, num_kv_heads, head_dim,
+                         page_size, dtype, sm_scale, o, lse, dev_ws, dev_bytes, stream, nullptr);
   PKC_TRY_END("pkc_batch_decode_paged")
 }
 
@@ -487,10 +502,10 @@ pkc_status pkc_batch_decode_paged_fp8(const pkc_plan_info* plan, const void* q, 
                                       float sm_scale, void* o, float* lse, void* dev_ws,
                                       size_t dev_bytes, void* stream) {
   PKC_TRY_BEGIN
-  return decode_impl(true, k_scale, v_scale, plan, q, k_pool, v_pool,
-                     num_pages, block_table, max_blocks, cache_seqlens, kv_start, batch,
-                     num_qo_heads, num_kv_heads, head_dim, page_size, q_dtype, sm_scale, o, lse,
-                     dev_ws, dev_bytes, stream);
+  return pkc::decode_run(true, k_scale, v_scale, plan, q, k_pool, v_pool, num_pages, block_table,
+                         max_blocks, cache_seqlens, kv_start, batch, num_qo_heads, num_kv_heads,
+                         head_dim, page_size, q_dtype, sm_scale, o, lse, dev_ws, dev_bytes, stream,
+                         nullptr);
   PKC_TRY_END("pkc_batch_decode_paged_fp8")
 }
 

@@ -312,3 +312,27 @@ def test_append_and_tree_validation_before_any_launch(api):
     p2.level_write_through = 3
     with pytest.raises(api.PkcError):
         api.plan_host(p2, [1, 2])
+
+
+def test_noalloc_decode_refuses_oversized_plans_before_any_hip_call(api):
+    """The allocation-free decode checks the plan against its fixed array before touching the
+    device (dummy non-NULL pointers are never dereferenced), and refuses plans with levels."""
+    lib = api.lib
+    d = ctypes.c_void_p(0x1000)
+    B = 4096
+    info, hb = api.plan_host(api.make_params(B, 32, 32, 128, 16, num_ctas=B, level_ctas=1), [64] * B)
+    assert info.dev_bytes > api.NOALLOC_SCRATCH_BYTES
+    st = lib.pkc_batch_decode_paged_noalloc(ctypes.byref(info), ctypes.c_void_p(hb.data_ptr()), hb.numel(),
+                                            d, d, d, 4, d, 4, d, None, B, 32, 32, 128, 16, 1, 0.1, d, d, None)
+    assert st == 3 and "allocation-free" in lib.pkc_last_error().decode()
+    # a host buffer smaller than the plan's integer arrays
+    small, hb2 = api.plan_host(api.make_params(8, 4, 4, 128, 16, num_ctas=4, level_ctas=1), [100] * 8)
+    assert lib.pkc_batch_decode_paged_noalloc(ctypes.byref(small), ctypes.c_void_p(hb2.data_ptr()), 16,
+                                              d, d, d, 4, d, 8, d, None, 8, 4, 4, 128, 16, 1, 0.1, d, d,
+                                              None) == 1
+    # a plan with levels
+    lv = [{"qo_indptr": [0, 8], "kv_lens": [64]}]
+    info3, hb3 = api.plan_host(api.make_params(8, 4, 4, 128, 16, num_ctas=4, level_ctas=1), [10] * 8, lv)
+    assert lib.pkc_batch_decode_paged_noalloc(ctypes.byref(info3), ctypes.c_void_p(hb3.data_ptr()), hb3.numel(),
+                                              d, d, d, 4, d, 8, d, None, 8, 4, 4, 128, 16, 1, 0.1, d, d,
+                                              None) == 4
