@@ -215,8 +215,10 @@ def make_params(batch, num_qo_heads, num_kv_heads, head_dim, page_size, num_ctas
                       1 if level_write_through else 0, level_streams)
 
 
-class _Levels:
-    """Host level descriptors kept alive for one call."""
+class HostLevels:
+    """Host level descriptors (pkc_level_host) marshalled once; pass the object itself to
+    plan / plan_buffer_sizes / Workspace in place of the list of dicts to skip the conversion
+    (a serving loop plans every step with the same level shapes)."""
 
     def __init__(self, levels: Sequence[dict]):
         self.keep = []
@@ -233,7 +235,7 @@ class _Levels:
 
 
 def plan_buffer_sizes(params: PlanParams, levels: Sequence[dict] = ()):
-    lv = _Levels(levels)
+    lv = _levels_arg(levels)
     hb, db = _SZ(), _SZ()
     _check(lib.pkc_plan_buffer_sizes(ctypes.byref(params), lv.arr, lv.n, ctypes.byref(hb), ctypes.byref(db)))
     return hb.value, db.value
@@ -249,13 +251,28 @@ class Workspace:
         self.device = torch.empty(max(db, 256), dtype=torch.uint8, device=device)
 
 
+def _lens_arg(kv_lens):
+    """kv_lens as a C int32 pointer: an int32 CPU tensor is passed as it is (no copy), anything
+    else is converted."""
+    if isinstance(kv_lens, torch.Tensor):
+        if kv_lens.dtype != torch.int32 or kv_lens.device.type != "cpu" or not kv_lens.is_contiguous():
+            raise PkcError(1, "kv_lens tensor must be contiguous int32 on the CPU")
+        return ctypes.cast(kv_lens.data_ptr(), ctypes.POINTER(ctypes.c_int32))
+    return _i32_array(list(kv_lens))
+
+
+def _levels_arg(levels):
+    return levels if isinstance(levels, HostLevels) else HostLevels(levels)
+
+
 def plan(params: PlanParams, kv_lens, levels: Sequence[dict] = (), workspace: Workspace = None,
          device="cuda") -> PlanInfo:
-    """pkc_plan: build the plan on the CPU and enqueue its copy on the current stream."""
+    """pkc_plan: build the plan on the CPU and enqueue its copy on the current stream.
+    kv_lens: a sequence of ints or an int32 CPU tensor; levels: dicts or a HostLevels."""
     if workspace is None:
         raise PkcError(1, "plan needs a Workspace")
-    kl = _i32_array(list(kv_lens))
-    lv = _Levels(levels)
+    kl = _lens_arg(kv_lens)
+    lv = _levels_arg(levels)
     info = PlanInfo()
     _check(lib.pkc_plan(ctypes.byref(params), kl, lv.arr, lv.n, _ptr(workspace.host),
                         workspace.host.numel(), _ptr(workspace.device), workspace.device.numel(),
@@ -269,8 +286,8 @@ def plan_host(params: PlanParams, kv_lens, levels: Sequence[dict] = (), host_buf
     hb, _ = plan_buffer_sizes(params, levels)
     if host_buf is None:
         host_buf = torch.zeros(max(hb, 16), dtype=torch.uint8)
-    kl = _i32_array(list(kv_lens))
-    lv = _Levels(levels)
+    kl = _lens_arg(kv_lens)
+    lv = _levels_arg(levels)
     info = PlanInfo()
     _check(lib.pkc_plan_host(ctypes.byref(params), kl, lv.arr, lv.n, _ptr(host_buf), host_buf.numel(),
                              ctypes.byref(info)))

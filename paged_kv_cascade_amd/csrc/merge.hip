@@ -53,28 +53,35 @@ __device__ __forceinline__ void finish(float m, float l, float* acc, float* lse_
   *lse_out = l > 0.f ? (m + log2f(l)) * kLn2 : kNegInf;
 }
 
+// A workgroup finishes kMergeRequestsPerBlock consecutive requests (all their heads), so the
+// pass stays a small launch when most requests were already written by the decode kernel:
+// a flagged request costs one uniform branch.
+constexpr int kMergeRequestsPerBlock = 4;
 template <typename TO, int D>
 __global__ __launch_bounds__(256) void merge_plan_kernel(const MergePlanParams p) {
   constexpr int TPH = D / 4;          // threads per head
-  constexpr int HPB = 256 / TPH;      // heads per block
-  const int b = blockIdx.x;
-  if (p.req_flags && p.req_flags[b]) return;
-  const int h = blockIdx.y * HPB + threadIdx.x / TPH;
-  if (h >= p.hq) return;
+  constexpr int HPB = 256 / TPH;      // heads per pass of the block
   const int d0 = (threadIdx.x % TPH) * 4;
-  const int beg = p.merge_ptr[(int64_t)b * p.nl2 + p.l0];
-  const int end = p.merge_ptr[(int64_t)b * p.nl2 + p.l1];
-  float m = kNegInf, l = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int k = beg; k < end; ++k) {
-    const int64_t r = p.merge_rows[k];
-    float o4[4];
-    load4<F32>(p.st_o, (r * p.hq + h) * D + d0, o4);
-    absorb(m, l, acc, p.st_lse[r * p.hq + h], o4);
+  for (int bi = 0; bi < kMergeRequestsPerBlock; ++bi) {
+    const int b = blockIdx.x * kMergeRequestsPerBlock + bi;
+    if (b >= p.batch) break;
+    if (p.req_flags && p.req_flags[b]) continue;
+    const int beg = p.merge_ptr[(int64_t)b * p.nl2 + p.l0];
+    const int end = p.merge_ptr[(int64_t)b * p.nl2 + p.l1];
+    for (int h = threadIdx.x / TPH; h < p.hq; h += HPB) {
+      float m = kNegInf, l = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int k = beg; k < end; ++k) {
+        const int64_t r = p.merge_rows[k];
+        float o4[4];
+        load4<F32>(p.st_o, (r * p.hq + h) * D + d0, o4);
+        absorb(m, l, acc, p.st_lse[r * p.hq + h], o4);
+      }
+      float lse;
+      finish(m, l, acc, &lse);
+      store4<TO>(p.o, ((int64_t)b * p.hq + h) * D + d0, acc);
+      if (d0 == 0) p.lse[(int64_t)b * p.hq + h] = lse;
+    }
   }
-  float lse;
-  finish(m, l, acc, &lse);
-  store4<TO>(p.o, ((int64_t)b * p.hq + h) * D + d0, acc);
-  if (d0 == 0) p.lse[(int64_t)b * p.hq + h] = lse;
 }
 
 template <typename TI, typename TO, int D>
@@ -190,11 +197,10 @@ hipError_t launch_read_stream(const void* src, int64_t mib, uint32_t* sink, hipS
 template <typename TO>
 static hipError_t merge_plan_d(int head_dim, const MergePlanParams& p, hipStream_t s) {
   if (p.batch <= 0) return hipSuccess;
+  const dim3 grid((p.batch + kMergeRequestsPerBlock - 1) / kMergeRequestsPerBlock);
   if (head_dim == 64) {
-    dim3 grid(p.batch, (p.hq + 15) / 16);
     hipLaunchKernelGGL((merge_plan_kernel<TO, 64>), grid, dim3(256), 0, s, p);
   } else if (head_dim == 128) {
-    dim3 grid(p.batch, (p.hq + 7) / 8);
     hipLaunchKernelGGL((merge_plan_kernel<TO, 128>), grid, dim3(256), 0, s, p);
   } else {
     return hipErrorInvalidValue;

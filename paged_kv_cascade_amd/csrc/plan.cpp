@@ -93,26 +93,34 @@ pkc_status lpt_plan(const int32_t* qo_lens, const int32_t* kv_lens, int32_t n, i
       }
     }
   }
-  // Step 5: longest first, stable.
-  std::vector<int32_t> order(st.items.size());
+  // Step 5: longest first, stable (equal lengths keep ascending w).
+  std::vector<int32_t>& order = st.order;
+  order.resize(st.items.size());
   std::iota(order.begin(), order.end(), 0);
-  std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
-    return (st.items[a].ke - st.items[a].kb) > (st.items[b].ke - st.items[b].kb);
-  });
-  // Steps 6-7: min-cost CTA first, ties to the smaller index.
+  bool sorted = true;
+  for (size_t i = 1; i < order.size() && sorted; ++i)
+    sorted = (st.items[i - 1].ke - st.items[i - 1].kb) >= (st.items[i].ke - st.items[i].kb);
+  if (!sorted)
+    std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
+      return (st.items[a].ke - st.items[a].kb) > (st.items[b].ke - st.items[b].kb);
+    });
+  // Steps 6-7: min-cost CTA first, ties to the smaller index (a min-heap on (cost, CTA)).
   using Entry = std::pair<int64_t, int32_t>;
-  std::priority_queue<Entry, std::vector<Entry>, std::greater<Entry>> queue;
-  for (int32_t c = 0; c < ctas; ++c) queue.push({0, c});
-  st.cta.assign(ctas, {});
+  std::vector<Entry>& heap = st.heap;
+  heap.resize(ctas);
+  for (int32_t c = 0; c < ctas; ++c) heap[c] = {0, c};   // already a valid min-heap
+  if ((int32_t)st.cta.size() < ctas) st.cta.resize(ctas);
+  for (int32_t c = 0; c < ctas; ++c) st.cta[c].clear();
   st.cta_cost.assign(ctas, 0);
+  const auto later = std::greater<Entry>();
   for (int32_t w : order) {
-    Entry e = queue.top();
-    queue.pop();
+    std::pop_heap(heap.begin(), heap.end(), later);
+    Entry& e = heap.back();
     const Item& it = st.items[w];
     st.cta[e.second].push_back(w);
     e.first += alpha * it.nq + beta * (int64_t)(it.ke - it.kb);
     st.cta_cost[e.second] = e.first;
-    queue.push(e);
+    std::push_heap(heap.begin(), heap.end(), later);
   }
   return PKC_OK;
 }
@@ -222,6 +230,22 @@ pkc_status compute_layout(const Resolved& r, const pkc_level_host* levels, int32
   return PKC_OK;
 }
 
+namespace {
+// Working storage of build_plan_host, kept per thread so that a plan built every step reuses
+// its vectors' capacity instead of allocating them again.
+struct PlanScratch {
+  std::vector<Stage> lv;
+  Stage dec;
+  std::vector<int32_t> flags, qo, chunks_of, chunks;
+  std::vector<char> wt_group;
+  std::vector<std::vector<int32_t>> per_req_lvl;
+};
+PlanScratch& plan_scratch() {
+  static thread_local PlanScratch s;
+  return s;
+}
+}  // namespace
+
 pkc_status build_plan_host(const Resolved& r, const int32_t* kv_lens_h,
                            const pkc_level_host* levels, int32_t num_levels, void* host_buf,
                            size_t host_bytes, pkc_plan_info* out) {
@@ -255,12 +279,16 @@ pkc_status build_plan_host(const Resolved& r, const int32_t* kv_lens_h,
 
   // Levels: every item gets a state block of T_q rows (rows numbered level by level), except
   // write-through level items, which write their rows' final output.
-  std::vector<Stage> lv(num_levels);
-  std::vector<int32_t> flags(B, 0);   // 1: the request's output is written by one item
+  PlanScratch& X = plan_scratch();
+  if ((int32_t)X.lv.size() < num_levels) X.lv.resize(num_levels);
+  std::vector<Stage>& lv = X.lv;
+  std::vector<int32_t>& flags = X.flags;   // 1: the request's output is written by one item
+  flags.assign(B, 0);
   int32_t row = 0;
   for (int32_t l = 0; l < num_levels; ++l) {
     const pkc_level_host& h = levels[l];
-    std::vector<int32_t> qo(h.num_groups);
+    std::vector<int32_t>& qo = X.qo;
+    qo.resize(h.num_groups);
     for (int32_t g = 0; g < h.num_groups; ++g) qo[g] = h.qo_indptr[g + 1] - h.qo_indptr[g];
     if ((s = lpt_plan(qo.data(), h.kv_lens, h.num_groups, p.level_tile_q, p.level_ctas, p.alpha,
                       p.beta, r.p.chunk_align, p.enable_split != 0, &lv[l], h.causal != 0)) != PKC_OK)
@@ -273,7 +301,8 @@ pkc_status build_plan_host(const Resolved& r, const int32_t* kv_lens_h,
     P.lvl_row_base[l] = row;
     // Write-through candidates: groups none of whose requests has own KV, when this is the
     // plan's only level; among their items, those whose tile has a single chunk.
-    std::vector<char> wt_group(h.num_groups, 0);
+    std::vector<char>& wt_group = X.wt_group;
+    wt_group.assign(h.num_groups, 0);
     if (p.level_write_through && num_levels == 1) {
       for (int32_t g = 0; g < h.num_groups; ++g) {
         bool own = false;
@@ -282,7 +311,8 @@ pkc_status build_plan_host(const Resolved& r, const int32_t* kv_lens_h,
       }
     }
     // Chunks per tile: the items of one tile are consecutive in w order.
-    std::vector<int32_t> chunks_of(lv[l].items.size(), 0);
+    std::vector<int32_t>& chunks_of = X.chunks_of;
+    chunks_of.assign(lv[l].items.size(), 0);
     for (size_t i = 0; i < lv[l].items.size();) {
       size_t j = i;
       while (j < lv[l].items.size() && lv[l].items[j].req == lv[l].items[i].req &&
@@ -305,11 +335,12 @@ pkc_status build_plan_host(const Resolved& r, const int32_t* kv_lens_h,
     }
   }
   // Decode stage over every request's own KV (one query per request, T_q = 1).
-  Stage dec;
+  Stage& dec = X.dec;
   if ((s = lpt_plan(nullptr, kv_lens_h, B, 1, p.num_ctas, p.alpha, p.beta, r.p.chunk_align,
                     p.enable_split != 0, &dec)) != PKC_OK)
     return s;
-  std::vector<int32_t> chunks(B, 0);
+  std::vector<int32_t>& chunks = X.chunks;
+  chunks.assign(B, 0);
   for (const Item& it : dec.items) chunks[it.req]++;
   P.dec_row_base = row;
   int32_t slots = 0;
@@ -356,7 +387,10 @@ pkc_status build_plan_host(const Resolved& r, const int32_t* kv_lens_h,
   int32_t* mptr = reinterpret_cast<int32_t*>(base + L.off_merge_ptr);
   int32_t* mrows = reinterpret_cast<int32_t*>(base + L.off_merge_rows);
   // Items listed by w are already (group, tile, chunk) ordered; bucket them per request.
-  std::vector<std::vector<int32_t>> per_req_lvl((size_t)B * (num_levels + 1));
+  std::vector<std::vector<int32_t>>& per_req_lvl = X.per_req_lvl;
+  const size_t nlists = (size_t)B * (num_levels + 1);
+  if (per_req_lvl.size() < nlists) per_req_lvl.resize(nlists);
+  for (size_t i = 0; i < nlists; ++i) per_req_lvl[i].clear();
   for (int32_t l = 0; l < num_levels; ++l)
     for (const Item& it : lv[l].items)
       if (it.row >= 0)

@@ -26,6 +26,8 @@ struct Item {
 };
 static_assert(sizeof(Item) == 32, "item record is 8 int32");
 
+// A stage's plan.  Stage objects are reused from one plan to the next (a serving loop plans
+// every step), so their vectors keep their capacity: only cta[0 .. ctas) is meaningful.
 struct Stage {
   int32_t ctas = 0;
   int32_t tile_q = 1;
@@ -33,6 +35,8 @@ struct Stage {
   std::vector<Item> items;                  // by w
   std::vector<std::vector<int32_t>> cta;    // per CTA: w in assignment order
   std::vector<int64_t> cta_cost;
+  std::vector<int32_t> order;               // scratch: items sorted longest first
+  std::vector<std::pair<int64_t, int32_t>> heap;   // scratch: the (cost, CTA) queue
 };
 
 // Steps 1-7 of the scheduler for one stage. qo_lens may be nullptr (all 1).  causal: a query

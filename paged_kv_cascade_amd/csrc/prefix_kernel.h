@@ -421,32 +421,72 @@ __global__ __launch_bounds__(64 * prefix_detail::kWavesPerStream * NS, NS == 1 ?
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) cbase[nt] = lim0 + (wq * kRowsPerWave + nt * 16 + l16) / G - 4 * lg;
     }
-    auto compute = [&](const char* ks_s, const char* vs_s, uint32_t mask, int tok0) __attribute__((always_inline)) {
-      if (!wave_active) return;
-      // S^T[mt][nt]: tokens mt*16 + 4*lg + i, query column nt*16 + l16.
-      f4_t s[2][2];
+    // Software pipeline inside each wave (kPipe): the step of tile j runs the S^T products of
+    // tile j while the vector ALU finishes the softmax of tile j-1, then tile j-1's PV
+    // products, then reads tile j's V^T operands into registers.  Every LDS read of a tile
+    // still happens in the tile's own step, so the ring protocol is unchanged; the operands,
+    // scores and weights of one tile are exactly those of the unpipelined order.  A dummy
+    // previous tile (scores -inf, V^T operands zero) starts the pipeline: its weights are 0
+    // and it adds nothing.  The pipeline keeps a second score tile and the V^T operands live
+    // across the step (about 250 VGPRs at D = 128); with grouped heads the extra row indexing
+    // no longer fits 256, nor does the FP8 conversion, so those instantiations run a tile's
+    // pieces in order in its step (FP8: with the V^T reads after the softmax, which needs
+    // fewer live registers).
+    constexpr bool kPipe = !F8 && (D == 64 || G == 1);
+    f4_t sp[2][2];   // scores of the previous tile, waiting for their softmax
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) sp[mt][nt] = f4_t{kNegInf, kNegInf, kNegInf, kNegInf};
+    uint32_t mask_p = ~0u;   // valid-token bits and first token of the previous tile
+    int tok0_p = 0;
+    V16 va[DM];      // V^T operands of the previous tile
+#pragma unroll
+    for (int dm = 0; dm < DM; ++dm) va[dm] = zero16();
+
+    // S^T[mt][nt] of a tile: tokens mt*16 + 4*lg + i, query column nt*16 + l16.  The K
+    // operands of each 16-token half are read together, then used by that half's products.
+    auto score = [&](const char* ks_s, f4_t (&s)[2][2]) __attribute__((always_inline)) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
+        const int r = mt * 16 + l16;
+        V16 ka[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) ka[ks] = lds_load16(ks_s + r * RB + (((ks * 4 + lg) ^ swz<D>(r)) * 16));
         s[mt][0] = f4_t{0.f, 0.f, 0.f, 0.f};
         s[mt][1] = f4_t{0.f, 0.f, 0.f, 0.f};
-        const int r = mt * 16 + l16;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const int c = (ks * 4 + lg) ^ swz<D>(r);
-          const V16 a = lds_load16(ks_s + r * RB + c * 16);
-          s[mt][0] = Mfma<T>::run(a, qb[0][ks], s[mt][0]);
-          s[mt][1] = Mfma<T>::run(a, qb[1][ks], s[mt][1]);
+          s[mt][0] = Mfma<T>::run(ka[ks], qb[0][ks], s[mt][0]);
+          s[mt][1] = Mfma<T>::run(ka[ks], qb[1][ks], s[mt][1]);
         }
       }
+    };
+    // V^T operands of a tile (see the PV products below).
+    auto vread = [&](const char* vs_s) __attribute__((always_inline)) {
+#pragma unroll
+      for (int dm = 0; dm < DM; ++dm)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int r = 16 * h + 4 * lg + tr_row;
+          const int c = (2 * dm + (tr_piece >> 1)) ^ swz<D>(r);
+          const uint2 x = lds_read_tr(vs_s + r * RB + c * 16 + (tr_piece & 1) * 8);
+          va[dm].w[2 * h] = x.x;
+          va[dm].w[2 * h + 1] = x.y;
+        }
+    };
+    // Softmax of the previous tile, first part: masks, each lane's share of the column
+    // maxima, and the rare raise of the reference maximum (a wave-uniform branch).
+    auto softmax_prepare = [&]() __attribute__((always_inline)) {
       // Tiles whose 32 tokens are all valid (every tile but the ragged ends) skip masking.
-      if (mask != ~0u) {
+      if (mask_p != ~0u) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const bool v = (mask >> (mt * 16 + 4 * lg + i)) & 1u;
-            s[mt][0][i] = v ? s[mt][0][i] : kNegInf;
-            s[mt][1][i] = v ? s[mt][1][i] : kNegInf;
+            const bool v = (mask_p >> (mt * 16 + 4 * lg + i)) & 1u;
+            sp[mt][0][i] = v ? sp[mt][0][i] : kNegInf;
+            sp[mt][1][i] = v ? sp[mt][1][i] : kNegInf;
           }
       }
       // Causal mask, per query column.
@@ -457,11 +497,11 @@ __global__ __launch_bounds__(64 * prefix_detail::kWavesPerStream * NS, NS == 1 ?
           for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-              s[mt][nt][i] = tok0 + mt * 16 + i > cbase[nt] ? kNegInf : s[mt][nt][i];
+              sp[mt][nt][i] = tok0_p + mt * 16 + i > cbase[nt] ? kNegInf : sp[mt][nt][i];
         // Tree mask on the tiles that reach the new tokens: a new token is visible to a query
         // where its mask byte is set (the causal limit above still applies).  Bytes of tokens
         // before the new ones are not read (an out-of-range offset reads zero).
-        if (p.tree_mask != nullptr && tok0 + kTK > tbase) {
+        if (p.tree_mask != nullptr && tok0_p + kTK > tbase) {
           const rsrc_t mr = make_rsrc(p.tree_mask, p.mask_bytes);
 #pragma unroll
           for (int nt = 0; nt < 2; ++nt) {
@@ -471,27 +511,21 @@ __global__ __launch_bounds__(64 * prefix_detail::kWavesPerStream * NS, NS == 1 ?
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
-                const int t = tok0 + mt * 16 + 4 * lg + i;
+                const int t = tok0_p + mt * 16 + 4 * lg + i;
                 const int32_t off = t >= tbase ? rowoff + t : kOffsetNone;
                 const uint32_t vis = __builtin_amdgcn_raw_buffer_load_b8(mr, off, 0, 0);
-                s[mt][nt][i] = (t < tbase || vis != 0) ? s[mt][nt][i] : kNegInf;
+                sp[mt][nt][i] = (t < tbase || vis != 0) ? sp[mt][nt][i] : kNegInf;
               }
           }
         }
       }
-      V16 pb[2];   // P^T operands per query tile nt (the tile's 32 tokens are one step)
-      // bf16 weights go to the matrix cores as two bf16 terms (rounded weight and residual):
-      // a single bf16 weight carries a relative error up to 2^-9, which over a few tokens with
-      // values of opposite sign exceeds the output tolerance.  fp16 weights (2^-12) need not.
-      constexpr bool kSplitP = std::is_same<T, BF16>::value;
-      V16 pl[2];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         float pmx = kNegInf;   // this lane's share of the column maximum (raw scores)
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) pmx = fmaxf(pmx, s[mt][nt][i]);
+          for (int i = 0; i < 4; ++i) pmx = fmaxf(pmx, sp[mt][nt][i]);
         // Lazy reference maximum: m_run moves only when a score exceeds it by more than
         // kSlack (log2 units), so O and l are rescaled only on such tiles (in practice the
         // first ones).  Weights stay below 2^kSlack, which fp32 and the 16-bit operand types
@@ -511,11 +545,23 @@ __global__ __launch_bounds__(64 * prefix_detail::kWavesPerStream * NS, NS == 1 ?
 #pragma unroll
           for (int dm = 0; dm < DM; ++dm) oacc[dm][nt] *= alpha;
         }
+      }
+    };
+    V16 pb[2];   // P^T operands per query tile nt (the tile's 32 tokens are one step)
+    // bf16 weights go to the matrix cores as two bf16 terms (rounded weight and residual): a
+    // single bf16 weight carries a relative error up to 2^-9, which over a few tokens with
+    // values of opposite sign exceeds the output tolerance.  fp16 weights (2^-12) need not.
+    constexpr bool kSplitP = std::is_same<T, BF16>::value;
+    V16 pl[2];
+    // Second part: the weights of the previous tile, their sums, and the operand packing.
+    auto softmax_finish = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
         float pr[2][4];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) pr[mt][i] = fast_exp2(fmaf(s[mt][nt][i], p.scale_log2, nmu[nt]));
+          for (int i = 0; i < 4; ++i) pr[mt][i] = fast_exp2(fmaf(sp[mt][nt][i], p.scale_log2, nmu[nt]));
         // P enters the PV product rounded to the operand type, but the denominator (and so the
         // LSE) sums the fp32 weights: with bf16, summing rounded weights would move LSE by up
         // to 2^-9.
@@ -538,27 +584,48 @@ __global__ __launch_bounds__(64 * prefix_detail::kWavesPerStream * NS, NS == 1 ?
           }
         }
       }
+    };
+    // PV products of the previous tile.
+    auto pv_products = [&]() __attribute__((always_inline)) {
       // O^T[dm][nt] += V^T * P^T over the tile's 32 tokens.  Lane group g supplies contraction
       // elements 8g .. 8g+7 = tokens 16h + 4g + i (h = 0, 1; i = 0..3), the order of the S^T
       // accumulators; each half is one transpose read of rows 16h + 4g + tr_row, elements
       // dm*16 + 4*tr_piece .. +4 (logical chunk 2*dm + tr_piece/2, swizzled by row).
 #pragma unroll
       for (int dm = 0; dm < DM; ++dm) {
-        V16 a;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int r = 16 * h + 4 * lg + tr_row;
-          const int c = (2 * dm + (tr_piece >> 1)) ^ swz<D>(r);
-          const uint2 x = lds_read_tr(vs_s + r * RB + c * 16 + (tr_piece & 1) * 8);
-          a.w[2 * h] = x.x;
-          a.w[2 * h + 1] = x.y;
-        }
+        const V16& a = va[dm];
         oacc[dm][0] = Mfma<T>::run(a, pb[0], oacc[dm][0]);
         oacc[dm][1] = Mfma<T>::run(a, pb[1], oacc[dm][1]);
         if constexpr (kSplitP) {
           oacc[dm][0] = Mfma<T>::run(a, pl[0], oacc[dm][0]);
           oacc[dm][1] = Mfma<T>::run(a, pl[1], oacc[dm][1]);
         }
+      }
+    };
+    auto compute = [&](const char* ks_s, const char* vs_s, uint32_t mask, int tok0) __attribute__((always_inline)) {
+      if (!wave_active) return;
+      if constexpr (kPipe) {
+        softmax_prepare();
+        f4_t s[2][2];
+        score(ks_s, s);
+        softmax_finish();
+        pv_products();
+        vread(vs_s);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) sp[mt][nt] = s[mt][nt];
+        mask_p = mask;
+        tok0_p = tok0;
+      } else {
+        score(ks_s, sp);
+        mask_p = mask;
+        tok0_p = tok0;
+        if constexpr (!F8) vread(vs_s);   // read now: the softmax below hides their latency
+        softmax_prepare();
+        softmax_finish();
+        if constexpr (F8) vread(vs_s);
+        pv_products();
       }
     };
 
@@ -598,14 +665,14 @@ __global__ __launch_bounds__(64 * prefix_detail::kWavesPerStream * NS, NS == 1 ?
       // Step j in stage S = j % STAGES (16-bit pools): wait for this wave's loads of the
       // stream's j-th tile (its next two tiles stay in flight), barrier (every wave's loads and
       // valid-row byte of the step's tiles have landed and every wave is done with step j-1),
-      // refill stage S-1 with the stream's tile j+3, request the page entries of its tile j+4,
-      // compute tile j.  No
-      // LDS wait is needed before the barrier: a wave's LDS operations complete in order, and
-      // the compiler waits for the last operand read of a tile before its final products, so
-      // by the end of a step the wave's valid-row byte is written and its reads of the stage
-      // are done.  Every stream runs the same number of steps (and barriers).  Stage numbers
-      // are compile-time constants (STAGES steps per loop trip), so ring addresses are immediate
-      // offsets.
+      // refill stage S-1 with the stream's tile j+3, compute tile j (its S^T products and
+      // V^T reads, and tile j-1's softmax and PV products), request the page entries of tile
+      // j+4 (after the step's LDS reads: scalar loads and LDS reads share one counter, so an
+      // LDS wait also waits for any scalar load in flight).  Before the barrier the wave waits
+      // for its own LDS operations (the V^T reads at the end of the previous step), so no wave
+      // still reads the stage the refill overwrites.  Every stream runs the same number of
+      // steps (and barriers).  Stage numbers are compile-time constants (STAGES steps per loop
+      // trip), so ring addresses are immediate offsets.
       //
       // F8: the wait leaves AHEAD - 1 tiles in flight; between the wait and the barrier the
       // wave converts the code rows it loaded into the 16-bit copy of parity j % 2 (that copy
@@ -638,19 +705,27 @@ __global__ __launch_bounds__(64 * prefix_detail::kWavesPerStream * NS, NS == 1 ?
             }
           }
           PKC_WAIT_LGKMCNT0();
+        } else {
+          PKC_WAIT_LGKMCNT0();
         }
         ring_barrier();
-        if constexpr (!F8) mask = sfl[S];   // the same on every lane; first needed after S^T
+        if constexpr (!F8) mask = sfl[S];   // the same on every lane; used in the next step
         issue(tt + AHEAD * NS, pg, lds_addr(sring) + N * SLOT, sfl + N);
-        pg = fetch(tt + (AHEAD + 1) * NS);
         if (tt < ntiles) {
           const int tok0 = t0 + tt * kTK;   // the tile's first token (causal mask)
           if constexpr (F8) compute(cb, cb + STB, mask, tok0);
           else compute(sring + S * SLOT, sring + S * SLOT + STB, mask, tok0);
         }
+        pg = fetch(tt + (AHEAD + 1) * NS);
       };
       for (int j = 0; j < nsteps; j += STAGES)
         if (!unrolled_steps<0, STAGES>(step, j, nsteps)) break;
+      // Drain the pipeline: the softmax and PV products of the stream's last tile.
+      if (kPipe && wave_active) {
+        softmax_prepare();
+        softmax_finish();
+        pv_products();
+      }
     }
 
     // Every load of the ring (including the empty ones past the last tile, which still write
@@ -700,39 +775,59 @@ __global__ __launch_bounds__(64 * prefix_detail::kWavesPerStream * NS, NS == 1 ?
       }
     }
 
-    // Finish (stream 0): total sum over the 4 lane groups, normalise, write the fp32 state.
+    // Finish (stream 0): total sum over the 4 lane groups, normalise, write the state.
     if (stream == 0 && wave_active) {
+      // The fp32 state of a row is D contiguous floats, but a lane holds 4-float pieces of it
+      // (the accumulator layout), so a direct store instruction would write 16 rows x 64 bytes.
+      // Instead each wave stages 16 rows at a time in its own part of the idle ring (past the
+      // stream hand-off values; rows padded by 16 bytes so they start on different banks) and
+      // stores whole rows: every instruction writes 64 / (D / 4) rows of D * 4 bytes.
+      constexpr int SRS = D * 4 + 16;
+      constexpr int HAND = NS == 2 ? (DM * 2 * 4 + 4) * 256 * 4 : 0;
+      static_assert(HAND + kWavesPerStream * 16 * SRS <= RING + CBUF, "state staging fits the ring");
+      char* const stage = smem + HAND + wq * 16 * SRS;
+      constexpr int LPR = D / 4;      // lanes per staged row (16 bytes each)
+      constexpr int RPI = 64 / LPR;   // rows per store instruction
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         const float lt = lane_groups_sum(l_run[nt]);
         const int r = wq * kRowsPerWave + nt * 16 + l16;
-        if (r < nrows) {
-          float inv = lt > 0.f ? 1.f / lt : 0.f;
-          if constexpr (F8) inv *= p.v_scale;
-          const int h = hk * G + r % G;
-          const float lse_r = lt > 0.f ? (m_run[nt] + log2f(lt)) * kLn2 : kNegInf;
-          if (srow >= 0) {
-            const int64_t srow_q = (int64_t)srow + r / G;
-            float* dst = p.st_o + (srow_q * p.hq + h) * D;
+        float inv = lt > 0.f ? 1.f / lt : 0.f;
+        if constexpr (F8) inv *= p.v_scale;
+        const int h = hk * G + r % G;
+        const float lse_r = lt > 0.f ? (m_run[nt] + log2f(lt)) * kLn2 : kNegInf;
+        if (srow >= 0) {
 #pragma unroll
-            for (int dm = 0; dm < DM; ++dm) {
-              const f4_t o = oacc[dm][nt] * inv;
-              *reinterpret_cast<float4*>(dst + dm * 16 + 4 * lg) = make_float4(o[0], o[1], o[2], o[3]);
-            }
-            if (lg == 0) p.st_lse[srow_q * p.hq + h] = lse_r;
-          } else if (p.o) {
-            // Write-through: the tile is its rows' only item, so this is their final output
-            // (O rounded once to the operand type).
-            const int64_t orow = (int64_t)q0 + r / G;
-            char* dst = static_cast<char*>(p.o) + (orow * p.hq + h) * (D * ES);
-#pragma unroll
-            for (int dm = 0; dm < DM; ++dm) {
-              const f4_t o = oacc[dm][nt] * inv;
-              *reinterpret_cast<uint2*>(dst + (dm * 16 + 4 * lg) * ES) =
-                  make_uint2(Mfma<T>::pack(o[0], o[1]), Mfma<T>::pack(o[2], o[3]));
-            }
-            if (lg == 0) p.lse[orow * p.hq + h] = lse_r;
+          for (int dm = 0; dm < DM; ++dm) {
+            const f4_t o = oacc[dm][nt] * inv;
+            *reinterpret_cast<float4*>(stage + l16 * SRS + (dm * 16 + 4 * lg) * 4) = make_float4(o[0], o[1], o[2], o[3]);
           }
+          if (lg == 0 && r < nrows) p.st_lse[((int64_t)srow + r / G) * p.hq + h] = lse_r;
+#pragma unroll
+          for (int k = 0; k < 16 / RPI; ++k) {
+            const int rr = k * RPI + lane / LPR;
+            const int row = wq * kRowsPerWave + nt * 16 + rr;
+            const float4 x = *reinterpret_cast<const float4*>(stage + rr * SRS + (lane % LPR) * 16);
+            if (row < nrows) {
+              const int64_t q = (int64_t)srow + row / G;
+              *reinterpret_cast<float4*>(p.st_o + (q * p.hq + hk * G + row % G) * D + (lane % LPR) * 4) = x;
+            }
+          }
+          // The next half's staging writes stay behind this half's reads (one wave's LDS
+          // operations complete in order; this keeps the compiler from reordering them).
+          __asm__ volatile("" ::: "memory");
+        } else if (p.o && r < nrows) {
+          // Write-through: the tile is its rows' only item, so this is their final output
+          // (O rounded once to the operand type).
+          const int64_t orow = (int64_t)q0 + r / G;
+          char* dst = static_cast<char*>(p.o) + (orow * p.hq + h) * (D * ES);
+#pragma unroll
+          for (int dm = 0; dm < DM; ++dm) {
+            const f4_t o = oacc[dm][nt] * inv;
+            *reinterpret_cast<uint2*>(dst + (dm * 16 + 4 * lg) * ES) =
+                make_uint2(Mfma<T>::pack(o[0], o[1]), Mfma<T>::pack(o[2], o[3]));
+          }
+          if (lg == 0) p.lse[orow * p.hq + h] = lse_r;
         }
       }
     }
