@@ -130,6 +130,15 @@ typedef struct pkc_plan_params {
                            most the compute-unit count (one 8-wave workgroup per compute unit,
                            two 4-wave streams over alternate KV tiles, merged at the end), else
                            1 (4-wave workgroups); 1 or 2 fix it */
+  int32_t contraction;  /* where the partial states of split requests are merged (the
+                           contraction of the FlashInfer paper summary, section A3):
+                           1 -> inside the decode kernel (attention and contraction in one
+                           launch: the workgroup whose partial state of a request arrives last
+                           merges that request's states; requests with no decode item are
+                           merged by the decode workgroups too), so a decode or cascade run
+                           launches no merge pass; 2 -> a separate merge pass after the decode
+                           kernel; 0 -> 1 when num_ctas <= batch (few split requests), else 2.
+                           Both give the same bits. */
 } pkc_plan_params;
 
 /* Host description of one cascade level: groups of consecutive requests sharing a KV run.
@@ -180,7 +189,8 @@ typedef struct pkc_plan_info {
   int32_t dec_row_base;    /* first state row of the decode stage */
   int32_t state_rows;      /* rows of the fp32 partial-state buffer */
   int32_t merge_entries;   /* length of the merge row list */
-  int32_t num_merge;       /* requests whose output the merge kernel writes */
+  int32_t num_merge;       /* requests merged from several states (by the decode kernel or the
+                              merge pass, per dec_contraction) */
   int64_t off_dec_indptr;  /* byte offsets inside the host buffer / device workspace */
   int64_t off_dec_items;
   int64_t off_lvl_indptr[PKC_MAX_LEVELS];
@@ -197,6 +207,11 @@ typedef struct pkc_plan_info {
   int32_t lvl_causal[PKC_MAX_LEVELS]; /* 1: the level was planned with causal tile extents */
   int32_t lvl_write_through;  /* level items that write the final output (level_write_through) */
   int32_t lvl_streams;     /* tile streams per level workgroup (1 or 2), from the parameters */
+  int32_t dec_contraction; /* 1: the decode kernel merges split requests (no merge pass);
+                              2: a merge pass follows it; from the parameters */
+  int64_t off_counters;    /* uint32 [B, Hkv] arrival counters of the in-kernel contraction:
+                              zero in every plan's integer arrays, and every run leaves them
+                              zero */
 } pkc_plan_info;
 
 /*

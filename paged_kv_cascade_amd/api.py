@@ -43,7 +43,8 @@ class PlanParams(ctypes.Structure):
                 ("level_ctas", ctypes.c_int32), ("level_tile_q", ctypes.c_int32),
                 ("chunk_align", ctypes.c_int32), ("enable_split", ctypes.c_int32),
                 ("alpha", ctypes.c_int64), ("beta", ctypes.c_int64), ("decode_waves", ctypes.c_int32),
-                ("level_write_through", ctypes.c_int32), ("level_streams", ctypes.c_int32)]
+                ("level_write_through", ctypes.c_int32), ("level_streams", ctypes.c_int32),
+                ("contraction", ctypes.c_int32)]
 
 
 class LevelHost(ctypes.Structure):
@@ -79,7 +80,8 @@ class PlanInfo(ctypes.Structure):
                 ("int_bytes", ctypes.c_int64),
                 ("off_state_o", ctypes.c_int64), ("off_state_lse", ctypes.c_int64),
                 ("dev_bytes", ctypes.c_int64), ("dev_ws", ctypes.c_uint64), ("lvl_causal", _L8),
-                ("lvl_write_through", ctypes.c_int32), ("lvl_streams", ctypes.c_int32)]
+                ("lvl_write_through", ctypes.c_int32), ("lvl_streams", ctypes.c_int32),
+                ("dec_contraction", ctypes.c_int32), ("off_counters", ctypes.c_int64)]
 
 
 _P = ctypes.c_void_p
@@ -209,10 +211,11 @@ def device_info(device: int = 0):
 
 def make_params(batch, num_qo_heads, num_kv_heads, head_dim, page_size, num_ctas=0, level_ctas=0,
                 level_tile_q=0, chunk_align=1, enable_split=True, alpha=1, beta=1,
-                decode_waves=0, level_write_through=False, level_streams=0) -> PlanParams:
+                decode_waves=0, level_write_through=False, level_streams=0,
+                contraction=0) -> PlanParams:
     return PlanParams(batch, num_qo_heads, num_kv_heads, head_dim, page_size, num_ctas, level_ctas,
                       level_tile_q, chunk_align, 1 if enable_split else 0, alpha, beta, decode_waves,
-                      1 if level_write_through else 0, level_streams)
+                      1 if level_write_through else 0, level_streams, contraction)
 
 
 class HostLevels:

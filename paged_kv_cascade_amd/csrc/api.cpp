@@ -153,6 +153,17 @@ pkc::DecodeParams decode_params(const void* q, const void* k, const void* v, int
   return p;
 }
 
+// In-kernel contraction of a decode or cascade run: the merge lists, the write-through flags
+// and the arrival counters of the plan.
+void set_contraction(pkc::DecodeParams* p, const pkc_plan_info* plan, void* ws, int32_t num_levels) {
+  p->merge_ptr = at<int32_t>(ws, plan->off_merge_ptr);
+  p->merge_rows = at<int32_t>(ws, plan->off_merge_rows);
+  p->nl2 = num_levels + 2;
+  p->counters = at<uint32_t>(ws, plan->off_counters);
+  p->req_flags = at<int32_t>(ws, plan->off_req_flags);
+  p->batch = plan->batch;
+}
+
 pkc::MergePlanParams merge_params(const pkc_plan_info* plan, void* ws, int l0, int l1, bool skip_wt,
                                   void* o, float* lse) {
   pkc::MergePlanParams m{};
@@ -448,6 +459,7 @@ pkc_status pkc::decode_run(bool fp8, float k_scale, float v_scale, const pkc_pla
     p.st_lse = at<float>(dev_ws, plan->off_state_lse);
     p.indptr = at<int32_t>(dev_ws, plan->off_dec_indptr);
     p.items = at<int32_t>(dev_ws, plan->off_dec_items);
+    if (plan->dec_contraction == 1) set_contraction(&p, plan, dev_ws, 0);
     grid_x = plan->num_ctas;
     if (plan_upload_src) {
       // Every check has passed: copy the plan's integer arrays from the host buffer into the
@@ -465,7 +477,7 @@ pkc_status pkc::decode_run(bool fp8, float k_scale, float v_scale, const pkc_pla
                     : pkc::launch_decode(dtype, head_dim, g, waves, p, grid_x, s);
        })) != PKC_OK)
     return st;
-  if (plan) {
+  if (plan && plan->dec_contraction != 1) {
     // Always enqueued (it skips the requests flagged as written through), so the launches of a
     // run do not depend on the plan's lengths.
     pkc::MergePlanParams m = merge_params(plan, dev_ws, 0, 1, true, o, lse);
@@ -771,12 +783,14 @@ static pkc_status cascade_impl(bool fp8, float k_scale, float v_scale, const pkc
       p.fold_lse_bytes = (int32_t)lse_bytes;
     }
   }
+  if (plan->dec_contraction == 1) set_contraction(&p, plan, dev_ws, num_levels);
   const int g = num_qo_heads / num_kv_heads;
   if ((st = timed(0, s, "decode kernel launch", [&] {
          return fp8 ? pkc::launch_decode_fp8(dtype, head_dim, g, plan->dec_waves, p, plan->num_ctas, s)
                     : pkc::launch_decode(dtype, head_dim, g, plan->dec_waves, p, plan->num_ctas, s);
        })) != PKC_OK)
     return st;
+  if (plan->dec_contraction == 1) return PKC_OK;   // the decode kernel merged every request
   // Always enqueued (it skips the requests finished by the decode kernel): the launches of a run
   // do not depend on the plan's lengths, so a captured run stays valid across re-plans.
   pkc::MergePlanParams m = merge_params(plan, dev_ws, 0, num_levels + 1, true, o, lse);

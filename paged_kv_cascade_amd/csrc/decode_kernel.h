@@ -28,6 +28,17 @@
 // level states.  A tile's chunks hold consecutive slots, so the request's rows at a level are
 // first + c * T_q: each lane prefetches its share into registers at item start (a fixed number
 // of buffer loads, empty ones outside the range) and writes it to LDS after its steps.
+//
+// Attention and contraction in one launch (FlashInfer paper summary, section A3: the partial
+// outputs of split KV are contracted by the same persistent kernel, whose grid is fixed by the
+// parameters).  Each workgroup that writes a partial state of a split request writes it with
+// device-scope atomic stores (coherent across the XCDs' L2 caches without flushing them), waits
+// for them to complete and then bumps the request's arrival counter (a device-scope atomic);
+// the one that brings it to the request's number of partial states reads the request's states
+// with device-scope atomic loads, merges its whole merge list (levels, then its own chunks)
+// into the final output with the merge pass's arithmetic, and sets the counter back to zero.
+// Nothing waits for another workgroup, so any number of workgroups may be resident.  Requests with no decode item and no write-through (empty KV; a cascade request
+// with no own KV) are merged at the start of workgroup (b mod #CTA, kv head).
 #pragma once
 
 #include <cstdlib>
@@ -35,6 +46,7 @@
 
 #include "device_common.h"
 #include "kernels.h"
+#include "merge_ops.h"
 
 namespace pkc {
 
@@ -69,6 +81,7 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(const DecodeParams p) {
   constexpr int FCAP = FL * 64 * NW;   // chunk capacity
   __shared__ f4_t sm_fold[FOLD ? FCAP : 1];
   __shared__ float sm_fold_lse[FOLD ? 64 * NW : 1];
+  __shared__ int sm_last;
 
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -86,6 +99,23 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(const DecodeParams p) {
   const int32_t head_off32 = (int32_t)head_off;
   const int32_t slot_stride32 = (int32_t)slot_stride;
   const int32_t page_bytes = P * slot_stride32;
+
+  // Merge of request b's list rows [beg, end) for this workgroup's G heads into its output.
+  using TO = typename OutType<T>::type;
+  auto contract = [&](auto coherent, int b, int beg, int end) {
+    for (int idx = threadIdx.x; idx < G * D / 4; idx += 64 * NW)
+      merge_rows_to_output<TO, D, decltype(coherent)::value>(p.st_o, p.st_lse, p.merge_rows, beg, end, p.hq, b,
+                                                              hq0 + idx / (D / 4), (idx % (D / 4)) * 4, p.o,
+                                                              p.lse);
+  };
+  const int nlv = p.nl2 - 2;
+  if (p.counters) {
+    for (int b = blockIdx.x; b < p.batch; b += gridDim.x) {
+      const int32_t* mp = p.merge_ptr + (int64_t)b * p.nl2;
+      if (scalar_load(p.req_flags + b) == 0 && scalar_load(mp + nlv) == scalar_load(mp + nlv + 1))
+        contract(std::false_type(), b, scalar_load(mp), scalar_load(mp + nlv + 1));
+    }
+  }
 
   int it_begin = 0, it_end = 1;
   if (p.indptr) {
@@ -405,10 +435,30 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(const DecodeParams p) {
       if (srow < 0) {
         Elem<typename OutType<T>::type>::store(p.o, ((int64_t)b * p.hq + h) * D + d, o);
         if (d == 0) p.lse[(int64_t)b * p.hq + h] = lse;
+      } else if (p.counters) {
+        // Read by the request's last workgroup while this kernel runs: coherent stores.
+        __hip_atomic_store(p.st_o + ((int64_t)srow * p.hq + h) * D + d, o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (d == 0) __hip_atomic_store(p.st_lse + (int64_t)srow * p.hq + h, lse, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       } else {
         p.st_o[((int64_t)srow * p.hq + h) * D + d] = o;
         if (d == 0) p.st_lse[(int64_t)srow * p.hq + h] = lse;
       }
+    }
+    if (p.counters && srow >= 0) {
+      // This workgroup's partial state is complete at device scope once its stores have
+      // completed; then count it in.  The last arrival merges.
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      const int32_t* mp = p.merge_ptr + (int64_t)b * p.nl2;
+      if (threadIdx.x == 0) {
+        const uint32_t expect = (uint32_t)(scalar_load(mp + nlv + 1) - scalar_load(mp + nlv));
+        uint32_t* ctr = p.counters + (int64_t)b * p.hkv + hk;
+        const bool last = atomicAdd(ctr, 1u) + 1u == expect;
+        if (last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sm_last = last ? 1 : 0;
+      }
+      __syncthreads();
+      if (sm_last) contract(std::true_type(), b, scalar_load(mp), scalar_load(mp + nlv + 1));
     }
     // Drain this item's stores before the next item's loads: with stores and loads both in
     // flight the compiler can no longer count loads in order and waits for all of them.
@@ -422,10 +472,10 @@ inline hipError_t launch_decode_t(const DecodeParams& p, int grid_x, hipStream_t
   dim3 grid(grid_x, p.hkv), block(64 * NW);
   if constexpr (std::is_same<T, F32>::value) {
     // Cascades need the matrix-core prefix kernel, which takes 16-bit and FP8 pools only.
-    if (p.merge_ptr) return hipErrorInvalidValue;
+    if (p.num_levels > 0) return hipErrorInvalidValue;
     hipLaunchKernelGGL((decode_kernel<T, D, G, NW, PM, false>), grid, block, 0, s, p);
   } else {
-    if (p.merge_ptr)
+    if (p.num_levels > 0)
       hipLaunchKernelGGL((decode_kernel<T, D, G, NW, PM, true>), grid, block, 0, s, p);
     else
       hipLaunchKernelGGL((decode_kernel<T, D, G, NW, PM, false>), grid, block, 0, s, p);

@@ -38,6 +38,14 @@ struct DecodeParams {
   // Bytes of st_o / st_lse a finishing item may prefetch level states from through 32-bit
   // buffer offsets (0: states beyond 2 GiB, read directly at the end instead).
   int32_t fold_o_bytes, fold_lse_bytes;
+  // In-kernel contraction (counters != nullptr; needs merge_ptr / merge_rows, nl2 = levels + 2):
+  // the workgroup whose partial state of a split request arrives last merges the request's
+  // merge list into its output, and a request with no decode item that no item writes through
+  // (req_flags[b] == 0) is merged by workgroup (b mod #CTA, kv head).  counters [B, Hkv] are
+  // zero before the launch and left zero by it.
+  uint32_t* counters;
+  const int32_t* req_flags;
+  int32_t batch;
 };
 
 // Multi-query (MFMA) stage of one cascade level.

@@ -5,82 +5,28 @@
 // merged in one pass.  The identity (0, -inf) results when there is nothing to merge.
 #include "device_common.h"
 #include "kernels.h"
+#include "merge_ops.h"
 
 namespace pkc {
 
-template <typename T>
-__device__ __forceinline__ void load4(const void* base, int64_t idx, float* out) {
-  if constexpr (Elem<T>::kBytes == 4) {
-    const float4 x = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx);
-    out[0] = x.x; out[1] = x.y; out[2] = x.z; out[3] = x.w;
-  } else {
-    const uint2 x = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + idx);
-    out[0] = Elem<T>::lo(x.x); out[1] = Elem<T>::hi(x.x);
-    out[2] = Elem<T>::lo(x.y); out[3] = Elem<T>::hi(x.y);
-  }
-}
-
-template <typename T>
-__device__ __forceinline__ void store4(void* base, int64_t idx, const float* v) {
-  if constexpr (Elem<T>::kBytes == 4) {
-    *reinterpret_cast<float4*>(static_cast<float*>(base) + idx) = make_float4(v[0], v[1], v[2], v[3]);
-  } else {
-    uint2 x;
-    x.x = (uint32_t)bits16<T>(v[0]) | ((uint32_t)bits16<T>(v[1]) << 16);
-    x.y = (uint32_t)bits16<T>(v[2]) | ((uint32_t)bits16<T>(v[3]) << 16);
-    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + idx) = x;
-  }
-}
-
-// Running merge of one more state (natural-log LSE `lse`, values o4) into (m, l, acc) kept in
-// base 2.
-__device__ __forceinline__ void absorb(float& m, float& l, float* acc, float lse, const float* o4) {
-  const float s = lse * kLog2e;
-  const float mn = fmaxf(m, s);
-  const float mu = (mn == kNegInf) ? 0.f : mn;
-  const float a = fast_exp2(m - mu);
-  const float w = fast_exp2(s - mu);
-  l = l * a + w;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) acc[e] = acc[e] * a + o4[e] * w;
-  m = mn;
-}
-
-__device__ __forceinline__ void finish(float m, float l, float* acc, float* lse_out) {
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) acc[e] = l > 0.f ? acc[e] * inv : 0.f;
-  *lse_out = l > 0.f ? (m + log2f(l)) * kLn2 : kNegInf;
-}
-
-// A workgroup finishes kMergeRequestsPerBlock consecutive requests (all their heads), so the
-// pass stays a small launch when most requests were already written by the decode kernel:
-// a flagged request costs one uniform branch.
-constexpr int kMergeRequestsPerBlock = 4;
+// Workgroup (x, y) finishes kMergeRequestsPerBlock consecutive requests for heads
+// y * HPB .. y * HPB + HPB - 1; a request the decode kernel already wrote costs one uniform
+// branch.
+constexpr int kMergeRequestsPerBlock = 2;
 template <typename TO, int D>
 __global__ __launch_bounds__(256) void merge_plan_kernel(const MergePlanParams p) {
   constexpr int TPH = D / 4;          // threads per head
-  constexpr int HPB = 256 / TPH;      // heads per pass of the block
+  constexpr int HPB = 256 / TPH;      // heads of the block
   const int d0 = (threadIdx.x % TPH) * 4;
+  const int h = blockIdx.y * HPB + threadIdx.x / TPH;
+  if (h >= p.hq) return;
   for (int bi = 0; bi < kMergeRequestsPerBlock; ++bi) {
     const int b = blockIdx.x * kMergeRequestsPerBlock + bi;
     if (b >= p.batch) break;
     if (p.req_flags && p.req_flags[b]) continue;
     const int beg = p.merge_ptr[(int64_t)b * p.nl2 + p.l0];
     const int end = p.merge_ptr[(int64_t)b * p.nl2 + p.l1];
-    for (int h = threadIdx.x / TPH; h < p.hq; h += HPB) {
-      float m = kNegInf, l = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
-      for (int k = beg; k < end; ++k) {
-        const int64_t r = p.merge_rows[k];
-        float o4[4];
-        load4<F32>(p.st_o, (r * p.hq + h) * D + d0, o4);
-        absorb(m, l, acc, p.st_lse[r * p.hq + h], o4);
-      }
-      float lse;
-      finish(m, l, acc, &lse);
-      store4<TO>(p.o, ((int64_t)b * p.hq + h) * D + d0, acc);
-      if (d0 == 0) p.lse[(int64_t)b * p.hq + h] = lse;
-    }
+    merge_rows_to_output<TO, D>(p.st_o, p.st_lse, p.merge_rows, beg, end, p.hq, b, h, d0, p.o, p.lse);
   }
 }
 
@@ -197,11 +143,11 @@ hipError_t launch_read_stream(const void* src, int64_t mib, uint32_t* sink, hipS
 template <typename TO>
 static hipError_t merge_plan_d(int head_dim, const MergePlanParams& p, hipStream_t s) {
   if (p.batch <= 0) return hipSuccess;
-  const dim3 grid((p.batch + kMergeRequestsPerBlock - 1) / kMergeRequestsPerBlock);
+  const int gx = (p.batch + kMergeRequestsPerBlock - 1) / kMergeRequestsPerBlock;
   if (head_dim == 64) {
-    hipLaunchKernelGGL((merge_plan_kernel<TO, 64>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((merge_plan_kernel<TO, 64>), dim3(gx, (p.hq + 15) / 16), dim3(256), 0, s, p);
   } else if (head_dim == 128) {
-    hipLaunchKernelGGL((merge_plan_kernel<TO, 128>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((merge_plan_kernel<TO, 128>), dim3(gx, (p.hq + 7) / 8), dim3(256), 0, s, p);
   } else {
     return hipErrorInvalidValue;
   }

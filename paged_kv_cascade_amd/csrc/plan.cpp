@@ -146,6 +146,8 @@ pkc_status check_params(const pkc_plan_params* params, bool need_ctas, Resolved*
     return fail(PKC_ERR_INVALID_ARG, "level_write_through must be 0 or 1");
   if (!(p.level_streams == 0 || p.level_streams == 1 || p.level_streams == 2))
     return fail(PKC_ERR_INVALID_ARG, "level_streams must be 0, 1 or 2");
+  if (!(p.contraction == 0 || p.contraction == 1 || p.contraction == 2))
+    return fail(PKC_ERR_INVALID_ARG, "contraction must be 0, 1 or 2");
   if (p.num_ctas < 0 || p.level_ctas < 0 || p.level_tile_q < 0)
     return fail(PKC_ERR_INVALID_ARG, "num_ctas, level_ctas, level_tile_q must be >= 0");
   if (need_ctas && (p.num_ctas == 0 || p.level_ctas == 0))
@@ -218,6 +220,7 @@ pkc_status compute_layout(const Resolved& r, const pkc_level_host* levels, int32
   L.off_merge_rows = take(merge_rows);
   L.off_req_flags = take(B);
   L.off_req_levels = take(B * NL * 2 + 8);   // + padding: the decode kernel reads 4 levels' entries
+  L.off_counters = take(B * (int64_t)p.num_kv_heads);   // zero in every plan
   L.int_bytes = off;
   L.max_state_rows = rows + L.max_dec_rows;
   const int64_t hd = (int64_t)p.num_qo_heads * p.head_dim;
@@ -276,6 +279,12 @@ pkc_status build_plan_host(const Resolved& r, const int32_t* kv_lens_h,
   P.num_ctas = p.num_ctas;
   P.level_ctas = p.level_ctas;
   P.lvl_streams = p.level_streams;   // resolved from the device by pkc_plan (0 in host-only plans)
+  // Automatic choice: with at most one decode CTA per request few requests are split, and
+  // merging those inside the decode kernel saves the merge pass; with more CTAs than requests
+  // splitting is the rule, and the dedicated pass merges faster than the in-kernel contraction,
+  // which adds a device-scope store / count / reload round trip to every split item's tail.
+  // A function of the parameters only, like every launch shape of a run.
+  P.dec_contraction = p.contraction ? p.contraction : (p.num_ctas <= p.batch ? 1 : 2);
 
   // Levels: every item gets a state block of T_q rows (rows numbered level by level), except
   // write-through level items, which write their rows' final output.
@@ -433,6 +442,7 @@ pkc_status build_plan_host(const Resolved& r, const int32_t* kv_lens_h,
   P.off_merge_rows = L.off_merge_rows;
   P.off_req_flags = L.off_req_flags;
   P.off_req_levels = L.off_req_levels;
+  P.off_counters = L.off_counters;
   P.int_bytes = L.int_bytes;
   P.off_state_o = L.off_state_o;
   P.off_state_lse = L.off_state_lse;

@@ -49,6 +49,7 @@ pkc_status lpt_plan(const int32_t* qo_lens, const int32_t* kv_lens, int32_t n, i
 // parameters and the level shapes only, so they do not move from one step to the next.
 struct Layout {
   int64_t off_dec_indptr, off_dec_items, off_merge_ptr, off_merge_rows, off_req_flags, off_req_levels;
+  int64_t off_counters;
   int64_t off_lvl_indptr[PKC_MAX_LEVELS], off_lvl_items[PKC_MAX_LEVELS];
   int64_t int_bytes;
   int64_t max_dec_items, max_lvl_items[PKC_MAX_LEVELS];

@@ -781,7 +781,10 @@ __global__ __launch_bounds__(64 * prefix_detail::kWavesPerStream * NS, NS == 1 ?
       // (the accumulator layout), so a direct store instruction would write 16 rows x 64 bytes.
       // Instead each wave stages 16 rows at a time in its own part of the idle ring (past the
       // stream hand-off values; rows padded by 16 bytes so they start on different banks) and
-      // stores whole rows: every instruction writes 64 / (D / 4) rows of D * 4 bytes.
+      // stores whole rows: every instruction writes 64 / (D / 4) rows of D * 4 bytes.  The
+      // states are written once and read once by a later kernel, so the stores are
+      // nontemporal: they stream to memory instead of filling the L2 with dirty lines that all
+      // workgroups would otherwise write back together at the end of the kernel.
       constexpr int SRS = D * 4 + 16;
       constexpr int HAND = NS == 2 ? (DM * 2 * 4 + 4) * 256 * 4 : 0;
       static_assert(HAND + kWavesPerStream * 16 * SRS <= RING + CBUF, "state staging fits the ring");
@@ -802,15 +805,15 @@ __global__ __launch_bounds__(64 * prefix_detail::kWavesPerStream * NS, NS == 1 ?
             const f4_t o = oacc[dm][nt] * inv;
             *reinterpret_cast<float4*>(stage + l16 * SRS + (dm * 16 + 4 * lg) * 4) = make_float4(o[0], o[1], o[2], o[3]);
           }
-          if (lg == 0 && r < nrows) p.st_lse[((int64_t)srow + r / G) * p.hq + h] = lse_r;
+          if (lg == 0 && r < nrows) __builtin_nontemporal_store(lse_r, p.st_lse + ((int64_t)srow + r / G) * p.hq + h);
 #pragma unroll
           for (int k = 0; k < 16 / RPI; ++k) {
             const int rr = k * RPI + lane / LPR;
             const int row = wq * kRowsPerWave + nt * 16 + rr;
-            const float4 x = *reinterpret_cast<const float4*>(stage + rr * SRS + (lane % LPR) * 16);
+            const f4_t x = *reinterpret_cast<const f4_t*>(stage + rr * SRS + (lane % LPR) * 16);
             if (row < nrows) {
               const int64_t q = (int64_t)srow + row / G;
-              *reinterpret_cast<float4*>(p.st_o + (q * p.hq + hk * G + row % G) * D + (lane % LPR) * 4) = x;
+              __builtin_nontemporal_store(x, reinterpret_cast<f4_t*>(p.st_o + (q * p.hq + hk * G + row % G) * D + (lane % LPR) * 4));
             }
           }
           // The next half's staging writes stay behind this half's reads (one wave's LDS
@@ -824,10 +827,11 @@ __global__ __launch_bounds__(64 * prefix_detail::kWavesPerStream * NS, NS == 1 ?
 #pragma unroll
           for (int dm = 0; dm < DM; ++dm) {
             const f4_t o = oacc[dm][nt] * inv;
-            *reinterpret_cast<uint2*>(dst + (dm * 16 + 4 * lg) * ES) =
-                make_uint2(Mfma<T>::pack(o[0], o[1]), Mfma<T>::pack(o[2], o[3]));
+            typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
+            __builtin_nontemporal_store(u2_t{Mfma<T>::pack(o[0], o[1]), Mfma<T>::pack(o[2], o[3])},
+                                        reinterpret_cast<u2_t*>(dst + (dm * 16 + 4 * lg) * ES));
           }
-          if (lg == 0) p.lse[orow * p.hq + h] = lse_r;
+          if (lg == 0) __builtin_nontemporal_store(lse_r, p.lse + orow * p.hq + h);
         }
       }
     }

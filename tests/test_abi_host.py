@@ -336,3 +336,27 @@ def test_noalloc_decode_refuses_oversized_plans_before_any_hip_call(api):
     assert lib.pkc_batch_decode_paged_noalloc(ctypes.byref(info3), ctypes.c_void_p(hb3.data_ptr()), hb3.numel(),
                                               d, d, d, 4, d, 8, d, None, 8, 4, 4, 128, 16, 1, 0.1, d, d,
                                               None) == 4
+
+
+def test_contraction_mode_and_counter_region(api):
+    """The contraction parameter selects where split requests are merged (1: inside the decode
+    kernel; 2: a merge pass; 0: 1 when #CTA <= B, else 2), and the plan's arrival counters (uint32 [B, Hkv],
+    inside the integer arrays) are zero in every plan, also when the host buffer held other
+    values before."""
+    rng = random.Random(7)
+    for mode, ctas, want in ((0, 24, 1), (0, 37, 1), (0, 38, 2), (1, 80, 1), (2, 24, 2)):
+        B, hkv = 37, 4
+        lens = [rng.randint(0, 5000) for _ in range(B)]
+        p = api.make_params(B, 16, hkv, 128, 16, num_ctas=ctas, level_ctas=2, contraction=mode)
+        nb = api.plan_buffer_sizes(p)[0]
+        hb = torch.full((nb,), 0x5A, dtype=torch.uint8)
+        info, hb = api.plan_host(p, lens, host_buf=hb)
+        assert info.dec_contraction == want
+        assert info.off_counters + B * hkv * 4 <= info.int_bytes
+        assert info.off_counters >= info.off_req_levels
+        ctr = hb.numpy().view("uint32")[info.off_counters // 4: info.off_counters // 4 + B * hkv]
+        assert not ctr.any(), "counters must be zero in every plan"
+        assert info.num_merge > 0
+    with pytest.raises(api.PkcError) as e:
+        api.plan_host(api.make_params(2, 4, 4, 128, 16, num_ctas=4, level_ctas=1, contraction=3), [1, 2])
+    assert e.value.status == 1
