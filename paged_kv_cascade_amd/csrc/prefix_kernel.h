@@ -428,11 +428,12 @@ __global__ __launch_bounds__(64 * prefix_detail::kWavesPerStream * NS, NS == 1 ?
     // scores and weights of one tile are exactly those of the unpipelined order.  A dummy
     // previous tile (scores -inf, V^T operands zero) starts the pipeline: its weights are 0
     // and it adds nothing.  The pipeline keeps a second score tile and the V^T operands live
-    // across the step (about 250 VGPRs at D = 128); with grouped heads the extra row indexing
-    // no longer fits 256, nor does the FP8 conversion, so those instantiations run a tile's
-    // pieces in order in its step (FP8: with the V^T reads after the softmax, which needs
-    // fewer live registers).
-    constexpr bool kPipe = !F8 && (D == 64 || G == 1);
+    // across the step (about 250 VGPRs at D = 128); with grouped heads at D = 128 the extra
+    // row indexing no longer fits 256, nor does the causal FP8 variant, so those
+    // instantiations run a tile's pieces in order in its step (FP8: with the V^T reads after
+    // the softmax, which needs fewer live registers).  With FP8 pools the tile's 16-bit copy
+    // (parity j % 2) is read only in step j here too, so the copy protocol below holds.
+    constexpr bool kPipe = (D == 64 || G == 1) && !(F8 && CAUSAL && D == 128);
     f4_t sp[2][2];   // scores of the previous tile, waiting for their softmax
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
