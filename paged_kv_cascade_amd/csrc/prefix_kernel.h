@@ -31,12 +31,12 @@
 // Output: one fp32 state (O normalised, natural-log LSE) per (query, head, item).
 //
 // FP8 pools (F8, OCP E4M3 codes with 16-bit queries; FlashInfer paper summary, appendix F):
-// the ring holds the codes (half the bytes per tile), and each wave, once its own loads of a
-// tile have landed, converts the rows it loaded into a 16-bit copy of the tile in LDS (the
-// same swizzled layout the 16-bit path loads into), double-buffered so the conversion of tile
-// j+1 never overwrites what another wave still reads for tile j.  The arithmetic then runs
-// unchanged on the copy.  Every E4M3 value is exact in fp16 and bf16; the pool scales act
-// outside the loop (K's on the softmax scale, V's on the final state).
+// the ring holds the codes (half the bytes per tile, so twice the tiles in flight), and the
+// codes are converted in registers on their way from LDS into the matrix-core operands: 8
+// bytes per lane per operand (ds_read_b64 for K, the 8-bit transpose read for V^T), 4
+// packed conversions each.  Every E4M3 value is exact in fp16 and bf16, so the arithmetic
+// is that of the 16-bit path; the pool scales act outside the loop (K's on the softmax scale,
+// V's on the final state).
 //
 // This header holds the kernel template; prefix.hip instantiates the 16-bit pools and
 // prefix_fp8.hip the FP8 ones.
@@ -175,29 +175,43 @@ __device__ __forceinline__ int swz(int r) {
   else return 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
 }
 
-// Converts 16 E4M3 codes (bytes in address order) to 16 values of the operand type T, as two
-// 16-byte halves (codes 0..7, then 8..15).
-template <typename T>
-__device__ __forceinline__ void e4m3_to_operand(const uint4& c, V16& lo, V16& hi) {
-  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t a, b;
-    if constexpr (std::is_same<T, F16>::value) {
-      a = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, false));
-      b = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, true));
-    } else {
-      a = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false));
-      b = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true));
-    }
-    V16& dst = i < 2 ? lo : hi;
-    dst.w[2 * (i & 1)] = a;
-    dst.w[2 * (i & 1) + 1] = b;
-  }
+// Physical 16-byte chunk of logical chunk c in LDS code row r (FP8 rings, D bytes per row):
+// c ^ swz8(r).  D = 128 (two rows per 256-byte bank sweep): the 16 rows of one K operand read
+// (8 bytes each, same column) and the 8 rows x 2 halves of one 8-bit transpose read (tokens
+// 4g + i and 16 + 4g + i) land on distinct banks in each half-wave.  D = 64 (four rows per
+// sweep): the same with the row's position in the sweep.
+template <int D>
+__device__ __forceinline__ int swz8(int r) {
+  if constexpr (D == 128) return ((r >> 1) & 7) ^ (((r >> 4) & 1) << 2);
+  else return ((r >> 2) & 3) ^ (((r >> 4) & 1) << 1);
 }
 
-__device__ __forceinline__ void lds_store16(char* p, const V16& v) {
-  *reinterpret_cast<uint4*>(p) = make_uint4(v.w[0], v.w[1], v.w[2], v.w[3]);
+// Converts 8 E4M3 codes (bytes in address order) to 8 values of the operand type T.
+template <typename T>
+__device__ __forceinline__ V16 e4m3x8_to_operand(uint2 c) {
+  V16 r;
+  const uint32_t w[2] = {c.x, c.y};
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    if constexpr (std::is_same<T, F16>::value) {
+      r.w[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, false));
+      r.w[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, true));
+    } else {
+      r.w[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false));
+      r.w[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true));
+    }
+  }
+  return r;
+}
+
+__device__ __forceinline__ uint2 lds_load8(const char* p) { return *reinterpret_cast<const uint2*>(p); }
+
+// 8-bit transpose read: within each 16-lane group, the 8-byte pieces named by lanes 2i and
+// 2i+1 form row i (16 bytes); lane j receives byte j of rows 0..7.
+typedef int i2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 lds_read_tr8(const char* p) {
+  const i2_t r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i2_t*)(p));
+  return __builtin_bit_cast(uint2, r);
 }
 
 // Runs f(integral_constant<S>, j + S) for S = S0 .. N-1 while j + S < n; false once it stops
@@ -225,29 +239,24 @@ __global__ __launch_bounds__(64 * prefix_detail::kWavesPerStream * NS, NS == 1 ?
   constexpr int RBG = D * KB;                // bytes per K / V row in the pool and the ring
   constexpr int CPRG = RBG / 16;             // 16-byte chunks per ring row
   constexpr int NDMA = 4;                    // load instructions per wave per tile (K and V)
-  constexpr int STB = kTK * RB;              // bytes of K (or V) of one 16-bit tile
   constexpr int STBG = kTK * RBG;            // bytes of K (or V) of one ring tile
   constexpr int SLOT = 2 * STBG;             // one tile in the ring: K rows, then V rows
-  // Ring depth and tiles in flight.  16-bit: a stage is read by the arithmetic of its step,
-  // so it is refilled one step later (3 tiles in flight of 4 stages).  F8: a stage is only
-  // read by the conversion before the step's barrier, so it is refilled right after that
-  // barrier, and the ring has 5 stages (5 tiles, 40 KB in flight, 72 KB of LDS per workgroup
-  // at D = 128 with the 16-bit copies: two workgroups still fit a compute unit).
-  constexpr int STAGES = F8 ? 5 : 4;
-  constexpr int AHEAD = F8 ? STAGES : STAGES - 1;
+  // Ring depth and tiles in flight: a stage is read by the arithmetic of its step, so it is
+  // refilled one step later (STAGES - 1 tiles in flight: 48 KB per stream with 16-bit pools,
+  // 56 KB with FP8 codes, whose half-size tiles leave room for 8 stages).
+  constexpr int STAGES = F8 ? 8 : 4;
+  constexpr int AHEAD = STAGES - 1;
   constexpr int KS = D / 32;                 // contraction steps of S^T
   constexpr int DM = D / 16;                 // 16-row tiles of O^T
   constexpr int RING = STAGES * NS * SLOT;
-  constexpr int CBUF = F8 ? NS * 2 * 2 * STB : 0;   // 16-bit copies: stream, parity, K / V
+  constexpr int CBUF = 0;
   static_assert(kTK == 32 && (D == 64 || D == 128) && (NS == 1 || NS == 2), "tile layout");
 
   // The ring: stage s of stream g is ring + (g * STAGES + s) * SLOT; the valid-row bits of that
-  // tile are word g * STAGES + s of sflag (byte w written by the stream's wave w).  With F8 the
-  // 16-bit copies follow the ring: copy (g, parity) at cbuf + (g * 2 + parity) * 2 * STB.
+  // tile are word g * STAGES + s of sflag (byte w written by the stream's wave w).
   __shared__ __attribute__((aligned(16))) char smem[RING + CBUF];
   __shared__ uint32_t sflag[STAGES * NS];
   char* const ring = smem;
-  char* const cbuf = smem + RING;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -274,9 +283,10 @@ __global__ __launch_bounds__(64 * prefix_detail::kWavesPerStream * NS, NS == 1 ?
   // 128-byte rows: one 1 KB instruction covers both groups as two exec-masked halves, lane l ->
   // row 8wq + l/8, LDS chunk l%8.  64-byte rows (FP8 codes, D = 64): lanes 0..31 cover both
   // groups the same way (lane l -> row 8wq + l/4) and lanes 32..63 load nothing.  16-bit rows
-  // are swizzled (each lane fetches logical chunk (LDS chunk) ^ swz(row)); code rows are stored
-  // as they are and swizzled when converted.  voff is a lane's byte offset from its group's
-  // first row in the page.
+  // are swizzled (each lane fetches logical chunk (LDS chunk) ^ swz(row)); code rows likewise
+  // with swz8.  voff is a lane's byte offset from its group's first row in the page.  Pages of
+  // 8 or more slots hold all 8 rows of the wave: then one buffer resource pair serves both
+  // groups.  Every path issues the same NDMA loads per tile (the ring's waits count them).
   constexpr int NI = RBG == 256 ? 2 : 1;   // instructions per operand per tile
   constexpr int LROWS = 64 / CPRG;         // rows one instruction covers (all lanes)
   int32_t voff[NI];
@@ -284,9 +294,10 @@ __global__ __launch_bounds__(64 * prefix_detail::kWavesPerStream * NS, NS == 1 ?
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     lrow[i] = 8 * wq + (RBG == 256 ? 4 * i + lane / 16 : (lane / CPRG) % 8);
-    const int cg = F8 ? lane % CPRG : (lane % CPRG) ^ swz<D>(lrow[i]);
+    const int cg = F8 ? (lane % CPRG) ^ swz8<D>(lrow[i]) : (lane % CPRG) ^ swz<D>(lrow[i]);
     voff[i] = ((lrow[i] - 8 * wq) & 3) * row_stride + hk * RBG + cg * 16;
   }
+  const bool one_page = P >= 8;
   static_assert(LROWS >= 4, "row geometry");
 
   const int it_begin = scalar_load(p.indptr + blockIdx.x);
@@ -347,7 +358,7 @@ __global__ __launch_bounds__(64 * prefix_detail::kWavesPerStream * NS, NS == 1 ?
       const int rb = t0 + tt * kTK + 8 * wq;
       Pg r;
       r.e0 = scalar_load(pages + min(rb >> shift, last_page));
-      r.e1 = scalar_load(pages + min((rb + 4) >> shift, last_page));
+      r.e1 = one_page ? r.e0 : scalar_load(pages + min((rb + 4) >> shift, last_page));
       return r;
     };
 
@@ -357,45 +368,77 @@ __global__ __launch_bounds__(64 * prefix_detail::kWavesPerStream * NS, NS == 1 ?
     auto issue = [&](int tt, const Pg& pg, uint32_t dst, uint32_t* flag) __attribute__((always_inline)) {
       const int rb = t0 + tt * kTK + 8 * wq;      // token of the wave's first row
       const bool in_tiles = tt < ntiles;
-      const int e[2] = {pg.e0, pg.e1};
-      u4_t rk[2], rw[2];
-      int32_t soff[2];
-      bool ok[2];
+      uint32_t okbits;
+      if (one_page) {
+        // The wave's 8 rows sit in one page: one resource pair, row offsets from its first row.
+        const bool ok = in_tiles & ((rb >> shift) < npages_grp) & (pg.e0 >= 0) & (pg.e0 < npool);
+        const int64_t pofs = ok ? (int64_t)pg.e0 * page_bytes : 0;
+        const u4_t rk = dma_rsrc(kg + pofs, ok ? page_bytes : 0);
+        const u4_t rw = dma_rsrc(vg + pofs, ok ? page_bytes : 0);
+        const int32_t soff = (rb & (P - 1)) * row_stride;   // group g: + 4 g rows
 #pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        const int tg = rb + 4 * g;
-        ok[g] = in_tiles & ((tg >> shift) < npages_grp) & (e[g] >= 0) & (e[g] < npool);
-        const int64_t pofs = ok[g] ? (int64_t)e[g] * page_bytes : 0;
-        rk[g] = dma_rsrc(kg + pofs, ok[g] ? page_bytes : 0);
-        rw[g] = dma_rsrc(vg + pofs, ok[g] ? page_bytes : 0);
-        soff[g] = (tg & (P - 1)) * row_stride;
-      }
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const int t = t0 + tt * kTK + lrow[i];
-        const int32_t off = ((t >= kb) & (t < ke)) ? voff[i] : kOffsetNone;
-        const uint32_t dk = dst + (8 * wq + 4 * i) * RBG;
-        const uint32_t dv = dk + STBG;
-        if constexpr (RBG == 256) {
-          load_lds16(rk[i], dk, off, soff[i]);
-          load_lds16(rw[i], dv, off, soff[i]);
-        } else {
-          // Two exec-masked halves (their rows may sit in different pages); both write the
-          // block's 8 rows, lane l at 16 * l.
-          constexpr int HALF = 4 * CPRG;   // lanes of one 4-row group
-          if (lane < HALF) {
-            load_lds16(rk[0], dk, off, soff[0]);
-            load_lds16(rw[0], dv, off, soff[0]);
-          } else if (lane < 2 * HALF) {
-            load_lds16(rk[1], dk, off, soff[1]);
-            load_lds16(rw[1], dv, off, soff[1]);
+        for (int i = 0; i < NI; ++i) {
+          const int t = t0 + tt * kTK + lrow[i];
+          const int32_t off = ((t >= kb) & (t < ke)) ? voff[i] : kOffsetNone;
+          const uint32_t dk = dst + (8 * wq + 4 * i) * RBG;
+          const uint32_t dv = dk + STBG;
+          if constexpr (RBG == 256) {
+            load_lds16(rk, dk, off, soff + 4 * i * row_stride);
+            load_lds16(rw, dv, off, soff + 4 * i * row_stride);
+          } else {
+            constexpr int HALF = 4 * CPRG;   // lanes of one 4-row group
+            if (lane < HALF) {
+              load_lds16(rk, dk, off, soff);
+              load_lds16(rw, dv, off, soff);
+            } else if (lane < 2 * HALF) {
+              load_lds16(rk, dk, off, soff + 4 * row_stride);
+              load_lds16(rw, dv, off, soff + 4 * row_stride);
+            }
           }
         }
+        okbits = ok ? 0xFFu : 0u;
+      } else {
+        const int e[2] = {pg.e0, pg.e1};
+        u4_t rk[2], rw[2];
+        int32_t soff[2];
+        bool ok[2];
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          const int tg = rb + 4 * g;
+          ok[g] = in_tiles & ((tg >> shift) < npages_grp) & (e[g] >= 0) & (e[g] < npool);
+          const int64_t pofs = ok[g] ? (int64_t)e[g] * page_bytes : 0;
+          rk[g] = dma_rsrc(kg + pofs, ok[g] ? page_bytes : 0);
+          rw[g] = dma_rsrc(vg + pofs, ok[g] ? page_bytes : 0);
+          soff[g] = (tg & (P - 1)) * row_stride;
+        }
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          const int t = t0 + tt * kTK + lrow[i];
+          const int32_t off = ((t >= kb) & (t < ke)) ? voff[i] : kOffsetNone;
+          const uint32_t dk = dst + (8 * wq + 4 * i) * RBG;
+          const uint32_t dv = dk + STBG;
+          if constexpr (RBG == 256) {
+            load_lds16(rk[i], dk, off, soff[i]);
+            load_lds16(rw[i], dv, off, soff[i]);
+          } else {
+            // Two exec-masked halves (their rows may sit in different pages); both write the
+            // block's 8 rows, lane l at 16 * l.
+            constexpr int HALF = 4 * CPRG;   // lanes of one 4-row group
+            if (lane < HALF) {
+              load_lds16(rk[0], dk, off, soff[0]);
+              load_lds16(rw[0], dv, off, soff[0]);
+            } else if (lane < 2 * HALF) {
+              load_lds16(rk[1], dk, off, soff[1]);
+              load_lds16(rw[1], dv, off, soff[1]);
+            }
+          }
+        }
+        okbits = (ok[0] ? 0x0Fu : 0u) | (ok[1] ? 0xF0u : 0u);
       }
       // Valid rows: inside [kb, ke) and in a valid page.
       const int lo = min(max(kb - rb, 0), 8), hi = min(max(ke - rb, 0), 8);
       uint32_t bits = hi > lo ? (((1u << hi) - 1u) & ~((1u << lo) - 1u)) : 0u;
-      bits &= (ok[0] ? 0x0Fu : 0u) | (ok[1] ? 0xF0u : 0u);
+      bits &= okbits;
       reinterpret_cast<uint8_t*>(flag)[wq] = (uint8_t)bits;
     };
 
@@ -429,11 +472,9 @@ __global__ __launch_bounds__(64 * prefix_detail::kWavesPerStream * NS, NS == 1 ?
     // previous tile (scores -inf, V^T operands zero) starts the pipeline: its weights are 0
     // and it adds nothing.  The pipeline keeps a second score tile and the V^T operands live
     // across the step (about 250 VGPRs at D = 128); with grouped heads at D = 128 the extra
-    // row indexing no longer fits 256, nor does the causal FP8 variant, so those
-    // instantiations run a tile's pieces in order in its step (FP8: with the V^T reads after
-    // the softmax, which needs fewer live registers).  With FP8 pools the tile's 16-bit copy
-    // (parity j % 2) is read only in step j here too, so the copy protocol below holds.
-    constexpr bool kPipe = (D == 64 || G == 1) && !(F8 && CAUSAL && D == 128);
+    // row indexing no longer fits 256, so those instantiations run a tile's pieces in order
+    // in its step.
+    constexpr bool kPipe = D == 64 || G == 1;
     f4_t sp[2][2];   // scores of the previous tile, waiting for their softmax
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
@@ -453,7 +494,12 @@ __global__ __launch_bounds__(64 * prefix_detail::kWavesPerStream * NS, NS == 1 ?
         const int r = mt * 16 + l16;
         V16 ka[KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) ka[ks] = lds_load16(ks_s + r * RB + (((ks * 4 + lg) ^ swz<D>(r)) * 16));
+        for (int ks = 0; ks < KS; ++ks) {
+          if constexpr (F8)   // codes ks*32 + 8*lg .. +8: half lg & 1 of logical chunk 2 ks + lg / 2
+            ka[ks] = e4m3x8_to_operand<T>(lds_load8(ks_s + r * RBG + (((2 * ks + (lg >> 1)) ^ swz8<D>(r)) * 16) + (lg & 1) * 8));
+          else
+            ka[ks] = lds_load16(ks_s + r * RB + (((ks * 4 + lg) ^ swz<D>(r)) * 16));
+        }
         s[mt][0] = f4_t{0.f, 0.f, 0.f, 0.f};
         s[mt][1] = f4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -464,17 +510,27 @@ __global__ __launch_bounds__(64 * prefix_detail::kWavesPerStream * NS, NS == 1 ?
       }
     };
     // V^T operands of a tile (see the PV products below).
+    // FP8: one 8-bit transpose read per dm gives lane (l16, lg) the codes of head_dim
+    // column dm*16 + l16 for its 8 tokens, in the same order: row i of the read (lanes 2i,
+    // 2i+1 of the group, each naming 8 bytes of logical chunk dm) is token 4*lg + i for
+    // i < 4, else 16 + 4*lg + i - 4.
+    const int tr8_tok = (l16 < 8 ? 0 : 12) + 4 * lg + (l16 >> 1);
     auto vread = [&](const char* vs_s) __attribute__((always_inline)) {
 #pragma unroll
-      for (int dm = 0; dm < DM; ++dm)
+      for (int dm = 0; dm < DM; ++dm) {
+        if constexpr (F8) {
+          va[dm] = e4m3x8_to_operand<T>(lds_read_tr8(vs_s + tr8_tok * RBG + ((dm ^ swz8<D>(tr8_tok)) * 16) + (l16 & 1) * 8));
+        } else {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int r = 16 * h + 4 * lg + tr_row;
-          const int c = (2 * dm + (tr_piece >> 1)) ^ swz<D>(r);
-          const uint2 x = lds_read_tr(vs_s + r * RB + c * 16 + (tr_piece & 1) * 8);
-          va[dm].w[2 * h] = x.x;
-          va[dm].w[2 * h + 1] = x.y;
+          for (int h = 0; h < 2; ++h) {
+            const int r = 16 * h + 4 * lg + tr_row;
+            const int c = (2 * dm + (tr_piece >> 1)) ^ swz<D>(r);
+            const uint2 x = lds_read_tr(vs_s + r * RB + c * 16 + (tr_piece & 1) * 8);
+            va[dm].w[2 * h] = x.x;
+            va[dm].w[2 * h + 1] = x.y;
+          }
         }
+      }
     };
     // Softmax of the previous tile, first part: masks, each lane's share of the column
     // maxima, and the rare raise of the reference maximum (a wave-uniform branch).
@@ -663,59 +719,30 @@ __global__ __launch_bounds__(64 * prefix_detail::kWavesPerStream * NS, NS == 1 ?
           qb[nt][ks] = V16{{qr[nt][ks][0], qr[nt][ks][1], qr[nt][ks][2], qr[nt][ks][3]}};
         }
 
-      // Step j in stage S = j % STAGES (16-bit pools): wait for this wave's loads of the
-      // stream's j-th tile (its next two tiles stay in flight), barrier (every wave's loads and
-      // valid-row byte of the step's tiles have landed and every wave is done with step j-1),
-      // refill stage S-1 with the stream's tile j+3, compute tile j (its S^T products and
-      // V^T reads, and tile j-1's softmax and PV products), request the page entries of tile
-      // j+4 (after the step's LDS reads: scalar loads and LDS reads share one counter, so an
+      // Step j in stage S = j % STAGES: wait for this wave's loads of the stream's j-th tile
+      // (its next AHEAD - 1 tiles stay in flight), barrier (every wave's loads and valid-row
+      // byte of the step's tiles have landed and every wave is done with step j-1), refill
+      // stage S-1 with the stream's tile j + AHEAD, compute tile j (its S^T products and V^T
+      // reads, and tile j-1's softmax and PV products), request the page entries of tile
+      // j + AHEAD + 1 (after the step's LDS reads: scalar loads and LDS reads share one counter, so an
       // LDS wait also waits for any scalar load in flight).  Before the barrier the wave waits
       // for its own LDS operations (the V^T reads at the end of the previous step), so no wave
       // still reads the stage the refill overwrites.  Every stream runs the same number of
       // steps (and barriers).  Stage numbers are compile-time constants (STAGES steps per loop
       // trip), so ring addresses are immediate offsets.
-      //
-      // F8: the wait leaves AHEAD - 1 tiles in flight; between the wait and the barrier the
-      // wave converts the code rows it loaded into the 16-bit copy of parity j % 2 (that copy
-      // was last read in step j-2, which every wave finished before the barrier of step j-1)
-      // and waits for its LDS writes, so after the barrier the whole copy is there and no
-      // wave reads stage S any more: the stream's tile j + AHEAD refills it.  The valid-row
-      // word of stage S is read before the barrier (its bytes were written at step j - AHEAD,
-      // before the barrier of step j-1), since the refill rewrites it.
+
       auto step = [&](auto stage_c, int j) __attribute__((always_inline)) {
         constexpr int S = decltype(stage_c)::value;
         constexpr int N = (S + AHEAD) % STAGES;
         const int tt = stream + j * NS;
         PKC_WAIT_VMCNT((AHEAD - 1) * NDMA);
-        char* const cb = cbuf + (stream * 2 + (j & 1)) * 2 * STB;
-        uint32_t mask = 0;
-        if constexpr (F8) {
-          mask = sfl[S];
-          __asm__ volatile("" ::: "memory");
-          if (lane < 8 * CPRG) {
-            const int r = 8 * wq + lane / CPRG;   // tile row this lane loaded
-            const int c = lane % CPRG;            // its 16 codes = 16-bit chunks 2c, 2c + 1
-#pragma unroll
-            for (int op = 0; op < 2; ++op) {
-              const uint4 x = *reinterpret_cast<const uint4*>(sring + S * SLOT + op * STBG + 8 * wq * RBG + 16 * lane);
-              V16 lo, hi;
-              e4m3_to_operand<T>(x, lo, hi);
-              char* drow = cb + op * STB + r * RB;
-              lds_store16(drow + ((2 * c) ^ swz<D>(r)) * 16, lo);
-              lds_store16(drow + ((2 * c + 1) ^ swz<D>(r)) * 16, hi);
-            }
-          }
-          PKC_WAIT_LGKMCNT0();
-        } else {
-          PKC_WAIT_LGKMCNT0();
-        }
+        PKC_WAIT_LGKMCNT0();
         ring_barrier();
-        if constexpr (!F8) mask = sfl[S];   // the same on every lane; used in the next step
+        const uint32_t mask = sfl[S];   // the same on every lane
         issue(tt + AHEAD * NS, pg, lds_addr(sring) + N * SLOT, sfl + N);
         if (tt < ntiles) {
           const int tok0 = t0 + tt * kTK;   // the tile's first token (causal mask)
-          if constexpr (F8) compute(cb, cb + STB, mask, tok0);
-          else compute(sring + S * SLOT, sring + S * SLOT + STB, mask, tok0);
+          compute(sring + S * SLOT, sring + S * SLOT + STBG, mask, tok0);
         }
         pg = fetch(tt + (AHEAD + 1) * NS);
       };
