@@ -40,7 +40,7 @@ METRIC = "KV bytes/s from HBM (% of peak) + decode steps/s, cascade 32K prefix, 
 PEAK_HBM_GBPS = 8000.0
 KERNEL_SOURCES = ["paged_kv_cascade_amd/csrc/prefix_kernel.h", "paged_kv_cascade_amd/csrc/decode.hip",
                   "paged_kv_cascade_amd/csrc/decode_kernel.h", "paged_kv_cascade_amd/csrc/merge.hip",
-                  "paged_kv_cascade_amd/csrc/device_common.h"]
+                  "paged_kv_cascade_amd/csrc/merge_ops.h", "paged_kv_cascade_amd/csrc/device_common.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "cascade32k_b128_hbm_traffic.json")
 # FETCH_SIZE of one non-cascade step over the same data (rocprofv3, scaled by the copy
 # calibration), from the committed counter summary of that kernel.
