@@ -83,8 +83,11 @@ def copy_calibration():
 class Step:
     """Buffers and per-step calls of the serving loop: the CPU plan of the step (into one of
     two pinned host buffers, uploaded on the stream into the one device workspace), then the
-    replay of the cascade run captured once in a HIP graph (FlashInfer paper summary, section
-    A3: plan on the CPU outside the graph, run captured; appendix D: fixed pointers)."""
+    cascade run launched on the stream (`__call__`), or the replay of that run captured once
+    in a HIP graph (`step_graph`; FlashInfer paper summary, section A3: plan on the CPU
+    outside the graph, run captured; appendix D: fixed pointers).  Both compute the same bits
+    (checked in main).  On this stack the graph launch costs the GPU about 6-7 us per step
+    more than the two direct launches, so the timed loop launches directly."""
 
     def __init__(self, api, w, capture=True):
         import torch
@@ -143,6 +146,11 @@ class Step:
         self.graph.replay()
 
     def __call__(self):
+        """One serving-loop step: plan and upload, then the cascade run (direct launches)."""
+        self.run(self.plan())
+
+    def step_graph(self):
+        """The same step with the run replayed from the captured graph."""
         self.plan()
         self.replay()
 
@@ -225,8 +233,8 @@ def percentiles(xs):
 
 
 def step_time_distribution(step, n, evict=None):
-    """Device time of n single cascade runs (replays of the captured run), each between its
-    own pair of events on the launch stream; with `evict`, a 512 MiB buffer is rewritten
+    """Device time of n single cascade runs (direct launches of the latest plan), each between
+    its own pair of events on the launch stream; with `evict`, a 512 MiB buffer is rewritten
     before each run, outside the pair, so the run starts with none of its KV in the
     last-level cache."""
     import torch
@@ -235,7 +243,7 @@ def step_time_distribution(step, n, evict=None):
         if evict is not None:
             evict.add_(1)
         a.record()
-        step.replay()
+        step.run(step.info)
         b.record()
     torch.cuda.synchronize()
     return percentiles([1e3 * a.elapsed_time(b) for a, b in evs])
@@ -595,28 +603,70 @@ def main():
     gc.freeze()
 
     # The replayed graph computes what the eager run computes (same kernels, same plan).
-    step()
+    step.step_graph()
     torch.cuda.synchronize()
     ref_o, ref_l = step.out.clone(), step.lse.clone()
     step.run(step.info)
     torch.cuda.synchronize()
     graph_equal = bool(torch.equal(ref_o, step.out) and torch.equal(ref_l, step.lse))
 
-    # Measurements outside the timed steps that also bring the GPU to its steady clocks:
-    # the plan's CPU time, per-kernel durations (HIP events the library records around each
-    # launch on its stream; eager launches) and the distribution of single-run device times.
-    t0 = time.perf_counter()
+    # An idle GPU comes back at lower clocks and takes tens of milliseconds of steady work to
+    # reach the serving loop's again (in a kernel trace the first ~80 level-kernel launches
+    # after start-up average 115-127 us, later ones 100 us): replays first, untimed.
     for _ in range(200):
-        step.plan()
-    ms_plan = 1e3 * (time.perf_counter() - t0) / 200
-    # Untimed runs first: the CPU-only plan loop above leaves the GPU idle for milliseconds,
-    # and launches measured right after an idle gap run at lower clocks.
-    for _ in range(30):
         step.run(step.info)
     torch.cuda.synchronize()
+    evict = torch.zeros(512 << 20, dtype=torch.uint8, device="cuda")
+    dist_cold = step_time_distribution(step, 50, evict)
+    del evict
+    dist_warm = step_time_distribution(step, max(100, args.steps))
+
+    # W warm-up steps, right after the GPU work above (no idle gap before the timed steps).
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Timed region: exactly K serving-loop steps (plan on the CPU and its upload, then the run).
+    gc.disable()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    gc.enable()
+    ms_step = 1e3 * elapsed / args.steps
+
+    # The same K steps with the run replayed from the captured graph.
+    for _ in range(20):
+        step.step_graph()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step.step_graph()
+    torch.cuda.synchronize()
+    ms_step_graph = 1e3 * (time.perf_counter() - t0) / args.steps
+
+    # Device-only steps (one plan, K runs; then K graph replays) -- the kernels alone.
+    step.plan()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step.run(step.info)
+    torch.cuda.synchronize()
+    ms_dev = 1e3 * (time.perf_counter() - t0) / args.steps
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step.replay()
+    torch.cuda.synchronize()
+    ms_dev_graph = 1e3 * (time.perf_counter() - t0) / args.steps
+
+    # Per-kernel durations: HIP events the library records around each launch on its stream
+    # (eager launches), taken right after the timed and device-only steps, at the clocks the
+    # serving loop runs at.
     api.timing_reset()
     api.timing_enable(True)
-    n_kern = max(50, args.steps)
+    n_kern = max(100, args.steps)
     for _ in range(n_kern):
         step.run(step.info)
     torch.cuda.synchronize()
@@ -632,35 +682,13 @@ def main():
         k = kern[name]
         k["achieved_GBps"] = round(k["alg_bytes"] / (k["avg_us"] * 1e-6) / 1e9, 1)
         k["frac_of_peak"] = round(k["achieved_GBps"] / PEAK_HBM_GBPS, 4)
-    evict = torch.zeros(512 << 20, dtype=torch.uint8, device="cuda")
-    dist_cold = step_time_distribution(step, 50, evict)
-    del evict
-    dist_warm = step_time_distribution(step, max(100, args.steps))
 
-    # W warm-up steps, right after the GPU work above (no idle gap before the timed steps).
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # Timed region: exactly K serving-loop steps (plan on the CPU, then the captured run).
-    gc.disable()
-    torch.cuda.synchronize()
+    # The plan's CPU time alone (the GPU idles meanwhile, so it comes after the GPU timings).
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    for _ in range(200):
+        step.plan()
+    ms_plan = 1e3 * (time.perf_counter() - t0) / 200
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    gc.enable()
-    ms_step = 1e3 * elapsed / args.steps
-
-    # Device-only steps (one plan, K replays) -- the cost of the kernels alone.
-    step.plan()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step.replay()
-    torch.cuda.synchronize()
-    ms_dev = 1e3 * (time.perf_counter() - t0) / args.steps
 
     dom = max(("prefix_mfma", "suffix_decode"), key=lambda n: kern[n]["avg_us"])
     src_hash = kernel_source_hash()
@@ -706,9 +734,12 @@ def main():
                    "page_size": 16, "alg_kv_bytes_per_step": alg_bytes},
         "steps_per_s": round(1e3 / ms_step, 1),
         "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBPS, 2),
-        "step": "CPU plan into a pinned buffer + its upload, then replay of the cascade run "
-                "captured once in a HIP graph",
+        "step": "CPU plan into a pinned buffer + its upload, then the cascade run (level kernel, "
+                "suffix kernel with the merge in the same launch) launched on the stream",
         "graph_replay_equals_eager_run": graph_equal,
+        "graph_replay_loop": {"ms_per_step": round(ms_step_graph, 4),
+                              "steps_per_s": round(1e3 / ms_step_graph, 1),
+                              "ms_per_step_device_only": round(ms_dev_graph, 4)},
         "read_stream_peak_GBps": round(stream_gbps, 1),
         "pct_of_read_stream_peak": round(100 * value / stream_gbps, 2),
         "ms_per_step_device_only": round(ms_dev, 4),

@@ -64,8 +64,11 @@ hipEvent_t take_event() {
     g_free_events.pop_back();
     return e;
   }
+  // Timing-only events: recording them performs no system-scope fence, so the bracket adds no
+  // cache writeback / invalidation between the kernels it measures (the reader synchronizes on
+  // the stop event before taking the elapsed time).
   hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
   return e;
 }
 
