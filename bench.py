@@ -38,6 +38,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "KV bytes/s from HBM (% of peak) + decode steps/s, cascade 32K prefix, batch 128"
 PEAK_HBM_GBPS = 8000.0
+PEAK_FP16_MFMA_TFLOPS = 2500.0   # dense fp16 matrix-core peak of the MI355X
 KERNEL_SOURCES = ["paged_kv_cascade_amd/csrc/prefix_kernel.h", "paged_kv_cascade_amd/csrc/decode.hip",
                   "paged_kv_cascade_amd/csrc/decode_kernel.h", "paged_kv_cascade_amd/csrc/merge.hip",
                   "paged_kv_cascade_amd/csrc/merge_ops.h", "paged_kv_cascade_amd/csrc/device_common.h"]
@@ -698,6 +699,18 @@ def main():
             "traffic": (traffic or {}).get(dom, {}).get("hbm_bytes_per_launch") if traffic else None,
             "alg_bytes_per_launch": kern[dom]["alg_bytes"], "avg_launch_us": kern[dom]["avg_us"]}
 
+    # The level kernel's matrix-core work: S^T = K Q^T and O^T += V^T P^T, 2 * head_dim flops
+    # each per (query, prefix token, head): 4 * 128 * 32768 * 32 * 128 = 68,719,476,736 per launch.
+    prefix_flops = 4 * w.head_dim * sum(w.levels[0]["kv_lens"]) * w.num_qo_heads * w.batch
+    pk = kern["prefix_mfma"]
+    mfma = {"kernel": "prefix_mfma", "flops_per_launch": prefix_flops,
+            "achieved_TFLOPs": round(prefix_flops / (pk["avg_us"] * 1e-6) / 1e12, 1),
+            "peak_TFLOPs": PEAK_FP16_MFMA_TFLOPS,
+            "frac": round(prefix_flops / (pk["avg_us"] * 1e-6) / 1e12 / PEAK_FP16_MFMA_TFLOPS, 4),
+            "busy_frac_counters": (traffic or {}).get("prefix_mfma", {}).get("mfma_busy_frac") if traffic else None}
+    if mfma["busy_frac_counters"] is not None:
+        mfma["busy_frac_counters"] = round(mfma["busy_frac_counters"], 4)
+
     info = step.info
     nonc = noncascade_comparison(api, w, step, info)
     if traffic and "noncascade_decode_full_tables" in traffic:
@@ -750,6 +763,7 @@ def main():
         "llc_evicted_alg_GBps": round(alg_bytes / (dist_cold["p50"] * 1e-6) / 1e9, 1),
         "kernels": kern,
         "roofline": roof,
+        "prefix_mfma_utilisation": mfma,
         "three_level_cascade": three,
         "noncascade_same_step": nonc,
         "append_kv": app,
