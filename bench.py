@@ -182,17 +182,21 @@ def cpu_oracle_baseline(n_req):
         n_req = w.batch
     reqs = list(range(0, w.batch, max(1, w.batch // n_req)))[:n_req]
     cores = min(cores, len(reqs))
-    t0 = time.perf_counter()
+    walls = []
     with mp.get_context("fork").Pool(cores, initializer=_cpu_worker_init) as pool:
-        outs = pool.map(_cpu_one_request, reqs)
-    dt = time.perf_counter() - t0
-    assert all(np.all(np.isfinite(o)) for o in outs)
+        for _ in range(3):
+            t0 = time.perf_counter()
+            outs = pool.map(_cpu_one_request, reqs)
+            walls.append(time.perf_counter() - t0)
+            assert all(np.all(np.isfinite(o)) for o in outs)
+    dt = sorted(walls)[1]   # median of three passes
     step_s = dt * w.batch / len(reqs)
     return {"value": round(alg_bytes / step_s / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "steps_per_s": round(1.0 / step_s, 5), "seconds_per_step": round(step_s, 3),
             "host_cores": os.cpu_count(), "cores_available": avail,
+            "pass_seconds": [round(x, 3) for x in walls],
             "sample": f"{len(reqs)} of {w.batch} requests x all {w.num_qo_heads} heads "
-                      f"(33,024 tokens each) in {dt:.1f} s wall on {cores} worker processes "
+                      f"(33,024 tokens each) in {dt:.1f} s wall (median of 3 passes) on {cores} worker processes "
                       f"({avail} cores available to the process, at most 16 used)"
                       + ("" if len(reqs) == w.batch else f", scaled to one {w.batch}-request step")}
 
@@ -213,6 +217,38 @@ def _cpu_one_request(b):
     q, k, v, P, scale, levels, bt, sl = _CPU_CTX
     O, L = oatt.cascade_decode(q, k, v, P, scale, levels, bt, sl, requests=[b])
     return O[b]
+
+
+def device_record(api):
+    """The device the run used: name, architecture, compute units, HIP version, and its GFX and
+    memory clocks read (read-only) through amdsmi, matched to this device by PCI bus; the clocks
+    are null when amdsmi is missing or the device cannot be matched."""
+    import torch
+    props = torch.cuda.get_device_properties(0)
+    rec = {"name": torch.cuda.get_device_name(0), "arch": getattr(props, "gcnArchName", None),
+           "compute_units": api.device_info(0)["num_cus"], "hip_version": torch.version.hip,
+           "clocks_mhz": None}
+    bus = getattr(props, "pci_bus_id", None)
+    if bus is None:
+        return rec
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        try:
+            for h in amdsmi.amdsmi_get_processor_handles():
+                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)
+                if int(bdf.split(":")[1], 16) != int(bus):
+                    continue
+                g = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)
+                m = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.MEM)
+                rec["clocks_mhz"] = {"gfx_now": g.get("clk"), "gfx_max": g.get("max_clk"),
+                                     "mem_now": m.get("clk"), "mem_max": m.get("max_clk"), "bdf": bdf}
+                break
+        finally:
+            amdsmi.amdsmi_shut_down()
+    except Exception:
+        rec["clocks_mhz"] = None
+    return rec
 
 
 def run_cpu_baseline_child(n_req):
@@ -684,6 +720,9 @@ def main():
         k["achieved_GBps"] = round(k["alg_bytes"] / (k["avg_us"] * 1e-6) / 1e9, 1)
         k["frac_of_peak"] = round(k["achieved_GBps"] / PEAK_HBM_GBPS, 4)
 
+    # The device, with its clocks right after the steady-state kernel timing.
+    device = device_record(api)
+
     # The plan's CPU time alone (the GPU idles meanwhile, so it comes after the GPU timings).
     t0 = time.perf_counter()
     for _ in range(200):
@@ -764,6 +803,7 @@ def main():
         "kernels": kern,
         "roofline": roof,
         "prefix_mfma_utilisation": mfma,
+        "device": device,
         "three_level_cascade": three,
         "noncascade_same_step": nonc,
         "append_kv": app,
