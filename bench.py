@@ -41,7 +41,8 @@ PEAK_HBM_GBPS = 8000.0
 PEAK_FP16_MFMA_TFLOPS = 2500.0   # dense fp16 matrix-core peak of the MI355X
 KERNEL_SOURCES = ["paged_kv_cascade_amd/csrc/prefix_kernel.h", "paged_kv_cascade_amd/csrc/decode.hip",
                   "paged_kv_cascade_amd/csrc/decode_kernel.h", "paged_kv_cascade_amd/csrc/merge.hip",
-                  "paged_kv_cascade_amd/csrc/merge_ops.h", "paged_kv_cascade_amd/csrc/device_common.h"]
+                  "paged_kv_cascade_amd/csrc/merge_ops.h", "paged_kv_cascade_amd/csrc/device_common.h",
+                  "paged_kv_cascade_amd/csrc/kernels.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "cascade32k_b128_hbm_traffic.json")
 # FETCH_SIZE of one non-cascade step over the same data (rocprofv3, scaled by the copy
 # calibration), from the committed counter summary of that kernel.
@@ -82,21 +83,25 @@ def copy_calibration():
 
 
 class Step:
-    """Buffers and per-step calls of the serving loop: the CPU plan of the step (into one of
-    two pinned host buffers, uploaded on the stream into the one device workspace), then the
-    cascade run launched on the stream (`__call__`), or the replay of that run captured once
-    in a HIP graph (`step_graph`; FlashInfer paper summary, section A3: plan on the CPU
-    outside the graph, run captured; appendix D: fixed pointers).  Both compute the same bits
-    (checked in main).  On this stack the graph launch costs the GPU about 6-7 us per step
-    more than the two direct launches, so the timed loop launches directly."""
+    """Buffers and per-step calls of the serving loop: the CPU plan of the step into one of
+    two pinned host buffers, then the cascade run launched on the stream (`__call__`; the plan
+    is built with defer_upload, so the run's level kernel reads its items from the host buffer
+    and copies the plan into the one device workspace, with no separate upload launch), or the
+    upload of the plan on the stream and the replay of the run captured once in a HIP graph
+    (`step_graph`; FlashInfer paper summary, section A3: plan on the CPU outside the graph,
+    run captured; appendix D: fixed pointers).  Both compute the same bits (checked in main).
+    On this stack a graph replay costs the GPU about 6-7 us per step more than the direct
+    launches, so the timed loop launches directly."""
 
     def __init__(self, api, w, capture=True):
         import torch
         self.api, self.w = api, w
         self.levels = api.HostLevels([{"qo_indptr": lv["qo_indptr"], "kv_lens": lv["kv_lens"]} for lv in w.levels])
-        self.params = api.make_params(w.batch, w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size)
+        shape = (w.batch, w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size)
+        self.params = api.make_params(*shape)
+        self.params_deferred = api.make_params(*shape, defer_upload=True)   # same layout
         # Two pinned host buffers used alternately: the CPU may write step i+1's plan while
-        # the copy of step i's plan is still queued.  One device workspace (fixed pointers).
+        # step i still reads (or copies) its own.  One device workspace (fixed pointers).
         self.ws = [api.Workspace(self.params, self.levels) for _ in range(2)]
         for k in (1,):
             self.ws[k].device = self.ws[0].device
@@ -111,6 +116,7 @@ class Step:
         self.lse = torch.empty(w.batch, w.num_qo_heads, dtype=torch.float32, device="cuda")
         self.i = 0
         self.info = self.plan()
+        self.mark()
         self.graph = None
         if capture:
             torch.cuda.synchronize()
@@ -124,17 +130,24 @@ class Step:
             torch.cuda.synchronize()
             self.graph = g
 
-    def plan(self):
-        import torch
+    def plan(self, deferred=False):
+        """The step's plan into the next host buffer, once the work that read it two steps ago
+        has completed (a deferred plan is read by the run, so mark() follows the run)."""
         k = self.i % 2
         if self.copy_done[k] is not None:
             self.copy_done[k].synchronize()
-        info = self.api.plan(self.params, self.kv_lens, self.levels, workspace=self.ws[k])
+        info = self.api.plan(self.params_deferred if deferred else self.params, self.kv_lens, self.levels,
+                             workspace=self.ws[k])
+        self.i += 1
+        self.k = k
+        return info
+
+    def mark(self):
+        """The host buffer of the latest plan may be rewritten once the work enqueued so far is done."""
+        import torch
         ev = torch.cuda.Event()
         ev.record()
-        self.copy_done[k] = ev
-        self.i += 1
-        return info
+        self.copy_done[self.k] = ev
 
     def run(self, info):
         """The cascade run itself, launched eagerly (per-kernel timing needs eager launches)."""
@@ -147,13 +160,17 @@ class Step:
         self.graph.replay()
 
     def __call__(self):
-        """One serving-loop step: plan and upload, then the cascade run (direct launches)."""
-        self.run(self.plan())
+        """One serving-loop step: the plan, then the cascade run that brings it over (direct
+        launches)."""
+        self.run(self.plan(deferred=True))
+        self.mark()
 
     def step_graph(self):
-        """The same step with the run replayed from the captured graph."""
+        """The same step with the plan uploaded on the stream and the run replayed from the
+        captured graph."""
         self.plan()
         self.replay()
+        self.mark()
 
 
 def cpu_oracle_baseline(n_req):
@@ -686,6 +703,7 @@ def main():
 
     # Device-only steps (one plan, K runs; then K graph replays) -- the kernels alone.
     step.plan()
+    step.mark()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -723,10 +741,11 @@ def main():
     # The device, with its clocks right after the steady-state kernel timing.
     device = device_record(api)
 
-    # The plan's CPU time alone (the GPU idles meanwhile, so it comes after the GPU timings).
+    # The plan's CPU time alone, as the timed steps build it (deferred: no GPU work; the GPU
+    # idles meanwhile, so it comes after the GPU timings).
     t0 = time.perf_counter()
     for _ in range(200):
-        step.plan()
+        step.plan(deferred=True)
     ms_plan = 1e3 * (time.perf_counter() - t0) / 200
     torch.cuda.synchronize()
 

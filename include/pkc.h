@@ -139,6 +139,15 @@ typedef struct pkc_plan_params {
                            launches no merge pass; 2 -> a separate merge pass after the decode
                            kernel; 0 -> 1 when num_ctas <= batch (few split requests), else 2.
                            Both give the same bits. */
+  int32_t defer_upload; /* 0: pkc_plan enqueues the copy of the plan into the workspace.
+                           1: pkc_plan enqueues nothing; the plan stays in host_buf (which must
+                           then be page-locked) and the first run call that uses it brings it
+                           over: in pkc_cascade_decode(_fp8) with levels, the first level kernel
+                           reads its own items from host_buf and copies the plan into the
+                           workspace while it runs (no separate launch); every other run call
+                           enqueues the copy first.  host_buf must then stay untouched until
+                           the run calls that use the plan have completed on their stream.
+                           Same results either way. */
 } pkc_plan_params;
 
 /* Host description of one cascade level: groups of consecutive requests sharing a KV run.
@@ -212,6 +221,8 @@ typedef struct pkc_plan_info {
   int64_t off_counters;    /* uint32 [B, Hkv] arrival counters of the in-kernel contraction:
                               zero in every plan's integer arrays, and every run leaves them
                               zero */
+  uint64_t host_src;       /* defer_upload: the page-locked host buffer the run calls copy the
+                              plan from (0: pkc_plan enqueued the copy) */
 } pkc_plan_info;
 
 /*

@@ -44,7 +44,7 @@ class PlanParams(ctypes.Structure):
                 ("chunk_align", ctypes.c_int32), ("enable_split", ctypes.c_int32),
                 ("alpha", ctypes.c_int64), ("beta", ctypes.c_int64), ("decode_waves", ctypes.c_int32),
                 ("level_write_through", ctypes.c_int32), ("level_streams", ctypes.c_int32),
-                ("contraction", ctypes.c_int32)]
+                ("contraction", ctypes.c_int32), ("defer_upload", ctypes.c_int32)]
 
 
 class LevelHost(ctypes.Structure):
@@ -81,7 +81,8 @@ class PlanInfo(ctypes.Structure):
                 ("off_state_o", ctypes.c_int64), ("off_state_lse", ctypes.c_int64),
                 ("dev_bytes", ctypes.c_int64), ("dev_ws", ctypes.c_uint64), ("lvl_causal", _L8),
                 ("lvl_write_through", ctypes.c_int32), ("lvl_streams", ctypes.c_int32),
-                ("dec_contraction", ctypes.c_int32), ("off_counters", ctypes.c_int64)]
+                ("dec_contraction", ctypes.c_int32), ("off_counters", ctypes.c_int64),
+                ("host_src", ctypes.c_uint64)]
 
 
 _P = ctypes.c_void_p
@@ -212,10 +213,11 @@ def device_info(device: int = 0):
 def make_params(batch, num_qo_heads, num_kv_heads, head_dim, page_size, num_ctas=0, level_ctas=0,
                 level_tile_q=0, chunk_align=1, enable_split=True, alpha=1, beta=1,
                 decode_waves=0, level_write_through=False, level_streams=0,
-                contraction=0) -> PlanParams:
+                contraction=0, defer_upload=False) -> PlanParams:
     return PlanParams(batch, num_qo_heads, num_kv_heads, head_dim, page_size, num_ctas, level_ctas,
                       level_tile_q, chunk_align, 1 if enable_split else 0, alpha, beta, decode_waves,
-                      1 if level_write_through else 0, level_streams, contraction)
+                      1 if level_write_through else 0, level_streams, contraction,
+                      1 if defer_upload else 0)
 
 
 class HostLevels:
@@ -577,7 +579,7 @@ def cascade_decode_fp8(plan_info: PlanInfo, q, k_pool, v_pool, lvl_devs: Sequenc
 
 def prefill_plan(qo_lens, kv_lens, num_qo_heads, num_kv_heads, head_dim, page_size, level_ctas=0,
                  level_tile_q=0, enable_split=True, alpha=1, beta=1, causal=True,
-                 workspace: Workspace = None, write_through=True):
+                 workspace: Workspace = None, write_through=True, defer_upload=False):
     """Plan of a batch prefill: every query row is one plan request (batch = total_q, no own
     KV) and one level whose groups are the requests (qo_indptr = cumulative query lengths,
     kv_lens; causal: tiles weighed by the KV their last query sees).  level_ctas = 0 takes
@@ -596,7 +598,8 @@ def prefill_plan(qo_lens, kv_lens, num_qo_heads, num_kv_heads, head_dim, page_si
     total_q = qo_indptr[-1]
     params = make_params(total_q, num_qo_heads, num_kv_heads, head_dim, page_size, num_ctas=1,
                          level_ctas=level_ctas, level_tile_q=level_tile_q, enable_split=enable_split,
-                         alpha=alpha, beta=beta, level_write_through=write_through)
+                         alpha=alpha, beta=beta, level_write_through=write_through,
+                         defer_upload=defer_upload)
     levels = [{"qo_indptr": qo_indptr, "kv_lens": [int(x) for x in kv_lens], "causal": bool(causal)}]
     if workspace is None:
         workspace = Workspace(params, levels)

@@ -127,6 +127,15 @@ pkc_status check_plan(const pkc_plan_info* plan, int32_t batch, int32_t hq, int3
   return PKC_OK;
 }
 
+// A plan built with defer_upload is still only in its page-locked host buffer: enqueue its copy
+// into the workspace ahead of a run that does not bring it over itself.
+pkc_status upload_if_deferred(const pkc_plan_info* plan, void* dev_ws, hipStream_t s) {
+  if (!plan || plan->host_src == 0) return PKC_OK;
+  hipError_t e = pkc::launch_plan_upload(reinterpret_cast<const void*>(plan->host_src), dev_ws, plan->int_bytes, s);
+  if (e != hipSuccess) return hip_fail(e, "plan upload launch");
+  return PKC_OK;
+}
+
 template <typename T>
 T* at(void* base, int64_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(base) + off);
@@ -205,7 +214,7 @@ struct PrefillLevel {
 pkc_status run_level(const pkc_plan_info* plan, int level, const void* q, const void* k, const void* v,
                      int64_t num_pages, const pkc_level_dev* lv, pkc_dtype dtype, float sm_scale,
                      void* ws, hipStream_t s, bool fp8 = false, float k_scale = 1.f,
-                     float v_scale = 1.f, const PrefillLevel* pf = nullptr) {
+                     float v_scale = 1.f, const PrefillLevel* pf = nullptr, bool bring_plan = false) {
   if (!pf && plan->lvl_groups[level] > 0 && (!lv->kv_page_indptr || !lv->kv_page_indices))
     return fail(PKC_ERR_INVALID_ARG, "level " + std::to_string(level) + ": NULL page arrays");
   pkc::PrefixParams p{};
@@ -243,6 +252,13 @@ pkc_status run_level(const pkc_plan_info* plan, int level, const void* q, const 
   p.st_lse = at<float>(ws, plan->off_state_lse);
   p.indptr = at<int32_t>(ws, plan->off_lvl_indptr[level]);
   p.items = at<int32_t>(ws, plan->off_lvl_items[level]);
+  if (bring_plan) {
+    // This launch reads its items from the deferred plan's host buffer and copies the plan's
+    // integer words into the workspace for the launches after it.
+    p.plan_host = reinterpret_cast<const int32_t*>(plan->host_src);
+    p.plan_dev = static_cast<int32_t*>(ws);
+    p.plan_words = (int32_t)(plan->int_bytes / 4);
+  }
   const int g = plan->num_qo_heads / plan->num_kv_heads;
   const int streams = plan->lvl_streams;
   if (streams != 1 && streams != 2) return fail(PKC_ERR_PLAN_MISMATCH, "plan has no level stream count");
@@ -411,6 +427,15 @@ pkc_status pkc_plan(const pkc_plan_params* params, const int32_t* kv_lens_h,
     return fail(PKC_ERR_WORKSPACE_TOO_SMALL, "device workspace smaller than " + std::to_string(out->dev_bytes) + " bytes");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
+  if (r.p.defer_upload) {
+    // The run calls bring the plan over (the first level kernel of a cascade, else the
+    // upload kernel ahead of the run): they read the page-locked buffer directly.
+    if (!pkc::host_buf_is_pinned(host_buf))
+      return fail(PKC_ERR_INVALID_ARG, "defer_upload needs a page-locked host buffer");
+    out->dev_ws = (uint64_t)(uintptr_t)dev_ws;
+    out->host_src = (uint64_t)(uintptr_t)host_buf;
+    return PKC_OK;
+  }
   if (pkc::host_buf_is_pinned(host_buf)) {
     // A kernel on the caller's queue reads the pinned buffer: no copy-engine synchronisation.
     e = pkc::launch_plan_upload(host_buf, dev_ws, out->int_bytes, s);
@@ -464,6 +489,7 @@ pkc_status pkc::decode_run(bool fp8, float k_scale, float v_scale, const pkc_pla
     p.items = at<int32_t>(dev_ws, plan->off_dec_items);
     if (plan->dec_contraction == 1) set_contraction(&p, plan, dev_ws, 0);
     grid_x = plan->num_ctas;
+    if (!plan_upload_src && plan->host_src) plan_upload_src = reinterpret_cast<const void*>(plan->host_src);
     if (plan_upload_src) {
       // Every check has passed: copy the plan's integer arrays from the host buffer into the
       // workspace on the same stream, ahead of the kernels that read them.
@@ -545,7 +571,7 @@ static pkc_status prefix_impl(bool fp8, float k_scale, float v_scale, const pkc_
   if (num_pages < 1) return fail(PKC_ERR_INVALID_ARG, "num_pages must be >= 1 (masked lanes read row 0 of page 0)");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if ((st = run_level(plan, level, q, k_pool, v_pool, num_pages, level_dev, dtype, sm_scale, dev_ws, s,
-                      fp8, k_scale, v_scale)) != PKC_OK)
+                      fp8, k_scale, v_scale, nullptr, plan->host_src != 0)) != PKC_OK)
     return st;
   pkc::MergePlanParams m = merge_params(plan, dev_ws, level, level + 1, false, o_state, lse_state);
   return timed(2, s, "merge kernel launch", [&] { return pkc::launch_merge_plan(o_dtype, head_dim, m, s); });
@@ -620,7 +646,7 @@ static pkc_status prefill_impl(bool fp8, float k_scale, float v_scale, const pkc
   const PrefillLevel pf{block_table, max_blocks, qo_indptr, kv_lens, causal ? 1 : 0, o, lse,
                         tree_mask, mask_indptr, mask_bytes};
   if ((st = run_level(plan, 0, q, k_pool, v_pool, num_pages, nullptr, dtype, sm_scale, dev_ws, s, fp8,
-                      k_scale, v_scale, &pf)) != PKC_OK)
+                      k_scale, v_scale, &pf, plan->host_src != 0)) != PKC_OK)
     return st;
   // Query rows written through by their tile's only item are flagged and skipped; the merge is
   // enqueued even when every row is (launches independent of the plan's lengths).
@@ -754,9 +780,12 @@ static pkc_status cascade_impl(bool fp8, float k_scale, float v_scale, const pkc
   if ((int64_t)max_blocks * page_size > INT32_MAX)
     return fail(PKC_ERR_INVALID_ARG, "max_blocks * page_size exceeds int32");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  // A deferred plan comes over with the first level kernel (or ahead of the decode kernel when
+  // the cascade has no level).
+  if (num_levels == 0 && (st = upload_if_deferred(plan, dev_ws, s)) != PKC_OK) return st;
   for (int32_t l = 0; l < num_levels; ++l)
     if ((st = run_level(plan, l, q, k_pool, v_pool, num_pages, &levels[l], dtype, sm_scale, dev_ws, s,
-                        fp8, k_scale, v_scale)) != PKC_OK)
+                        fp8, k_scale, v_scale, nullptr, l == 0 && plan->host_src != 0)) != PKC_OK)
       return st;
   pkc::DecodeParams p = decode_params(q, k_pool, v_pool, num_pages, block_table, max_blocks,
                                       suffix_seqlens, nullptr, num_qo_heads, num_kv_heads,
@@ -864,6 +893,8 @@ pkc_status pkc_debug_cta_trace(const pkc_plan_info* plan, int32_t stage, const v
   if (trace_len < (int64_t)ctas * max_items_per_cta * 8)
     return fail(PKC_ERR_WORKSPACE_TOO_SMALL, "trace buffer too small");
   void* ws = const_cast<void*>(dev_ws);
+  pkc_status st = upload_if_deferred(plan, ws, reinterpret_cast<hipStream_t>(stream));
+  if (st != PKC_OK) return st;
   const int32_t* indptr = at<int32_t>(ws, dec ? plan->off_dec_indptr : plan->off_lvl_indptr[stage]);
   const int32_t* items = at<int32_t>(ws, dec ? plan->off_dec_items : plan->off_lvl_items[stage]);
   hipError_t e = pkc::launch_debug_trace(indptr, items, ctas, trace_out, max_items_per_cta,

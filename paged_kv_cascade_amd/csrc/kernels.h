@@ -80,6 +80,13 @@ struct PrefixParams {
   const uint8_t* tree_mask;
   const int32_t* mask_indptr;
   int32_t mask_bytes;
+  // Deferred plan (plan_host != nullptr): the plan's integer words are still only in the
+  // page-locked host buffer plan_host; this launch reads its items there and copies all
+  // plan_words words to plan_dev (the workspace) for the launches that follow on the stream.
+  // indptr and items keep their workspace addresses (their offsets locate the host copies).
+  const int32_t* plan_host;
+  int32_t* plan_dev;
+  int32_t plan_words;
 };
 
 // Plan-driven merge: request b merges merge_rows[merge_ptr[b*NL2 + l0] .. merge_ptr[b*NL2 + l1]).

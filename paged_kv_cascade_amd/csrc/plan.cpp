@@ -148,6 +148,8 @@ pkc_status check_params(const pkc_plan_params* params, bool need_ctas, Resolved*
     return fail(PKC_ERR_INVALID_ARG, "level_streams must be 0, 1 or 2");
   if (!(p.contraction == 0 || p.contraction == 1 || p.contraction == 2))
     return fail(PKC_ERR_INVALID_ARG, "contraction must be 0, 1 or 2");
+  if (!(p.defer_upload == 0 || p.defer_upload == 1))
+    return fail(PKC_ERR_INVALID_ARG, "defer_upload must be 0 or 1");
   if (p.num_ctas < 0 || p.level_ctas < 0 || p.level_tile_q < 0)
     return fail(PKC_ERR_INVALID_ARG, "num_ctas, level_ctas, level_tile_q must be >= 0");
   if (need_ctas && (p.num_ctas == 0 || p.level_ctas == 0))

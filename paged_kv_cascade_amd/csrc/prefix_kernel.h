@@ -300,14 +300,45 @@ __global__ __launch_bounds__(64 * prefix_detail::kWavesPerStream * NS, NS == 1 ?
   const bool one_page = P >= 8;
   static_assert(LROWS >= 4, "row geometry");
 
-  const int it_begin = scalar_load(p.indptr + blockIdx.x);
-  const int it_end = scalar_load(p.indptr + blockIdx.x + 1);
+  // A deferred plan: the workgroups take their own items from the host copy and copy the
+  // plan's words into the workspace, thread t of the grid word t (further words, for plans
+  // larger than the grid, after the items).  The copy load is issued first and
+  // unconditionally (from a valid address in every case: a branch around it would make the
+  // compiler wait for it), so its latency passes while the item reads below go to the host
+  // buffer too; its store follows the items, once the ring has drained.  The load is older
+  // than every load of the ring, so it can only lengthen the ring's vector-memory waits.
+  const bool deferred = p.plan_host != nullptr;
+  const int nthreads = (int)(blockDim.x * gridDim.x * gridDim.y);
+  const int cw = (int)((blockIdx.y * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x);
+  const int32_t* copy_src = deferred ? p.plan_host + min(cw, max(p.plan_words - 1, 0)) : p.indptr;
+  const int32_t copy_val = *copy_src;
+  const int32_t* indptr_r = deferred ? p.plan_host + (p.indptr - p.plan_dev) : p.indptr;
+  const int32_t* items_r = deferred ? p.plan_host + (p.items - p.plan_dev) : p.items;
+  const int it_begin = scalar_load(indptr_r + blockIdx.x);
+  const int it_end = scalar_load(indptr_r + blockIdx.x + 1);
+  // The record of item blockIdx.x is read together with the CTA's item range: when a level
+  // has one item per CTA (a decode step's shared prefix), CTA c's item is item c, and its
+  // record then needs no second round trip.  (The items array holds at least #CTA records.)
+  const int32_t* rec_c = items_r + 8 * (int64_t)blockIdx.x;
+  int c_grp = scalar_load(rec_c), c_q0 = scalar_load(rec_c + 1), c_nq = scalar_load(rec_c + 2);
+  int c_kb = scalar_load(rec_c + 3), c_ke = scalar_load(rec_c + 4), c_srow = scalar_load(rec_c + 5);
+  // Both reads complete here, together (an empty statement that takes all their values keeps
+  // the compiler from moving the record's reads behind the range test).
+  __asm__ volatile("" : "+s"(c_grp), "+s"(c_q0), "+s"(c_nq), "+s"(c_kb), "+s"(c_ke), "+s"(c_srow)
+                   : "s"(it_begin), "s"(it_end));
   for (int it = it_begin; it < it_end; ++it) {
-    const int32_t* rec = p.items + 8 * (int64_t)it;
-    const int grp = scalar_load(rec);
-    const int q0 = scalar_load(rec + 1), nq = scalar_load(rec + 2);
-    const int kb = scalar_load(rec + 3), srow = scalar_load(rec + 5);
-    int ke = scalar_load(rec + 4);
+    int grp, q0, nq, kb, ke, srow;
+    if (it == (int)blockIdx.x) {
+      grp = c_grp; q0 = c_q0; nq = c_nq; kb = c_kb; ke = c_ke; srow = c_srow;
+    } else {
+      const int32_t* rec = items_r + 8 * (int64_t)it;
+      grp = scalar_load(rec);
+      q0 = scalar_load(rec + 1);
+      nq = scalar_load(rec + 2);
+      kb = scalar_load(rec + 3);
+      ke = scalar_load(rec + 4);
+      srow = scalar_load(rec + 5);
+    }
     const int nrows = nq * G;
     // A group's page run [pbeg, pbeg + npages_grp) is clamped into the page list, so a
     // malformed indptr cannot make the scalar loads below read past it.
@@ -867,6 +898,10 @@ __global__ __launch_bounds__(64 * prefix_detail::kWavesPerStream * NS, NS == 1 ?
     // ring before the next item refills it.
     __builtin_amdgcn_s_waitcnt(0);
     ring_barrier();
+  }
+  if (deferred) {
+    if (cw < p.plan_words) p.plan_dev[cw] = copy_val;
+    for (int w = cw + nthreads; w < p.plan_words; w += nthreads) p.plan_dev[w] = p.plan_host[w];
   }
 }
 

@@ -360,3 +360,15 @@ def test_contraction_mode_and_counter_region(api):
     with pytest.raises(api.PkcError) as e:
         api.plan_host(api.make_params(2, 4, 4, 128, 16, num_ctas=4, level_ctas=1, contraction=3), [1, 2])
     assert e.value.status == 1
+
+
+def test_defer_upload_parameter(api):
+    """defer_upload is 0 or 1; a host-only plan never carries a pending host source."""
+    p = api.make_params(5, 8, 2, 128, 16, num_ctas=4, level_ctas=1, defer_upload=True)
+    info, _ = api.plan_host(p, [3, 70, 0, 16, 900])
+    assert info.host_src == 0
+    bad = api.make_params(5, 8, 2, 128, 16, num_ctas=4, level_ctas=1)
+    bad.defer_upload = 2
+    with pytest.raises(api.PkcError) as e:
+        api.plan_host(bad, [3, 70, 0, 16, 900])
+    assert e.value.status == 1
