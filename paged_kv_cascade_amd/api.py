@@ -272,7 +272,9 @@ def _levels_arg(levels):
 
 def plan(params: PlanParams, kv_lens, levels: Sequence[dict] = (), workspace: Workspace = None,
          device="cuda") -> PlanInfo:
-    """pkc_plan: build the plan on the CPU and enqueue its copy on the current stream.
+    """pkc_plan: build the plan on the CPU and enqueue its copy on the current stream (with
+    params.defer_upload, enqueue nothing: the run calls bring the plan over from the workspace's
+    pinned host buffer, which must then stay untouched until they complete).
     kv_lens: a sequence of ints or an int32 CPU tensor; levels: dicts or a HostLevels."""
     if workspace is None:
         raise PkcError(1, "plan needs a Workspace")
