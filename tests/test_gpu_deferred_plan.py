@@ -184,3 +184,26 @@ def test_deferred_plan_needs_pinned_host_buffer(api):
     with pytest.raises(api.PkcError) as e:
         api.plan(p, [5, 0, 17, 300], workspace=ws)
     assert e.value.status == 1
+
+
+def test_alternating_host_buffers_deferred_plan(api):
+    """Four steps over two host buffers (A, B, A, B), each with other suffix lengths: every run
+    reads the plan its buffer holds now, not what the buffer held two steps before."""
+    say("case: deferred plan, host buffers A B A B with a different plan each step")
+    w = _small_cascade(411, torch.float16, 128, 1, 16)
+    host_levels, devs, keep = _levels(api, w)
+    lens0 = w.cache_seqlens.cpu().tolist()
+    shape = (w.batch, w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size)
+    p0 = api.make_params(*shape, num_ctas=7, level_ctas=3)
+    p1 = api.make_params(*shape, num_ctas=7, level_ctas=3, defer_upload=True)
+    ws0 = api.Workspace(p0, host_levels)
+    bufs = [api.Workspace(p1, host_levels) for _ in range(2)]
+    bufs[1].device = bufs[0].device
+    for step, div in enumerate((1, 2, 3, 5)):
+        lens = [n // div for n in lens0]
+        sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+        ref = _cascade(api, w, api.plan(p0, lens, host_levels, workspace=ws0), devs, sl)
+        ws = bufs[step % 2]
+        info = api.plan(p1, lens, host_levels, workspace=ws)
+        _zero_plan_copy(ws, info)
+        _same(_cascade(api, w, info, devs, sl), ref, f"step {step}")
