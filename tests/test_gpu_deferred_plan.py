@@ -207,3 +207,29 @@ def test_alternating_host_buffers_deferred_plan(api):
         info = api.plan(p1, lens, host_levels, workspace=ws)
         _zero_plan_copy(ws, info)
         _same(_cascade(api, w, info, devs, sl), ref, f"step {step}")
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_fp8_cascade_deferred_plan(api, seed):
+    """Cascades over E4M3 pools: the FP8 level kernel brings a deferred plan over the same way."""
+    qdt = [torch.float16, torch.bfloat16, torch.float16][seed]
+    D, g, P = [(128, 1, 16), (64, 4, 4), (128, 2, 32)][seed]
+    w = _small_cascade(520 + seed, qdt, D, g, P)
+    k8 = workloads.fp8_e4m3_pool(w.k_pool, 0.5)
+    v8 = workloads.fp8_e4m3_pool(w.v_pool, 0.25)
+    host_levels, devs, keep = _levels(api, w)
+    lens = w.cache_seqlens.cpu().tolist()
+    say(f"case: deferred plan, fp8 small cascade seed={520 + seed} q {qdt} D={D} g={g} P={P} B={w.batch}")
+    shape = (w.batch, w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size)
+    outs = []
+    for defer in (False, True):
+        p = api.make_params(*shape, num_ctas=9, level_ctas=2, defer_upload=defer)
+        ws = api.Workspace(p, host_levels)
+        info = api.plan(p, lens, host_levels, workspace=ws)
+        if defer:
+            _zero_plan_copy(ws, info)
+        o, lse = api.cascade_decode_fp8(info, w.q, k8, v8, devs, w.block_table, w.cache_seqlens,
+                                        k_scale=0.5, v_scale=0.25, sm_scale=w.sm_scale)
+        torch.cuda.synchronize()
+        outs.append((o, lse))
+    _same(outs[1], outs[0], "fp8 cascade")
