@@ -206,6 +206,19 @@ __device__ __forceinline__ V16 e4m3x8_to_operand(uint2 c) {
 
 __device__ __forceinline__ uint2 lds_load8(const char* p) { return *reinterpret_cast<const uint2*>(p); }
 
+// Keeps N (4 or 8) 8-byte LDS reads together: an empty statement that takes all of their
+// values makes the compiler issue every read before it waits for the first, where it would
+// otherwise wait for each read right before converting it.
+typedef uint32_t u2v_t __attribute__((ext_vector_type(2)));
+template <int N>
+__device__ __forceinline__ void hold_reads(u2v_t (&x)[N]) {
+  static_assert(N == 4 || N == 8, "read batch");
+  if constexpr (N == 4)
+    __asm__ volatile("" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]));
+  else
+    __asm__ volatile("" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]), "+v"(x[7]));
+}
+
 // 8-bit transpose read: within each 16-lane group, the 8-byte pieces named by lanes 2i and
 // 2i+1 form row i (16 bytes); lane j receives byte j of rows 0..7.
 typedef int i2_t __attribute__((ext_vector_type(2)));
@@ -519,15 +532,46 @@ __global__ __launch_bounds__(64 * prefix_detail::kWavesPerStream * NS, NS == 1 ?
 
     // S^T[mt][nt] of a tile: tokens mt*16 + 4*lg + i, query column nt*16 + l16.  The K
     // operands of each 16-token half are read together, then used by that half's products.
+    // FP8 code operands: codes ks*32 + 8*lg .. +8 of K row r, half lg & 1 of logical chunk
+    // 2 ks + lg / 2.  With the in-wave pipeline every code read of a tile is issued before
+    // the first wait (8 K reads at D = 128, then 8 V^T reads); the in-order step has no
+    // registers to spare for that and converts each read as it arrives.
+    auto kcode = [&](const char* ks_s, int r, int ks) __attribute__((always_inline)) {
+      return lds_load8(ks_s + r * RBG + (((2 * ks + (lg >> 1)) ^ swz8<D>(r)) * 16) + (lg & 1) * 8);
+    };
     auto score = [&](const char* ks_s, f4_t (&s)[2][2]) __attribute__((always_inline)) {
+      if constexpr (F8 && kPipe) {
+        u2v_t kc[2 * KS];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            kc[mt * KS + ks] = __builtin_bit_cast(u2v_t, kcode(ks_s, mt * 16 + l16, ks));
+          }
+        hold_reads(kc);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          V16 ka[KS];
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) ka[ks] = e4m3x8_to_operand<T>(__builtin_bit_cast(uint2, kc[mt * KS + ks]));
+          s[mt][0] = f4_t{0.f, 0.f, 0.f, 0.f};
+          s[mt][1] = f4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            s[mt][0] = Mfma<T>::run(ka[ks], qb[0][ks], s[mt][0]);
+            s[mt][1] = Mfma<T>::run(ka[ks], qb[1][ks], s[mt][1]);
+          }
+        }
+        return;
+      }
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
         const int r = mt * 16 + l16;
         V16 ka[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          if constexpr (F8)   // codes ks*32 + 8*lg .. +8: half lg & 1 of logical chunk 2 ks + lg / 2
-            ka[ks] = e4m3x8_to_operand<T>(lds_load8(ks_s + r * RBG + (((2 * ks + (lg >> 1)) ^ swz8<D>(r)) * 16) + (lg & 1) * 8));
+          if constexpr (F8)
+            ka[ks] = e4m3x8_to_operand<T>(kcode(ks_s, r, ks));
           else
             ka[ks] = lds_load16(ks_s + r * RB + (((ks * 4 + lg) ^ swz<D>(r)) * 16));
         }
@@ -546,11 +590,23 @@ __global__ __launch_bounds__(64 * prefix_detail::kWavesPerStream * NS, NS == 1 ?
     // 2i+1 of the group, each naming 8 bytes of logical chunk dm) is token 4*lg + i for
     // i < 4, else 16 + 4*lg + i - 4.
     const int tr8_tok = (l16 < 8 ? 0 : 12) + 4 * lg + (l16 >> 1);
+    auto vcode = [&](const char* vs_s, int dm) __attribute__((always_inline)) {
+      return lds_read_tr8(vs_s + tr8_tok * RBG + ((dm ^ swz8<D>(tr8_tok)) * 16) + (l16 & 1) * 8);
+    };
     auto vread = [&](const char* vs_s) __attribute__((always_inline)) {
+      if constexpr (F8 && kPipe) {
+        u2v_t vc[DM];
+#pragma unroll
+        for (int dm = 0; dm < DM; ++dm) vc[dm] = __builtin_bit_cast(u2v_t, vcode(vs_s, dm));
+        hold_reads(vc);
+#pragma unroll
+        for (int dm = 0; dm < DM; ++dm) va[dm] = e4m3x8_to_operand<T>(__builtin_bit_cast(uint2, vc[dm]));
+        return;
+      }
 #pragma unroll
       for (int dm = 0; dm < DM; ++dm) {
         if constexpr (F8) {
-          va[dm] = e4m3x8_to_operand<T>(lds_read_tr8(vs_s + tr8_tok * RBG + ((dm ^ swz8<D>(tr8_tok)) * 16) + (l16 & 1) * 8));
+          va[dm] = e4m3x8_to_operand<T>(vcode(vs_s, dm));
         } else {
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
