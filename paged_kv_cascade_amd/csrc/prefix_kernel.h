@@ -402,7 +402,9 @@ __global__ __launch_bounds__(64 * prefix_detail::kWavesPerStream * NS, NS == 1 ?
       const int rb = t0 + tt * kTK + 8 * wq;
       Pg r;
       r.e0 = scalar_load(pages + min(rb >> shift, last_page));
-      r.e1 = one_page ? r.e0 : scalar_load(pages + min((rb + 4) >> shift, last_page));
+      // One page holds all 8 rows: the second entry is not read (a copy of the first would
+      // make the wave wait for its load here instead of at the next step's barrier).
+      r.e1 = one_page ? 0 : scalar_load(pages + min((rb + 4) >> shift, last_page));
       return r;
     };
 
