@@ -591,6 +591,7 @@ pkc_status pkc_read_stream_probe(const void* src, int64_t bytes, uint32_t* sink,
  * Per-kernel timing with HIP events (for measurements): when enabled, every kernel launch
  * of the calls above is bracketed by events recorded on the same stream (created without the
  * system-scope fence on record, so the brackets add no cache writeback between kernels).
+ * Launches on a stream that is being captured into a graph are not bracketed (nor counted).
  * pkc_timing_read waits for the recorded events and returns, per kernel kind, the number of
  * launches and the summed duration in milliseconds since the last reset.
  * Kernel kinds: 0 decode, 1 prefix (MFMA), 2 merge (plan-driven), 3 merge (generic / in place).

@@ -72,19 +72,24 @@ hipEvent_t take_event() {
   return e;
 }
 
-// Runs `launch` and, when timing is on, brackets it with events on the same stream.
+// Runs `launch` and, when timing is on, brackets it with events on the same stream.  Not while
+// the stream is being captured into a graph: events recorded there would only be recorded by
+// the graph's replays, and the reader would wait on them.
 template <typename F>
 pkc_status timed(int kind, hipStream_t s, const char* what, F&& launch) {
   hipEvent_t a = nullptr, b = nullptr;
   if (g_timing) {
-    std::lock_guard<std::mutex> lk(g_mu);
-    a = take_event();
-    b = take_event();
-    if (a) (void)hipEventRecord(a, s);
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) == hipSuccess && cs == hipStreamCaptureStatusNone) {
+      std::lock_guard<std::mutex> lk(g_mu);
+      a = take_event();
+      b = take_event();
+      if (a) (void)hipEventRecord(a, s);
+    }
   }
   hipError_t e = launch();
   if (e != hipSuccess) return hip_fail(e, what);
-  if (g_timing && a && b) {
+  if (a && b) {
     (void)hipEventRecord(b, s);
     std::lock_guard<std::mutex> lk(g_mu);
     g_pending.push_back({kind, a, b});
