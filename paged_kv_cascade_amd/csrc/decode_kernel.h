@@ -37,8 +37,9 @@
 // the one that brings it to the request's number of partial states reads the request's states
 // with device-scope atomic loads, merges its whole merge list (levels, then its own chunks)
 // into the final output with the merge pass's arithmetic, and sets the counter back to zero.
-// Nothing waits for another workgroup, so any number of workgroups may be resident.  Requests with no decode item and no write-through (empty KV; a cascade request
-// with no own KV) are merged at the start of workgroup (b mod #CTA, kv head).
+// Nothing waits for another workgroup, so any number of workgroups may be resident.  Requests
+// with no decode item and no write-through (empty KV; a cascade request with no own KV) are
+// merged at the start of workgroup (b mod #CTA, kv head).
 #pragma once
 
 #include <cstdlib>

@@ -7,12 +7,14 @@
 // block-sparse matrix processed with a large row tile.  Many queries against one KV set is a
 // real dense contraction, so both products run on matrix cores.
 //
-// Workgroup = 4 waves = 128 query rows (a row is one (query, head) pair of the KV head's
-// group; heads of one query are adjacent rows); two workgroups per compute unit.
+// Tile stream = 4 waves = 128 query rows (a row is one (query, head) pair of the KV head's
+// group; heads of one query are adjacent rows).  A workgroup runs one tile stream (4 waves,
+// two workgroups per compute unit) or two streams over alternate tiles of its item (8 waves,
+// one workgroup per compute unit), whose states are merged through LDS at the end.
 //
-// KV streaming: 32-token tiles go straight from HBM into a 4-stage LDS ring with buffer loads
-// that write LDS (no register staging), so three tiles (48 KB per workgroup) are in flight
-// while one is computed.  Each load instruction moves 1 KB: whole 16-byte chunks of a few
+// KV streaming: 32-token tiles go straight from HBM into a 4-stage LDS ring per stream with
+// buffer loads that write LDS (no register staging), so three tiles (48 KB per stream) are in
+// flight while one is computed.  Each load instruction moves 1 KB: whole 16-byte chunks of a few
 // head_dim-contiguous K (or V) rows of one page, through a buffer resource over that page.
 // Rows outside the item's token range and pages outside [0, num_pages) are out of the
 // resource's range, so the hardware writes zeros to LDS and reads nothing.  Chunk positions
